@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for the Sampling-VT view transform.
+
+This module only *draws* inputs: camera rigs (K, R, t), feature maps,
+upstream gradients and BEV ranges.  It holds none of the operator's own
+arithmetic (no voxel centres, projection, validity test, sampling or
+reduction), so both the CPU oracle and the GPU path can be fed from it
+without sharing any of the computation under test.
+
+The shapes follow the camera-BEV setting the FlashBEV reading notes
+describe (B x N x C x H x W features, a B x C x X x Y output, Z height
+bins; "Problem Setting"), with nuScenes-like sizes taken from the
+Lift-Splat-Shoot tutorial (six surround cameras, an 8 x 22 stride-16
+feature map, a +-50 m BEV at 0.5 m; "Lift" and "Splat" sections).  No
+dataset is read: every tensor is drawn from a seeded numpy generator.
+
+Rig convention (also used by the oracle's documentation):
+  * ego frame: x forward, y left, z up (metres);
+  * camera frame: x right, y down, z forward;
+  * (R, t) maps ego to camera, p_cam = R p_ego + t, as in the projection
+    equation of the SparseDriveV2 notes ("Deformable Aggregation", step 2);
+  * camera k looks outward at yaw psi_k = k * 360/N deg + U(-5, 5) deg
+    (counter-clockwise from +x seen from above), pitch 0, roll 0, with its
+    centre 1 m from the ego origin along psi_k at height 1.6 m;
+  * intrinsics are in feature-map pixels: fx = fy = (W/2) / tan(35 deg),
+    cx = (W-1)/2, cy = (H-1)/2, so integer (u, v) are pixel centres.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# Half of the horizontal field of view (70 deg in total).
+HALF_HFOV_DEG = 35.0
+CAM_RADIUS_M = 1.0
+CAM_HEIGHT_M = 1.6
+YAW_JITTER_DEG = 5.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One named problem size.  ``rng6`` = (xmin, xmax, ymin, ymax, zmin, zmax)."""
+
+    cid: int
+    name: str
+    B: int
+    N: int
+    C: int
+    H: int
+    W: int
+    X: int
+    Y: int
+    Z: int
+    rng6: Tuple[float, float, float, float, float, float]
+    dtypes: Tuple[str, ...]
+    per_sample_rig: bool
+    backward: bool
+
+    @property
+    def out_elems(self) -> int:
+        return self.B * self.C * self.X * self.Y
+
+    @property
+    def tuples(self) -> int:
+        return self.B * self.X * self.Y * self.Z * self.N
+
+
+_R50 = (-50.0, 50.0, -50.0, 50.0, -5.0, 3.0)
+_R512 = (-51.2, 51.2, -51.2, 51.2, -5.0, 3.0)
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload(0, "tiny", 1, 6, 16, 8, 22, 50, 50, 4, _R50, ("f32",), False, False),
+    "nuscenes": Workload(1, "nuscenes", 1, 6, 64, 16, 44, 200, 200, 8, _R50, ("f32",), False, False),
+    "batched": Workload(2, "batched", 4, 6, 80, 32, 88, 200, 200, 16, _R50, ("f32", "bf16"), True, False),
+    "large": Workload(3, "large", 1, 6, 128, 64, 176, 400, 400, 32, _R50, ("bf16",), False, False),
+    "fwdbwd": Workload(4, "fwdbwd", 2, 6, 64, 16, 44, 256, 256, 16, _R512, ("f32",), True, True),
+}
+
+
+def intrinsics(H: int, W: int) -> np.ndarray:
+    """3x3 pinhole intrinsics in feature-map pixels (fp32)."""
+    f = (W / 2.0) / math.tan(math.radians(HALF_HFOV_DEG))
+    K = np.array([[f, 0.0, (W - 1) / 2.0], [0.0, f, (H - 1) / 2.0], [0.0, 0.0, 1.0]], dtype=np.float64)
+    return K.astype(np.float32)
+
+
+def extrinsics_from_yaw(yaw_deg: float, radius: float = CAM_RADIUS_M, height: float = CAM_HEIGHT_M,
+                        pitch_deg: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Ego->camera (R, t) for an outward-looking camera at ``yaw_deg``.
+
+    Rows of R are the camera axes written in the ego frame:
+    right = (sin psi, -cos psi, 0), down = (0, 0, -1), forward = (cos psi, sin psi, 0)
+    for pitch 0.  A positive ``pitch_deg`` tilts the optical axis upward
+    (rotation about the camera's right axis).  t = -R c with c the camera
+    centre at ``radius`` along psi and ``height`` above the ego origin.
+    """
+    psi = math.radians(yaw_deg)
+    th = math.radians(pitch_deg)
+    right = np.array([math.sin(psi), -math.cos(psi), 0.0])
+    fwd0 = np.array([math.cos(psi), math.sin(psi), 0.0])
+    up0 = np.array([0.0, 0.0, 1.0])
+    fwd = math.cos(th) * fwd0 + math.sin(th) * up0
+    down = -(math.cos(th) * up0 - math.sin(th) * fwd0)
+    R = np.stack([right, down, fwd])
+    c = np.array([radius * math.cos(psi), radius * math.sin(psi), height])
+    t = -R @ c
+    return R.astype(np.float32), t.astype(np.float32)
+
+
+def make_rig(cid: int, B: int, N: int, H: int, W: int, per_sample: bool,
+             jitter: bool = True) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Seeded ring rig: K [B,N,3,3], R [B,N,3,3], t [B,N,3], all fp32.
+
+    Sample b draws its yaw jitter from ``default_rng([cid, b, 0])`` when
+    ``per_sample`` is set; otherwise every sample reuses the b = 0 rig.
+    """
+    K = np.empty((B, N, 3, 3), np.float32)
+    R = np.empty((B, N, 3, 3), np.float32)
+    t = np.empty((B, N, 3), np.float32)
+    Kn = intrinsics(H, W)
+    for b in range(B):
+        g = np.random.default_rng([cid, b if per_sample else 0, 0])
+        jit = g.uniform(-YAW_JITTER_DEG, YAW_JITTER_DEG, N) if jitter else np.zeros(N)
+        for n in range(N):
+            Rn, tn = extrinsics_from_yaw(n * 360.0 / N + float(jit[n]))
+            K[b, n], R[b, n], t[b, n] = Kn, Rn, tn
+    return K, R, t
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bfloat16 (round-to-nearest-even), returned as uint16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(a)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to fp32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def make_features(cid: int, B: int, N: int, C: int, H: int, W: int, dtype: str = "f32") -> np.ndarray:
+    """Logical [B,N,C,H,W] features ~ N(0,1) from ``default_rng([cid, 1])``.
+
+    For ``dtype == "bf16"`` the fp32 draws are rounded to bfloat16 (RNE) and
+    returned as their exact fp32 values, so every consumer sees the same
+    numbers.
+    """
+    g = np.random.default_rng([cid, 1])
+    F = g.standard_normal((B, N, C, H, W), dtype=np.float32)
+    if dtype == "bf16":
+        F = bf16_bits_to_f32(to_bf16_bits(F))
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return F
+
+
+def make_grad_out(cid: int, B: int, C: int, X: int, Y: int) -> np.ndarray:
+    """Upstream gradient [B,C,X,Y] ~ N(0,1) from ``default_rng([cid, 2])``."""
+    g = np.random.default_rng([cid, 2])
+    return g.standard_normal((B, C, X, Y), dtype=np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    F: np.ndarray            # logical [B,N,C,H,W] fp32 values (bf16-representable when dtype == "bf16")
+    K: np.ndarray
+    R: np.ndarray
+    t: np.ndarray
+    rng6: Tuple[float, ...]
+    X: int
+    Y: int
+    Z: int
+    dtype: str
+    grad_out: Optional[np.ndarray] = None
+
+
+def make_inputs(name: str, dtype: Optional[str] = None, with_grad: bool = False, **override) -> Inputs:
+    """Inputs for a named workload; keyword overrides replace its sizes (same seeds)."""
+    w = dataclasses.replace(WORKLOADS[name], **override) if override else WORKLOADS[name]
+    dt = dtype or w.dtypes[0]
+    K, R, t = make_rig(w.cid, w.B, w.N, w.H, w.W, w.per_sample_rig)
+    F = make_features(w.cid, w.B, w.N, w.C, w.H, w.W, dt)
+    g = make_grad_out(w.cid, w.B, w.C, w.X, w.Y) if (with_grad or w.backward) else None
+    return Inputs(F, K, R, t, tuple(float(np.float32(r)) for r in w.rng6), w.X, w.Y, w.Z, dt, g)
+
+
+def random_case(seed: int, B: int, N: int, C: int, H: int, W: int, X: int, Y: int, Z: int,
+                rng6=(-50.0, 50.0, -50.0, 50.0, -5.0, 3.0), dtype: str = "f32",
+                per_sample: bool = True, with_grad: bool = True) -> Inputs:
+    """An arbitrary-size seeded case (used for ragged / edge-case parity runs)."""
+    K, R, t = make_rig(1000 + seed, B, N, H, W, per_sample)
+    F = make_features(1000 + seed, B, N, C, H, W, dtype)
+    g = make_grad_out(1000 + seed, B, C, X, Y) if with_grad else None
+    return Inputs(F, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y, Z, dtype, g)

@@ -1,0 +1,92 @@
+"""Scalar brute-force checker for the Sampling-VT oracle (pure Python, float64).
+
+TEST INFRASTRUCTURE ONLY; it shares no code with ``sampling_vt`` (which it
+checks) nor with the HIP path.
+
+It evaluates one output element at a time the way the FlashBEV notes describe
+the per-element gather-reduction ("Core Idea"; "Method" item 2): for cell
+(b, i, j), for every height bin k and camera n, build the voxel centre,
+transform it into the camera (p_cam = R p + t), apply K, divide by the depth,
+test depth > 0 and the closed in-view box [0, W-1] x [0, H-1], interpolate the
+four neighbouring pixels, average over the cameras that see the point, and add
+the per-bin means over k.  Written with explicit loops and ``math`` only.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+
+def _centre(lo: float, hi: float, n: int, i: int) -> float:
+    return lo + (i + 0.5) * (hi - lo) / n
+
+
+def _to_pixel(K, R, t, p) -> Tuple[float, float, float]:
+    pc = [R[r][0] * p[0] + R[r][1] * p[1] + R[r][2] * p[2] + t[r] for r in range(3)]
+    h = [K[r][0] * pc[0] + K[r][1] * pc[1] + K[r][2] * pc[2] for r in range(3)]
+    d = h[2]
+    if d == 0.0:
+        return d, math.inf, math.inf
+    return d, h[0] / d, h[1] / d
+
+
+def _sample(img_c, H: int, W: int, u: float, v: float) -> float:
+    """Bilinear value of one channel image ``img_c[y][x]`` at pixel-centre coords (u, v)."""
+    xl = math.floor(u)
+    yt = math.floor(v)
+    fx = u - xl
+    fy = v - yt
+    xr = xl + 1 if xl + 1 < W else W - 1
+    yb = yt + 1 if yt + 1 < H else H - 1
+    top = img_c[yt][xl] * (1.0 - fx) + img_c[yt][xr] * fx
+    bot = img_c[yb][xl] * (1.0 - fx) + img_c[yb][xr] * fx
+    return top * (1.0 - fy) + bot * fy
+
+
+def cell_value(F, K, R, t, rng6: Sequence[float], X: int, Y: int, Z: int,
+               b: int, i: int, j: int) -> Tuple[List[float], List[int]]:
+    """Output channels out[b, :, i, j] and the per-bin valid-camera counts.
+
+    F is indexable as F[b][n][c][y][x]; K, R as [b][n][3][3]; t as [b][n][3].
+    """
+    N = len(F[b])
+    C = len(F[b][0])
+    H = len(F[b][0][0])
+    W = len(F[b][0][0][0])
+    xmin, xmax, ymin, ymax, zmin, zmax = (float(r) for r in rng6)
+    px = _centre(xmin, xmax, X, i)
+    py = _centre(ymin, ymax, Y, j)
+    acc = [0.0] * C
+    counts = []
+    for k in range(Z):
+        p = (px, py, _centre(zmin, zmax, Z, k))
+        seen = []
+        for n in range(N):
+            d, u, v = _to_pixel(K[b][n], R[b][n], t[b][n], p)
+            if d > 0.0 and 0.0 <= u <= W - 1 and 0.0 <= v <= H - 1:
+                seen.append((n, u, v))
+        counts.append(len(seen))
+        if not seen:
+            continue
+        for c in range(C):
+            s = 0.0
+            for (n, u, v) in seen:
+                s += _sample(F[b][n][c], H, W, u, v)
+            acc[c] += s / len(seen)
+    return acc, counts
+
+
+def brute_forward(F, K, R, t, rng6, X: int, Y: int, Z: int):
+    """Whole output [B][C][X][Y] and counts [B][X][Y][Z] as nested lists (tiny sizes only)."""
+    B = len(F)
+    C = len(F[0][0])
+    out = [[[[0.0] * Y for _ in range(X)] for _ in range(C)] for _ in range(B)]
+    cnt = [[[None] * Y for _ in range(X)] for _ in range(B)]
+    for b in range(B):
+        for i in range(X):
+            for j in range(Y):
+                vals, cs = cell_value(F, K, R, t, rng6, X, Y, Z, b, i, j)
+                for c in range(C):
+                    out[b][c][i][j] = vals[c]
+                cnt[b][i][j] = cs
+    return out, cnt

@@ -1,0 +1,94 @@
+"""CPU: the oracle against its pins (brute force, closed forms, invariants, library routines)."""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+import oracle.sampling_vt as ovt
+from camera_bev_view_amd import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return wl.make_inputs("tiny", with_grad=True)
+
+
+@pytest.fixture(scope="module")
+def small():
+    return P.small_case(0)
+
+
+def test_p1_brute_force_tiny_workload(tiny):
+    P.pin_brute_force(tiny)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p1_brute_force_small_random(seed):
+    P.pin_brute_force(P.small_case(seed))
+
+
+def test_p2_constant_features(tiny, small):
+    P.pin_constant_features(tiny)
+    P.pin_constant_features(small)
+
+
+def test_p3_camera_permutation(tiny, small):
+    P.pin_camera_permutation(tiny)
+    P.pin_camera_permutation(small)
+
+
+def test_p4_zero_valid(small):
+    P.pin_zero_valid(small)
+    P.pin_behind_single_camera()
+
+
+def test_p5_closed_forms():
+    P.pin_closed_forms()
+
+
+def test_p6_linearity(small):
+    P.pin_linearity(small)
+
+
+def test_p7_adjoint(tiny, small):
+    P.pin_adjoint(tiny)
+    P.pin_adjoint(small)
+
+
+def test_p7_dense_jacobian():
+    P.pin_jacobian()
+
+
+def test_p8_rig_symmetry():
+    P.pin_rig_symmetry()
+
+
+def test_p9_library_bilinear():
+    P.pin_library_bilinear()
+
+
+def test_row_chunking_is_exact(monkeypatch, small):
+    """Building the stages a few X-rows at a time changes nothing (cells are independent)."""
+    full = ovt.oracle_forward(small.F, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z)
+    monkeypatch.setattr(ovt, "_MAX_CHUNK_ELEMS", 1)
+    part = ovt.oracle_forward(small.F, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z)
+    assert np.array_equal(full["out"], part["out"]) and np.array_equal(full["counts"], part["counts"])
+    rows = [4, 1]
+    sub = ovt.oracle_forward(small.F, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z, rows=rows)
+    assert np.array_equal(sub["out"], full["out"][:, :, rows])
+
+
+def test_workload_generator_is_seeded_and_bf16_exact():
+    a = wl.make_inputs("batched", dtype="bf16")
+    b = wl.make_inputs("batched", dtype="bf16")
+    assert np.array_equal(a.F, b.F) and np.array_equal(a.K, b.K)
+    bits = wl.to_bf16_bits(a.F)
+    assert np.array_equal(wl.bf16_bits_to_f32(bits), a.F)
+    # per-sample rigs differ, the shared rig does not
+    assert not np.array_equal(a.R[0], a.R[1])
+    s = wl.make_inputs("nuscenes")
+    assert s.K.shape == (1, 6, 3, 3)
+    # RNE: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 and rounds to the even mantissa (1.0)
+    assert wl.bf16_bits_to_f32(wl.to_bf16_bits(np.array([1 + 2 ** -8], np.float32)))[0] == 1.0
+    assert wl.bf16_bits_to_f32(wl.to_bf16_bits(np.array([1 + 3 * 2 ** -8], np.float32)))[0] == 1 + 2 ** -6
