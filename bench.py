@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Sampling-VT hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: fbev_forward (voxel
+centres, projection, validity, bilinear gather, valid-camera mean, height
+sum) followed by fbev_backward (zero-fill + atomic scatter of dL/dF) on the
+nuScenes-shaped workload: B=1, N=6 cameras, C=64, 16x44 fp32 features,
+200x200 BEV cells over +-50 m, Z=8 height bins over [-5, 3) m, seeded
+synthetic rig and N(0,1) features and upstream gradient.  Inputs are resident
+in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is BEV output elements per second of whole
+steps; per-pass figures (output elems/s, bilinear samples/s, algorithmic
+HBM GB/s) follow in ``forward`` / ``backward``; ``roofline`` covers the
+dominant kernel; ``cpu_baseline`` times the fp64 CPU oracle on the same
+workload (a reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BEV output elems/s + bilinear samples/s; achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "sampling_vt.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(kernel: str, algo_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
+    they were taken on a different kernel source (or never)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, rows):
+    """Time the fp64 oracle (forward + backward) on the first ``rows`` X-rows."""
+    import numpy as np
+    import oracle
+    H, W = inp.F.shape[-2:]
+    sel = list(range(rows))
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, rows=sel)
+    oracle.oracle_backward(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, H, W, rows=sel)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    B, C = inp.F.shape[0], inp.F.shape[2]
+    return {
+        "value": B * C * rows * inp.Y / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, forward + backward over X-rows 0..{rows - 1} of {inp.X} "
+                  f"({B * C * rows * inp.Y} outputs), wall {wall:.2f} s, process CPU {cpu:.2f} s, "
+                  f"{len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="nuscenes")
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--cpu-rows", type=int, default=None, help="X-rows of the CPU-oracle sample (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch sample or BEV rows with no exchange in the forward; "
+              "multi-GPU runs are not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from camera_bev_view_amd import ops
+    from camera_bev_view_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    inp = wl.make_inputs(args.workload, dtype=args.dtype, with_grad=True)
+    B, N, C, H, W = inp.F.shape
+    X, Y, Z = inp.X, inp.Y, inp.Z
+    dev = torch.device("cuda:0")
+    Fcl = torch.from_numpy(np.ascontiguousarray(inp.F.transpose(0, 1, 3, 4, 2)))
+    if inp.dtype == "bf16":
+        Fcl = Fcl.to(torch.bfloat16)
+    Fcl = Fcl.to(dev)
+    K, R, t = (torch.from_numpy(a).to(dev) for a in (inp.K, inp.R, inp.t))
+    g = torch.from_numpy(inp.grad_out).to(dev)
+    out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
+    es = Fcl.element_size()
+
+    # valid (cell, z, camera) samples, for the samples/s figures (outside the timed region)
+    _, cnt = ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, with_counts=True)
+    torch.cuda.synchronize()
+    valid_tuples = int(cnt.to(torch.int64).sum().item())
+    del cnt
+
+    def step():
+        ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, out=out)
+        return ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+
+    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done (x3)")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, out=out)
+        ev[k][1].record(stream)
+        ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+        ev[k][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
+
+    out_elems = B * C * X * Y
+    cam_bytes = B * N * 21 * 4
+    feat_bytes = B * N * H * W * C * es
+    fwd_bytes = feat_bytes + out_elems * 4 + cam_bytes            # features once, output once
+    bwd_bytes = out_elems * 4 + B * N * H * W * C * 4 + cam_bytes  # grad_out once, dL/dF once
+    samples = valid_tuples * C
+    logical = B * N * C * X * Y * Z
+
+    def rates(ms, nbytes):
+        s = ms * 1e-3
+        return {"ms": ms, "out_elems_per_s": out_elems / s, "bilinear_samples_per_s": samples / s,
+                "logical_samples_per_s": logical / s, "algorithmic_bytes": nbytes,
+                "hbm_gbps_algorithmic": nbytes / s / 1e9, "hbm_frac_algorithmic": nbytes / s / 1e9 / HBM_PEAK_GBPS}
+
+    fwd = rates(fwd_ms, fwd_bytes)
+    bwd = rates(bwd_ms, bwd_bytes)
+    dom_name, dom, dom_bytes = ("sampling_vt_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        ("sampling_vt_bwd", bwd, bwd_bytes)
+    achieved = dom["hbm_gbps_algorithmic"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, dom_bytes),
+                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+
+    line = {
+        "metric": METRIC,
+        "value": out_elems / (ms_step * 1e-3),
+        "unit": "BEV output elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
+        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
+        "config": {"workload": f"{args.workload}: B={B} N={N} C={C} HxW={H}x{W} {inp.dtype} -> "
+                               f"X*Y*Z={X}x{Y}x{Z}, one step = forward + backward",
+                   "B": B, "N": N, "C": C, "H": H, "W": W, "X": X, "Y": Y, "Z": Z,
+                   "valid_samples_per_pass": valid_tuples},
+        "bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3),
+        "forward": fwd,
+        "backward": bwd,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows or X)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,48 @@
+"""Build libflashbev.so in-tree with hipcc for gfx950.
+
+``python -m camera_bev_view_amd.build`` (or ``__graft_entry__.build()``)
+compiles the C-ABI host layer and the HIP kernels into
+``camera_bev_view_amd/libflashbev.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libflashbev.so")
+SOURCES = [os.path.join(CSRC, "flashbev_api.cpp"), os.path.join(CSRC, "sampling_vt.hip")]
+ARCH = "gfx950"
+
+# Packed-fp32 VALU forms are switched off for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libflashbev)")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source into libflashbev.so (always recompiles); returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+           "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra_flags, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

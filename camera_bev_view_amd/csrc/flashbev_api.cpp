@@ -1,0 +1,147 @@
+// C-ABI host layer of libflashbev: argument validation, launch-shape choice
+// and error reporting.  Every check runs on the host before anything is
+// enqueued, so a non-OK status means nothing was written.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "../../include/flashbev.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fbev_status fail(fbev_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+fbev_status fail(fbev_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool finite_range(float lo, float hi) { return std::isfinite(lo) && std::isfinite(hi) && hi > lo; }
+
+// Shared validation of the geometry arguments; fills `p` on success.
+fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* R, const float* t,
+                         const fbev_range& r, int32_t X, int32_t Y, int32_t Z, fbev::Problem& p) {
+  if (fd.B < 0 || fd.N < 0 || fd.C < 0 || fd.H < 0 || fd.W < 0)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "negative feature size (B=%d N=%d C=%d H=%d W=%d)", fd.B, fd.N, fd.C,
+                fd.H, fd.W);
+  if (X < 0 || Y < 0 || Z < 0) return fail(FBEV_ERR_INVALID_ARGUMENT, "negative grid size (X=%d Y=%d Z=%d)", X, Y, Z);
+  if (X > FBEV_MAX_GRID || Y > FBEV_MAX_GRID || Z > FBEV_MAX_GRID)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "grid size above %d (X=%d Y=%d Z=%d)", FBEV_MAX_GRID, X, Y, Z);
+  if (fd.N > FBEV_MAX_CAMERAS)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "N=%d cameras exceeds FBEV_MAX_CAMERAS=%d", fd.N, FBEV_MAX_CAMERAS);
+  if (fd.H > FBEV_MAX_GRID || fd.W > FBEV_MAX_GRID)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "feature map %dx%d above %d", fd.H, fd.W, FBEV_MAX_GRID);
+  if (!finite_range(r.x_min, r.x_max) || !finite_range(r.y_min, r.y_max) || !finite_range(r.z_min, r.z_max))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "each BEV range axis needs finite min < max");
+  if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "K, R and t must be non-NULL when B*N > 0");
+  p.K = K;
+  p.R = R;
+  p.t = t;
+  p.B = fd.B;
+  p.N = fd.N;
+  p.C = fd.C;
+  p.H = fd.H;
+  p.W = fd.W;
+  p.X = X;
+  p.Y = Y;
+  p.Z = Z;
+  // voxel centre of index i: min + (i + 1/2) (max - min) / n, evaluated in double
+  p.ox = (double)r.x_min;
+  p.dx = ((double)r.x_max - (double)r.x_min) / (X > 0 ? X : 1);
+  p.oy = (double)r.y_min;
+  p.dy = ((double)r.y_max - (double)r.y_min) / (Y > 0 ? Y : 1);
+  p.oz = (double)r.z_min;
+  p.dz = ((double)r.z_max - (double)r.z_min) / (Z > 0 ? Z : 1);
+  return FBEV_OK;
+}
+
+fbev_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FBEV_OK;
+  return fail(FBEV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K, const float* R,
+                         const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out,
+                         uint8_t* counts, void* stream) {
+  fbev::Problem p{};
+  fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  if (dtype != FBEV_DTYPE_F32 && dtype != FBEV_DTYPE_BF16)
+    return fail(FBEV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  const int es = (dtype == FBEV_DTYPE_F32) ? 4 : 2;
+  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  const int64_t n_cnt = (int64_t)fd.B * X * Y * Z;
+  if (n_feat > 0 && features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "features is NULL");
+  if (n_out > 0 && out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
+  if ((fd.C * es) % 4 != 0) return fail(FBEV_ERR_UNSUPPORTED, "bf16 features need an even C (got %d)", fd.C);
+  const int64_t batch_bytes = (int64_t)fd.N * fd.H * fd.W * fd.C * es;
+  if (batch_bytes >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld bytes (limit 2^31 - 1)",
+                (long long)batch_bytes);
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(features);
+  if (n_feat > 0 && (addr & 3) != 0) return fail(FBEV_ERR_UNSUPPORTED, "features must be 4-byte aligned");
+  p.feat = features;
+  p.elem_bytes = es;
+  p.vec_bytes = ((fd.C * es) % 16 == 0 && (addr & 15) == 0) ? 16 : 4;
+  if (n_out == 0 && (counts == nullptr || n_cnt == 0)) return FBEV_OK;
+  return device_status(fbev::launch_forward(p, n_out > 0 ? out : nullptr, n_cnt > 0 ? counts : nullptr,
+                                            static_cast<hipStream_t>(stream)),
+                       "fbev_forward launch");
+}
+
+fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R, const float* t,
+                          fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* grad_features,
+                          void* stream) {
+  fbev::Problem p{};
+  fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  if (n_feat > 0 && grad_features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_features is NULL");
+  if (n_out > 0 && n_feat > 0 && grad_out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  const int64_t batch_elems = (int64_t)fd.N * fd.H * fd.W * fd.C;
+  if (batch_elems >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "one sample's gradient spans %lld elements (limit 2^31 - 1)",
+                (long long)batch_elems);
+  p.feat = nullptr;
+  p.elem_bytes = 4;
+  p.vec_bytes = 4;
+  if (n_feat == 0) return FBEV_OK;
+  return device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
+                       "fbev_backward launch");
+}
+
+const char* fbev_status_string(fbev_status s) {
+  switch (s) {
+    case FBEV_OK: return "ok";
+    case FBEV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FBEV_ERR_UNSUPPORTED: return "unsupported";
+    case FBEV_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* fbev_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fbev_abi_version(void) { return FBEV_ABI_VERSION; }
+
+}  // extern "C"

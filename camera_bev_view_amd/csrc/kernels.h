@@ -1,0 +1,25 @@
+// Internal interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fbev {
+
+// Everything a launch needs, already validated by the host layer.
+struct Problem {
+  const void* feat;       // [B,N,H,W,C] channels-last (fp32 or bf16 bits)
+  const float* K;         // [B,N,3,3]
+  const float* R;         // [B,N,3,3]
+  const float* t;         // [B,N,3]
+  int B, N, C, H, W;
+  int X, Y, Z;
+  double ox, dx, oy, dy, oz, dz;   // voxel centre i -> o + (i + 1/2) d
+  int elem_bytes;         // 4 (fp32) or 2 (bf16)
+  int vec_bytes;          // bytes one lane moves per tap: 16 or 4
+};
+
+hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream);
+hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream);
+
+}  // namespace fbev

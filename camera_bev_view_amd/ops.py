@@ -1,0 +1,103 @@
+"""PyTorch-facing calls of libflashbev: argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+view transform runs in the library's kernels.  Names follow the notation of
+the FlashBEV reading notes: features F with B samples, N cameras, C channels
+on an H x W map; a BEV grid of X x Y cells and Z height bins.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.FBEV_DTYPE_F32, torch.bfloat16: _lib.FBEV_DTYPE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _check_cams(K: torch.Tensor, R: torch.Tensor, t: torch.Tensor, B: int, N: int, device) -> None:
+    for name, x, shape in (("K", K, (B, N, 3, 3)), ("R", R, (B, N, 3, 3)), ("t", t, (B, N, 3))):
+        if tuple(x.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(x.shape)}")
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.device != device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor on {device}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor,
+            bev_range: Sequence[float], X: int, Y: int, Z: int, *, with_counts: bool = False,
+            out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fbev_forward on channels-last features [B,N,H,W,C] (fp32 or bf16).
+
+    Returns (out [B,C,X,Y] fp32, counts [B,X,Y,Z] uint8 or None).
+    """
+    if features.dim() != 5:
+        raise ValueError("features must be [B,N,H,W,C]")
+    if features.dtype not in _DTYPES:
+        raise ValueError(f"unsupported feature dtype {features.dtype}")
+    if not features.is_cuda or not features.is_contiguous():
+        raise ValueError("features must be a contiguous device tensor")
+    B, N, H, W, C = features.shape
+    dev = features.device
+    _check_cams(K, R, t, B, N, dev)
+    if out is None:
+        out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
+    lib = _lib.load()
+    _lib.check(lib.fbev_forward(_ptr(features), _DTYPES[features.dtype], _lib.feat_desc(B, N, C, H, W),
+                                _ptr(K), _ptr(R), _ptr(t), _lib.bev_range(bev_range), X, Y, Z,
+                                _ptr(out), _ptr(counts), _stream(dev)))
+    return out, counts
+
+
+def backward(grad_out: torch.Tensor, feat_shape: Sequence[int], K: torch.Tensor, R: torch.Tensor,
+             t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, Z: int) -> torch.Tensor:
+    """fbev_backward: dL/dF as fp32 channels-last [B,N,H,W,C] from grad_out [B,C,X,Y]."""
+    B, N, H, W, C = (int(v) for v in feat_shape)
+    if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32 [B,C,X,Y]")
+    grad_out = grad_out.contiguous()
+    dev = grad_out.device
+    _check_cams(K, R, t, B, N, dev)
+    gF = torch.empty((B, N, H, W, C), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.fbev_backward(_ptr(grad_out), _lib.feat_desc(B, N, C, H, W), _ptr(K), _ptr(R), _ptr(t),
+                                 _lib.bev_range(bev_range), X, Y, Z, _ptr(gF), _stream(dev)))
+    return gF
+
+
+class SamplingVT(torch.autograd.Function):
+    """Autograd wrapper: gradient with respect to the features only."""
+
+    @staticmethod
+    def forward(ctx, features, K, R, t, bev_range, X, Y, Z):
+        out, _ = forward(features, K, R, t, bev_range, X, Y, Z)
+        ctx.save_for_backward(K, R, t)
+        ctx.meta = (tuple(features.shape), features.dtype, tuple(bev_range), X, Y, Z)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        K, R, t = ctx.saved_tensors
+        shape, dtype, rng, X, Y, Z = ctx.meta
+        gF = backward(grad_out.float(), shape, K, R, t, rng, X, Y, Z)
+        return gF.to(dtype), None, None, None, None, None, None, None
+
+
+def bev_sample(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor,
+               bev_range: Sequence[float], X: int, Y: int, Z: int, channels_last: bool = True) -> torch.Tensor:
+    """Differentiable Sampling-VT.  ``channels_last=False`` accepts [B,N,C,H,W] and
+    permutes it to the library's [B,N,H,W,C] layout first (one copy)."""
+    if not channels_last:
+        features = features.permute(0, 1, 3, 4, 2).contiguous()
+    return SamplingVT.apply(features, K, R, t, tuple(bev_range), X, Y, Z)

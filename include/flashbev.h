@@ -1,0 +1,124 @@
+/*
+ * libflashbev -- exact dense Sampling-VT camera-to-BEV view transform, fused,
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI: no C++ types, no exceptions,
+ * no framework types cross this boundary.
+ *
+ * The operation (FlashBEV reading notes, "Problem Setting", "Core Idea" and
+ * "Method" items 1-4): for every batch sample b, BEV cell (x, y) and channel c,
+ *
+ *   out[b,c,x,y] = sum_z  mean_{n valid at (b,x,y,z)}  bilinear(F[b,n,:,:,c], u, v)
+ *
+ * where, for height bin z, the voxel centre p = (x_x, y_y, z_z) is projected
+ * through camera n as [u, v, 1]^T ~ K_n (R_n p + t_n) (SparseDriveV2 notes,
+ * "Deformable Aggregation", step 2) and camera n is valid when the depth
+ * d = (K_n (R_n p + t_n))_3 > 0 and the point lands in the image.  A point
+ * no camera sees contributes 0.  Nothing per (camera, height, channel) is
+ * stored in device memory: projection, validity test, sampling, mean and
+ * height sum happen in one kernel.
+ *
+ * Conventions (the pages leave these open; this library fixes them):
+ *   - voxel centres of the half-open ranges: x_i = x_min + (i + 1/2)(x_max - x_min)/X,
+ *     likewise y_j, z_k; out[b, c, i, j] has i along ego x, j along ego y;
+ *   - (R, t) maps ego to camera coordinates, p_cam = R p + t;
+ *   - integer (u, v) are pixel centres, u along W (columns), v along H (rows);
+ *     "in the image" means 0 <= u <= W-1 and 0 <= v <= H-1 (closed), so every
+ *     valid sample is a convex combination of existing pixels;
+ *   - bilinear taps x0 = floor(u), x1 = min(x0 + 1, W - 1), likewise rows;
+ *   - projection and the in-image test are evaluated in double precision;
+ *     interpolation weights and accumulation are fp32.
+ *
+ * Memory: every pointer is caller-owned *device* memory unless stated.  The
+ * library allocates no device memory and keeps no state beyond the calling
+ * thread's last-error text.  All work is enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream) and calls return before it completes.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * on a non-OK status nothing has been written.  FBEV_ERR_DEVICE reports a
+ * launch error from the HIP runtime; fbev_last_error() gives the text.
+ */
+#ifndef FLASHBEV_H
+#define FLASHBEV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FBEV_ABI_VERSION 1
+#define FBEV_MAX_CAMERAS 64
+#define FBEV_MAX_GRID 65536
+
+typedef enum {
+  FBEV_OK = 0,
+  FBEV_ERR_INVALID_ARGUMENT = 1, /* negative size, NULL pointer for a non-empty buffer, bad range, N > FBEV_MAX_CAMERAS */
+  FBEV_ERR_UNSUPPORTED = 2,      /* unknown dtype, odd C for bf16, misaligned features, per-sample features >= 2 GiB */
+  FBEV_ERR_DEVICE = 3            /* the HIP runtime reported an error when enqueueing */
+} fbev_status;
+
+typedef enum { FBEV_DTYPE_F32 = 0, FBEV_DTYPE_BF16 = 1 } fbev_dtype;
+
+/* Feature maps are channels-last [B, N, H, W, C], contiguous. */
+typedef struct {
+  int32_t B, N, C, H, W;
+} fbev_feat_desc;
+
+/* BEV extent in metres, ego frame; each axis is the half-open [min, max). */
+typedef struct {
+  float x_min, x_max, y_min, y_max, z_min, z_max;
+} fbev_range;
+
+/*
+ * Forward of the fused Sampling-VT (FlashBEV notes, "Method" items 1-2).
+ *
+ *   features : [B,N,H,W,C] of `dtype` (fp32, or bf16 bit patterns), device, read only.
+ *              Must be 4-byte aligned; 16-byte alignment with C*elem_size a
+ *              multiple of 16 takes the wide-load path.
+ *   K        : [B,N,3,3] fp32 intrinsics (feature-map pixels), device.
+ *   R, t     : [B,N,3,3] and [B,N,3] fp32 ego->camera extrinsics, device.
+ *   bev_range, X, Y, Z : the voxel grid (X, Y, Z >= 0, each <= FBEV_MAX_GRID).
+ *   out      : [B,C,X,Y] fp32, device; fully overwritten (zero where no camera
+ *              sees any height bin, all zeros when Z == 0).
+ *   counts   : [B,X,Y,Z] uint8 valid-camera counts, device, or NULL to skip.
+ *
+ * Sizes of zero are allowed and give the empty / all-zero result.  The result
+ * is deterministic (fixed reduction order).
+ */
+fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K,
+                         const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                         int32_t Z, float* out, uint8_t* counts, void* stream);
+
+/*
+ * Gradient of fbev_forward with respect to the features (FlashBEV notes,
+ * "Method" item 4: the fused operator keeps the forward/backward semantics
+ * of the tensorized one).  The forward is linear in the features with the
+ * validity mask, bilinear weights and camera counts fixed, so
+ *
+ *   dF[b,n,y,x,c] = sum over (cell, z) valid for n, and taps of that sample
+ *                   landing on (y, x), of grad_out[b,c,cell] * w_tap / count.
+ *
+ *   grad_out      : [B,C,X,Y] fp32, device, read only.
+ *   grad_features : [B,N,H,W,C] fp32, device; fully overwritten (zeroed on
+ *                   `stream`, then accumulated with fp32 atomics, so the
+ *                   bit pattern may vary from run to run within fp32
+ *                   rounding).  Returned in fp32 also for bf16 forwards.
+ * Other arguments as for fbev_forward; no feature values are needed.
+ */
+fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,
+                          const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z,
+                          float* grad_features, void* stream);
+
+/* Static text for a status code. */
+const char* fbev_status_string(fbev_status s);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* fbev_last_error(void);
+
+/* FBEV_ABI_VERSION of the built library. */
+int32_t fbev_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHBEV_H */

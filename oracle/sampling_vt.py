@@ -210,7 +210,7 @@ def oracle_forward(F: np.ndarray, K: np.ndarray, R: np.ndarray, t: np.ndarray, r
 
 
 def oracle_backward(grad_out: np.ndarray, K: np.ndarray, R: np.ndarray, t: np.ndarray, rng6: Sequence[float],
-                    X: int, Y: int, Z: int, H: int, W: int) -> np.ndarray:
+                    X: int, Y: int, Z: int, H: int, W: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Gradient of the forward w.r.t. the features, [B,N,C,H,W] float64.
 
     The forward is linear in F once the mask, bilinear weights and counts are
@@ -226,14 +226,15 @@ def oracle_backward(grad_out: np.ndarray, K: np.ndarray, R: np.ndarray, t: np.nd
     N = K.shape[1]
     gF = np.zeros((B, N, C, H, W), np.float64)
     step = _rows_per_chunk(N, C, Y, Z)
+    all_rows = np.arange(X) if rows is None else np.asarray(rows, np.int64)
     for b in range(B):
         acc = np.zeros((C, N * H * W), np.float64)
-        for s in range(0, X, step):
-            r = np.arange(s, min(X, s + step))
+        for s in range(0, len(all_rows), step):
+            r = all_rows[s:s + step]
             grid = voxel_grid(rng6, X, Y, Z, r)
             d, u, v = project(grid, K[b], R[b], t[b])
             mask = in_view_mask(d, u, v, H, W)
-            g_m = np.broadcast_to(grad_out[b, :, s:s + len(r), :, None], (C, len(r), Y, Z))   # adjoint of height sum
+            g_m = np.broadcast_to(grad_out[b][:, r][:, :, :, None], (C, len(r), Y, Z))         # adjoint of height sum
             scale = valid_mean_adjoint_scale(mask)                                           # adjoint of valid mean
             g_s = g_m[None] * scale[:, None]                                                 # [N, C, r, Y, Z]
             n_idx = np.arange(N).reshape(N, 1, 1, 1)

@@ -1,0 +1,201 @@
+"""GPU: libflashbev through its C ABI against the fp64 oracle.
+
+Every case prints its label before the GPU work starts, so a failing run
+names it.  Parity rules are in gpu_helpers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from camera_bev_view_amd import ops
+from camera_bev_view_amd import workloads as wl
+from gpu_helpers import BWD_REL_L2, check_forward, rel_l2, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def run_forward(inp, with_counts=True):
+    F, K, R, t = to_device(inp)
+    out, cnt = ops.forward(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, with_counts=with_counts)
+    torch.cuda.synchronize()
+    return out, cnt
+
+
+def forward_parity(inp, label, rows=None):
+    say(f"[case] {label}: B,N,C,H,W={inp.F.shape} X,Y,Z={inp.X},{inp.Y},{inp.Z} dtype={inp.dtype}")
+    out, cnt = run_forward(inp)
+    ref = oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, rows=rows)
+    check_forward(out, cnt, ref, rows=rows, label=label)
+    return out, cnt, ref
+
+
+def test_tiny_full():
+    forward_parity(wl.make_inputs("tiny"), "tiny 1x6x16x8x22 -> 50x50x4")
+
+
+def test_nuscenes_full():
+    forward_parity(wl.make_inputs("nuscenes"), "nuscenes 1x6x64x16x44 -> 200x200x8")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batched_sampled_rows(dtype):
+    inp = wl.make_inputs("batched", dtype=dtype)
+    forward_parity(inp, f"batched 4x6x80x32x88 {dtype} -> 200x200x16 (rows sampled)", rows=[0, 37, 99, 100, 163, 199])
+
+
+def test_large_sampled_rows_and_no_materialisation():
+    inp = wl.make_inputs("large")
+    say("[case] large 1x6x128x64x176 bf16 -> 400x400x32")
+    F, K, R, t = to_device(inp)
+    out = torch.empty((1, 128, 400, 400), dtype=torch.float32, device=F.device)
+    ops.forward(F, K, R, t, inp.rng6, 400, 400, 32, out=out)       # loads the code object
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    torch.cuda.reset_peak_memory_stats()
+    alloc0 = torch.cuda.memory_allocated()
+    ops.forward(F, K, R, t, inp.rng6, 400, 400, 32, out=out)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert torch.cuda.max_memory_allocated() == alloc0
+    # the tensorized Features3D alone would be 6*128*400*400*32*4 B = 15.7 GB
+    assert free0 - free1 < (64 << 20), (free0, free1)
+    rows = [0, 133, 200, 399]
+    _, cnt = ops.forward(F, K, R, t, inp.rng6, 400, 400, 32, with_counts=True)
+    torch.cuda.synchronize()
+    ref = oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, 400, 400, 32, rows=rows)
+    check_forward(out, cnt, ref, rows=rows, label="large (rows sampled)")
+
+
+def test_fwdbwd_workload():
+    inp = wl.make_inputs("fwdbwd")
+    B, N, C, H, W = inp.F.shape
+    label = "fwdbwd 2x6x64x16x44 -> 256x256x16"
+    forward_parity(inp, label + " fwd (rows sampled)", rows=[0, 64, 127, 128, 255])
+    say(f"[case] {label} bwd (full)")
+    F, K, R, t = to_device(inp)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    gF = ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, inp.X, inp.Y, inp.Z)
+    torch.cuda.synchronize()
+    got = gF.cpu().numpy().transpose(0, 1, 4, 2, 3)
+    ref = oracle.oracle_backward(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, H, W)
+    err = rel_l2(got, ref)
+    say(f"[parity] {label} bwd rel L2 = {err:.3e}")
+    assert err <= BWD_REL_L2
+    # adjoint identity <g, fwd(f)> = <bwd(g), f> on the GPU results, at full size
+    out, _ = ops.forward(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z)
+    torch.cuda.synchronize()
+    lhs = float(np.sum(inp.grad_out.astype(np.float64) * out.cpu().numpy()))
+    rhs = float(np.sum(got.astype(np.float64) * inp.F.astype(np.float64)))
+    say(f"[parity] adjoint identity: {lhs:.9e} vs {rhs:.9e}")
+    assert abs(lhs - rhs) <= 1e-5 * abs(lhs)
+
+
+RAGGED = [
+    # dtype, B, N, C, H, W, X, Y, Z      what it exercises
+    ("f32", 1, 6, 20, 16, 44, 37, 45, 5),     # 5 chunks/pixel, 12 slots (linear slot sum), ragged tile
+    ("bf16", 2, 6, 80, 32, 88, 9, 70, 9),     # 10 chunks, 6 slots, two samples with their own rigs
+    ("f32", 1, 5, 7, 12, 30, 11, 33, 6),      # C*4 not a multiple of 16: 4-byte lane chunks
+    ("bf16", 1, 6, 6, 8, 22, 10, 31, 4),      # bf16, 4-byte chunks of two channels
+    ("f32", 1, 6, 260, 8, 22, 5, 33, 3),      # two channel groups (64 + 1 chunks)
+    ("bf16", 1, 6, 512, 8, 22, 3, 40, 4),     # two bf16 channel groups
+    ("f32", 1, 64, 16, 8, 22, 6, 35, 3),      # the maximum camera count: one height bin per pass
+    ("f32", 3, 1, 64, 16, 44, 21, 19, 8),     # one camera
+    ("f32", 1, 11, 32, 16, 44, 13, 64, 17),   # 5 bins per pass, 4 passes
+    ("f32", 1, 6, 64, 16, 44, 1, 1, 8),       # a single cell
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "x".join(map(str, c)))
+def test_ragged_forward(case):
+    dt, B, N, C, H, W, X, Y, Z = case
+    inp = wl.random_case(sum(case[1:]), B, N, C, H, W, X, Y, Z, rng6=(-30.0, 30.0, -30.0, 30.0, -5.0, 3.0), dtype=dt)
+    forward_parity(inp, "ragged " + "x".join(map(str, case)))
+
+
+BWD_CASES = [
+    ("f32", 1, 6, 20, 16, 44, 37, 45, 5),
+    ("f32", 2, 6, 200, 8, 22, 7, 40, 4),      # two backward channel groups (128 + 72)
+    ("f32", 1, 5, 7, 12, 30, 11, 33, 6),
+    ("f32", 1, 64, 16, 8, 22, 6, 35, 3),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_ragged_backward(case):
+    dt, B, N, C, H, W, X, Y, Z = case
+    inp = wl.random_case(sum(case[1:]) + 1, B, N, C, H, W, X, Y, Z, rng6=(-30.0, 30.0, -30.0, 30.0, -5.0, 3.0))
+    say(f"[case] backward {case}")
+    _, K, R, t = to_device(inp)
+    gF = ops.backward(torch.from_numpy(inp.grad_out).cuda(), (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+    torch.cuda.synchronize()
+    got = gF.cpu().numpy().transpose(0, 1, 4, 2, 3)
+    ref = oracle.oracle_backward(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, X, Y, Z, H, W)
+    err = rel_l2(got, ref)
+    say(f"[parity] backward {case}: rel L2 = {err:.3e}, max|d| = {np.abs(got - ref).max():.3e}")
+    assert err <= BWD_REL_L2
+    assert np.abs(got - ref).max() <= 1e-4 + 1e-5 * np.abs(ref).max()
+
+
+def test_degenerate_cases():
+    say("[case] degenerate: no cameras, Z = 0, C = 0 with counts, width-1 and height-1 maps, nothing in view")
+    inp = wl.random_case(5, 2, 0, 8, 8, 22, 9, 40, 3)
+    out, cnt = run_forward(inp)
+    assert not out.any() and not cnt.any() and cnt.shape == (2, 9, 40, 3)
+    inp = wl.random_case(6, 1, 6, 8, 8, 22, 9, 40, 0)
+    out, cnt = run_forward(inp)
+    assert out.shape == (1, 8, 9, 40) and not out.any() and cnt.numel() == 0
+    inp = wl.random_case(7, 1, 6, 0, 8, 22, 9, 40, 3)
+    out, cnt = run_forward(inp)
+    ref = oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, 9, 40, 3)
+    assert out.numel() == 0 and np.array_equal(cnt.cpu().numpy(), ref["counts"])
+    for (H, W) in [(1, 22), (8, 1), (1, 1)]:
+        forward_parity(wl.random_case(8, 1, 6, 16, H, W, 12, 33, 4, rng6=(-20.0, 20.0, -20.0, 20.0, -5.0, 3.0)),
+                       f"map {H}x{W}")
+    inp = wl.random_case(9, 1, 6, 16, 8, 22, 12, 33, 4)
+    inp.t = inp.t - np.einsum("bnij,j->bni", inp.R, np.array([0, 0, 1e4], np.float32)).astype(np.float32)
+    out, cnt = run_forward(inp)
+    assert not out.any() and not cnt.any()
+
+
+def test_gpu_invariants():
+    inp = wl.make_inputs("nuscenes")
+    say("[case] invariants on nuscenes: constant features, camera permutation, determinism")
+    F, K, R, t = to_device(inp)
+    a, cnt = ops.forward(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, with_counts=True)
+    b, _ = ops.forward(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "forward is not deterministic"
+    const = torch.full_like(F, 1.75)
+    o, c = ops.forward(const, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, with_counts=True)
+    torch.cuda.synchronize()
+    nz = (c >= 1).sum(-1).float()                          # [B, X, Y]
+    assert torch.allclose(o, 1.75 * nz[:, None].expand_as(o), rtol=1e-6, atol=1e-5)
+    perm = torch.tensor([3, 0, 5, 1, 4, 2], device=F.device)
+    p, pc = ops.forward(F[:, perm].contiguous(), K[:, perm].contiguous(), R[:, perm].contiguous(),
+                        t[:, perm].contiguous(), inp.rng6, inp.X, inp.Y, inp.Z, with_counts=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, cnt)
+    assert torch.allclose(p, a, rtol=1e-5, atol=1e-5)
+
+
+def test_autograd_function_and_layout():
+    inp = wl.random_case(11, 1, 6, 24, 16, 44, 17, 35, 6, rng6=(-30.0, 30.0, -30.0, 30.0, -5.0, 3.0))
+    say("[case] autograd through bev_sample with [B,N,C,H,W] input")
+    F = torch.from_numpy(inp.F).cuda().requires_grad_(True)
+    _, K, R, t = to_device(inp)
+    out = ops.bev_sample(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, channels_last=False)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    out.backward(g)
+    torch.cuda.synchronize()
+    ref = oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z)
+    check_forward(out.detach(), None, ref, label="autograd fwd")
+    refg = oracle.oracle_backward(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, 16, 44)
+    assert rel_l2(F.grad.cpu().numpy(), refg) <= BWD_REL_L2

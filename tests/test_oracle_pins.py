@@ -92,3 +92,15 @@ def test_workload_generator_is_seeded_and_bf16_exact():
     # RNE: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 and rounds to the even mantissa (1.0)
     assert wl.bf16_bits_to_f32(wl.to_bf16_bits(np.array([1 + 2 ** -8], np.float32)))[0] == 1.0
     assert wl.bf16_bits_to_f32(wl.to_bf16_bits(np.array([1 + 3 * 2 ** -8], np.float32)))[0] == 1 + 2 ** -6
+
+
+def test_backward_row_restriction_is_exact(small):
+    """The backward restricted to some X-rows equals the full backward of a grad that is zero elsewhere."""
+    H, W = small.F.shape[-2:]
+    rows = [1, 4, 5]
+    g = np.zeros_like(small.grad_out)
+    g[:, :, rows] = small.grad_out[:, :, rows]
+    full = ovt.oracle_backward(g, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z, H, W)
+    part = ovt.oracle_backward(small.grad_out, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z,
+                               H, W, rows=rows)
+    np.testing.assert_allclose(part, full, rtol=0, atol=1e-13)
