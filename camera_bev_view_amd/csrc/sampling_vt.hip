@@ -9,28 +9,40 @@
 //
 // What differs from the thread-per-output design the notes describe (one
 // thread per (b, x, y, c) that recomputes the geometry for every channel,
-// "Method" items 2-3, and flagged there as the cost that grows with C,
-// "Limitation" item 2): here the geometry is computed once per
-// (cell, height bin, camera) and shared by all channels of the cell.
+// "Method" items 2-3, flagged there as the cost that grows with C,
+// "Limitation" item 2): the geometry is computed once per
+// (cell, height bin, camera) and shared by all channels of the cell, and the
+// expensive part of it (division, floor, weights) only for the samples that
+// turn out to be in view.
 //
-//   * One workgroup = 4 wavefronts = one tile of kTileY consecutive cells along
-//     y in one x row of one batch sample (one channel group).  The camera
-//     matrices P = K [R | t] are staged in LDS in double precision.
-//   * A wavefront owns one cell at a time.  Its 64 lanes first act as
-//     (height bin, camera) tuples: each lane projects one voxel centre in
-//     fp64, applies the in-view test, and the wave counts valid cameras per
-//     height bin with one ballot.  Valid lanes compact their four bilinear
-//     taps (byte offset, weight * 1/count) into an LDS record list.
-//   * The same lanes then act as channel chunks: lane = (slot, q), q picks a
-//     16-byte chunk of the pixel's channels (4 fp32 or 8 bf16 channels) and
-//     the 64/Q slots walk different records.  Channels-last features make each
-//     tap one coalesced C*elem-byte read; accumulation is fp32 in registers.
-//   * Slots are summed with cross-lane shuffles, the cell's channels go to an
-//     LDS tile, and the tile leaves as coalesced rows of the [B,C,X,Y] output.
+// Geometry, per wavefront, in three phases over a batch of "items" (one item
+// = one cell and a block of up to 64/N height bins):
+//   A  validity: lane = (bin, camera).  The projective coordinates
+//      h = P [p; 1] are affine in the voxel centre, and "depth > 0,
+//      0 <= u <= W-1, 0 <= v <= H-1" equals five sign tests on h, so no
+//      division is needed to decide validity.  One ballot gives every bin's
+//      valid-camera count; valid lanes append a small descriptor to a
+//      wave-private list in LDS.
+//   B  taps: lane = one listed (valid) sample.  Divide in fp64 (reciprocal
+//      estimate + two Newton steps), split into integer tap and fp32
+//      fraction, and write the four (offset, weight / count) records.
+//   C  gather (forward) or scatter (backward) over the records.
 //
-// The backward reuses the geometry and scatters grad * weight / count onto
-// the four taps with fp32 atomics (no feature values needed: the map is
-// linear in the features).
+// Forward gather: lanes = (slot, q).  q selects D consecutive dwords of the
+// pixel's channel group, so a tap is one coalesced channels-last read; the
+// 64/L slots take different taps (and samples).  Accumulation is fp32 in
+// registers; slots are summed with lane swaps, the cell's channels go to an
+// LDS tile, and the tile leaves as coalesced rows of the [B,C,X,Y] output.
+//
+// Backward (gradient with respect to the features; the map is linear in
+// them): one workgroup = a 4 x 8 block of cells and one group of <= 64
+// channels.  Each tap's pixel is inserted into a workgroup-private hash table
+// in LDS (integer compare-and-swap) and gets a rank within its pixel from an
+// integer LDS atomic; a counting sort then makes every pixel's contributions
+// contiguous, a wave sums them per channel in registers (grad * weight /
+// count, grad read from an LDS tile), and each distinct pixel leaves the
+// workgroup with one fp32 global atomic per channel.  LDS float atomics are
+// avoided on purpose: on this chip they are far slower than integer ones.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,15 +55,30 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kBlock = kWave * kWaves;
-constexpr int kTileY = 32;             // cells per workgroup
-constexpr int kTileLd = kTileY + 1;    // padded LDS row of the output tile
-constexpr int kRecPerWave = 4 * kWave; // taps of one geometry pass
-constexpr int kMaxGroupCh = 256;       // channels per workgroup (one channel group)
-constexpr int kBwdLanes = 16;          // lanes per tap slot in the backward
-constexpr int kBwdMaxCh = 128;         // channels per backward channel group
+constexpr int kOutOfRange = 0x7ffffff0;  // buffer offset the range check turns into a zero load
+
+// forward
+constexpr int kTileY = 32;               // cells per workgroup (one x row)
+constexpr int kTileLd = kTileY + 1;      // padded LDS row of the output tile
+constexpr int kPend = 96;                // listed valid samples per wave
+constexpr int kItems = 16;               // items per batch
+constexpr int kRec = 4 * kPend;          // tap records per wave
+constexpr int kUnroll = 8;               // loads in flight per lane and step
+
+// backward
+constexpr int kBwdTX = 4;                // tile rows along x
+constexpr int kBwdTY = 8;                // tile cells along y
+constexpr int kBwdCells = kBwdTX * kBwdTY;
+constexpr int kBwdGLd = kBwdCells + 1;   // padded grad-tile row
+constexpr int kBwdCg = 64;               // channels per group (one per lane)
+constexpr int kSlots = 256;              // hash-table entries (power of two)
+constexpr int kSlotBits = 8;
+constexpr int kOver = 64;                // per-wave queue of taps that found no table slot
+constexpr int kProbes = 32;
+constexpr int kBwdRegion = 512;          // tap records per wave and round
 
 struct Rec {
-  int off;   // byte (forward) or element (backward) offset of the tap within the batch sample
+  int off;   // forward: byte offset of the tap's pixel
   float w;   // bilinear weight / valid-camera count
 };
 
@@ -82,31 +109,11 @@ __device__ void stage_cameras(double* sP, const float* K, const float* R, const 
   }
 }
 
-// Projection of one voxel centre through one camera and the in-view test
-// (SparseDriveV2 notes, "Deformable Aggregation" step 2; closed pixel-centre
-// box).  Returns false for an invalid sample; otherwise the top-left tap and
-// the fp32 fractions.
-__device__ __forceinline__ bool project_sample(const double* P, double px, double py, double pz, int H, int W,
-                                               int& x0, int& y0, float& fa, float& fb) {
-  const double h0 = fma(P[0], px, fma(P[1], py, fma(P[2], pz, P[3])));
-  const double h1 = fma(P[4], px, fma(P[5], py, fma(P[6], pz, P[7])));
-  const double h2 = fma(P[8], px, fma(P[9], py, fma(P[10], pz, P[11])));
-  if (!(h2 > 0.0)) return false;
-  const double r = 1.0 / h2;
-  const double u = h0 * r, v = h1 * r;
-  if (!(u >= 0.0 && u <= (double)(W - 1) && v >= 0.0 && v <= (double)(H - 1))) return false;
-  const double fu = floor(u), fv = floor(v);
-  x0 = (int)fu;
-  y0 = (int)fv;
-  fa = (float)(u - fu);
-  fb = (float)(v - fv);
-  return true;
-}
-
-// Rank of this lane among the set bits of `mask` below it.
 __device__ __forceinline__ int rank_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -114,116 +121,178 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Geometry pass for one cell and a block of height bins [zc, zc + zpc):
-// lane = (zl, n).  Writes the compacted tap records of the valid samples
-// (offsets in units of `pix_stride` per pixel plus `group_off`) and returns
-// the number of valid samples.  `cnt_out` receives the valid-camera count of
-// this lane's height bin; `writer_out` marks one lane per in-range bin.
-__device__ __forceinline__ int geometry_pass(const double* sP, Rec* rec, double px, double py, double oz,
-                                             double dz, int zc, int zpc, int Z, int N, int H, int W,
-                                             int pix_stride, int group_off, int lane, int& z_out, int& cnt_out,
-                                             bool& writer_out) {
-  const int Nn = (N > 0) ? N : 1;
-  const int zl = lane / Nn;
-  const int n = lane - zl * Nn;
-  const int z = zc + zl;
-  const bool in_range = (lane < zpc * Nn) && (z < Z);
-  const bool active = in_range && (N > 0);
-  int x0 = 0, y0 = 0;
-  float fa = 0.f, fb = 0.f;
-  bool valid = false;
-  if (active) {
-    const double pz = oz + ((double)z + 0.5) * dz;
-    valid = project_sample(sP + n * 12, px, py, pz, H, W, x0, y0, fa, fb);
-  }
-  const uint64_t mask = __ballot(valid);
-  const uint64_t grp_mask = (Nn >= 64) ? ~0ull : ((1ull << Nn) - 1ull);
-  const int shift = zl * Nn;
-  const int cnt = (active && shift < 64) ? (int)__popcll((mask >> shift) & grp_mask) : 0;
-  if (valid) {
-    const float rc = 1.0f / (float)cnt;
-    const int x1 = min(x0 + 1, W - 1);
-    const int y1 = min(y0 + 1, H - 1);
-    const int row0 = (n * H + y0) * W, row1 = (n * H + y1) * W;
-    const int pos = 4 * rank_below(mask);
-    const float wa0 = (1.0f - fa) * rc, wa1 = fa * rc;
-    const float wb0 = 1.0f - fb, wb1 = fb;
-    rec[pos + 0] = Rec{(row0 + x0) * pix_stride + group_off, wa0 * wb0};
-    rec[pos + 1] = Rec{(row0 + x1) * pix_stride + group_off, wa1 * wb0};
-    rec[pos + 2] = Rec{(row1 + x0) * pix_stride + group_off, wa0 * wb1};
-    rec[pos + 3] = Rec{(row1 + x1) * pix_stride + group_off, wa1 * wb1};
-  }
-  z_out = z;
-  cnt_out = cnt;
-  writer_out = in_range && n == 0;
-  return (int)__popcll(mask);
+// 1/x in double: hardware estimate plus two Newton steps.
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
 }
 
-template <int VB, bool BF16>
-struct Chunk;
-
-template <>
-struct Chunk<16, false> {
-  static constexpr int kVec = 4;
-  __device__ static void fma_into(float* acc, __amdgpu_buffer_rsrc_t rs, int off, float w) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    acc[0] = fmaf(w, __uint_as_float(v[0]), acc[0]);
-    acc[1] = fmaf(w, __uint_as_float(v[1]), acc[1]);
-    acc[2] = fmaf(w, __uint_as_float(v[2]), acc[2]);
-    acc[3] = fmaf(w, __uint_as_float(v[3]), acc[3]);
-  }
+// Camera rows of one lane for phase A: h = A + Bc * py + Cc * pz with
+// A = P[:,0] * px + P[:,3] (px is fixed for the item's cell).
+struct LaneCam {
+  double A[3], Bc[3], Cc[3];
 };
 
-template <>
-struct Chunk<4, false> {
-  static constexpr int kVec = 1;
-  __device__ static void fma_into(float* acc, __amdgpu_buffer_rsrc_t rs, int off, float w) {
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-    acc[0] = fmaf(w, __uint_as_float(v), acc[0]);
-  }
-};
-
-template <>
-struct Chunk<16, true> {
-  static constexpr int kVec = 8;
-  __device__ static void fma_into(float* acc, __amdgpu_buffer_rsrc_t rs, int off, float w) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+__device__ __forceinline__ LaneCam lane_camera(const double* sP, int n, int N, double px) {
+  LaneCam lc;
+  const double* P = sP + (N > 0 ? n : 0) * 12;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
+  for (int i = 0; i < 3; ++i) {
+    lc.A[i] = (N > 0) ? fma(P[4 * i], px, P[4 * i + 3]) : 0.0;
+    lc.Bc[i] = (N > 0) ? P[4 * i + 1] : 0.0;
+    lc.Cc[i] = (N > 0) ? P[4 * i + 2] : 0.0;
+  }
+  return lc;
+}
+
+// Phase A for one item: lane = (zl, n).  Validity by sign tests on
+// h = P [p; 1] (SparseDriveV2 notes, "Deformable Aggregation" step 2:
+// [u, v, 1]^T ~ K (R p + t); depth > 0 and the closed pixel-centre box),
+// and one ballot for the valid-camera count of every bin.
+struct PassA {
+  uint64_t mask;
+  int z, cnt;
+  bool writer;
+};
+
+__device__ __forceinline__ PassA validity_pass(const LaneCam& lc, double py, double oz, double dz, int zc, int zl,
+                                               int n, bool lane_ok, int Z, int N, double Wm1, double Hm1) {
+  PassA a;
+  a.z = zc + zl;
+  const bool in_range = lane_ok && a.z < Z;
+  bool valid = false;
+  if (in_range && N > 0) {
+    const double pz = oz + ((double)a.z + 0.5) * dz;
+    const double h2 = fma(lc.Cc[2], pz, fma(lc.Bc[2], py, lc.A[2]));
+    const double h0 = fma(lc.Cc[0], pz, fma(lc.Bc[0], py, lc.A[0]));
+    const double h1 = fma(lc.Cc[1], pz, fma(lc.Bc[1], py, lc.A[1]));
+    valid = (h2 > 0.0) && (h0 >= 0.0) && (fma(Wm1, h2, -h0) >= 0.0) && (h1 >= 0.0) && (fma(Hm1, h2, -h1) >= 0.0);
+  }
+  a.mask = __ballot(valid);
+  const int Nn = (N > 0) ? N : 1;
+  const uint64_t grp = (Nn >= 64) ? ~0ull : ((1ull << Nn) - 1ull);
+  const int shift = zl * Nn;
+  a.cnt = (in_range && N > 0 && shift < 64) ? (int)__popcll((a.mask >> shift) & grp) : 0;
+  a.writer = in_range && n == 0;
+  return a;
+}
+
+// Phase B for one valid sample: exact division, taps and weights.
+struct Taps {
+  int pix[4];
+  float w[4];
+};
+
+__device__ __forceinline__ Taps tap_geometry(const double* sP, int n, double px, double py, double pz, int cnt,
+                                             int H, int W) {
+  const double* P = sP + n * 12;
+  const double h0 = fma(P[0], px, fma(P[1], py, fma(P[2], pz, P[3])));
+  const double h1 = fma(P[4], px, fma(P[5], py, fma(P[6], pz, P[7])));
+  const double h2 = fma(P[8], px, fma(P[9], py, fma(P[10], pz, P[11])));
+  const double r = recip(h2);
+  const double u = h0 * r, v = h1 * r;
+  // validity was decided in phase A; clamping only guards rounding at the edges
+  const double fu = fmin(fmax(floor(u), 0.0), (double)(W - 1));
+  const double fv = fmin(fmax(floor(v), 0.0), (double)(H - 1));
+  const int x0 = (int)fu, y0 = (int)fv;
+  const float fa = (float)(u - fu), fb = (float)(v - fv);
+  const float rc = __builtin_amdgcn_rcpf((float)cnt);
+  Taps t;
+  const int p00 = (n * H + y0) * W + x0;
+  const int dxp = (x0 + 1 < W) ? 1 : 0;      // the clamped tap has weight 0
+  const int dyp = (y0 + 1 < H) ? W : 0;
+  t.pix[0] = p00;
+  t.pix[1] = p00 + dxp;
+  t.pix[2] = p00 + dyp;
+  t.pix[3] = p00 + dyp + dxp;
+  const float wa0 = (1.0f - fa) * rc, wa1 = fa * rc;
+  const float wb0 = 1.0f - fb, wb1 = fb;
+  t.w[0] = wa0 * wb0;
+  t.w[1] = wa1 * wb0;
+  t.w[2] = wa0 * wb1;
+  t.w[3] = wa1 * wb1;
+  return t;
+}
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+
+// D consecutive dwords of one tap, accumulated into fp32 registers.
+template <int D, bool BF16>
+struct Lane {
+  static constexpr int kVec = BF16 ? 2 * D : D;
+  struct Raw {
+    uint32_t d[D];
+  };
+  __device__ static Raw load(__amdgpu_buffer_rsrc_t rs, int off) {
+    Raw r;
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= D; i += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * i, 0, 0);
+      r.d[i] = v[0];
+      r.d[i + 1] = v[1];
+      r.d[i + 2] = v[2];
+      r.d[i + 3] = v[3];
+    }
+#pragma unroll
+    for (; i < D; ++i) r.d[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * i, 0, 0);
+    return r;
+  }
+  __device__ static void fma_into(float* acc, const Raw& v, float w) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if constexpr (BF16) {
+        acc[2 * i] = fmaf(w, __uint_as_float(v.d[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(v.d[i] & 0xffff0000u), acc[2 * i + 1]);
+      } else {
+        acc[i] = fmaf(w, __uint_as_float(v.d[i]), acc[i]);
+      }
     }
   }
 };
 
-template <>
-struct Chunk<4, true> {
-  static constexpr int kVec = 2;
-  __device__ static void fma_into(float* acc, __amdgpu_buffer_rsrc_t rs, int off, float w) {
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-    acc[0] = fmaf(w, __uint_as_float(v << 16), acc[0]);
-    acc[1] = fmaf(w, __uint_as_float(v & 0xffff0000u), acc[1]);
-  }
-};
+// x + x[lane ^ 16] and x + x[lane ^ 32] with the gfx950 lane-swap instructions.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct FwdArgs {
   Problem p;
   float* out;
   uint8_t* counts;
-  int Q;         // chunks per pixel
-  int Gq;        // chunks per channel group
-  int tiles_y;   // ceil(Y / kTileY)
+  int c_lo;          // first channel of this launch's group
+  int Cg;            // channels of the group
+  int tiles_y;       // ceil(Y / kTileY)
+  int write_counts;
 };
 
-template <int VB, bool BF16>
+// Forward kernel.  L lanes cover one tap's channel group with D dwords each
+// (L * D * 4 == group bytes); S = 64 / L slots; T = S / 4 samples per step.
+template <int D, int L, bool BF16>
 __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
-  using Ch = Chunk<VB, BF16>;
-  constexpr int kVec = Ch::kVec;
+  using Ln = Lane<D, BF16>;
+  constexpr int kVec = Ln::kVec;
+  constexpr int S = kWave / L;
+  constexpr int T = S / 4;
+  static_assert(S >= 4 && (S & 3) == 0, "a step covers whole samples");
   const Problem& p = a.p;
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
-  Rec* sRec = reinterpret_cast<Rec*>(smem + sizeof(double) * 12 * p.N);
-  float* sOut = reinterpret_cast<float*>(smem + sizeof(double) * 12 * p.N + sizeof(Rec) * kRecPerWave * kWaves);
+  unsigned char* cur = smem + sizeof(double) * 12 * p.N;
+  int2* sPend = reinterpret_cast<int2*>(cur);
+  cur += sizeof(int2) * kPend * kWaves;
+  Rec* sRec = reinterpret_cast<Rec*>(cur);
+  cur += sizeof(Rec) * kRec * kWaves;
+  int2* sItem = reinterpret_cast<int2*>(cur);
+  cur += sizeof(int2) * kItems * kWaves;
+  float* sOut = reinterpret_cast<float*>(cur);
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int yt = tile % a.tiles_y;
@@ -233,98 +302,152 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
   const int y_base = yt * kTileY;
   const int n_cells = min(kTileY, p.Y - y_base);
 
-  const int g = blockIdx.y;
-  const int q_lo = g * a.Gq;
-  const int Qg = min(a.Q - q_lo, a.Gq);            // chunks in this channel group (0 when C == 0)
-  const int S = (Qg > 0) ? kWave / Qg : 0;           // tap slots per wave
-  const int Cg = Qg * kVec;                           // channels in this group
-  const int c_lo = q_lo * kVec;
-
   stage_cameras(sP, p.K, p.R, p.t, b, p.N);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  Rec* rec = sRec + wid * kRecPerWave;
-  const int slot = (Qg > 0) ? lane / Qg : kWave;
-  const int q = (Qg > 0) ? lane - slot * Qg : 0;
-  const bool gather_lane = slot < S;
+  const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
+  int2* pend = sPend + wid * kPend;
+  Rec* rec = sRec + wid * kRec;
+  int2* items = sItem + wid * kItems;
 
-  const size_t batch_bytes = (size_t)p.N * p.H * p.W * p.C * p.elem_bytes;
-  const unsigned char* fb = reinterpret_cast<const unsigned char*>(p.feat) + (size_t)b * batch_bytes;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(fb), 0, (int)batch_bytes, 0x00020000);
-  const int pix_bytes = p.C * p.elem_bytes;
-  const int group_off = q_lo * VB;
-  const int zpc = (p.N > 0) ? kWave / p.N : kWave;   // height bins per geometry pass
+  // phase-A lane role
+  const int Nn = (p.N > 0) ? p.N : 1;
+  const int zpc = kWave / Nn;                       // height bins per item
+  const int zl = lane / Nn;
+  const int ln = lane - zl * Nn;
+  const bool lane_ok = lane < zpc * Nn;
   const double px = p.ox + ((double)x + 0.5) * p.dx;
+  const LaneCam lc = lane_camera(sP, ln, p.N, px);
+  const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
 
-  for (int cl = wid; cl < n_cells; cl += kWaves) {
-    const int y = y_base + cl;
-    const double py = p.oy + ((double)y + 0.5) * p.dy;
-    float acc[kVec];
+  // gather lane role
+  const int slot = lane / L;
+  const int q = lane - slot * L;
+  const int tap = slot & 3;
+  const int j_off = slot >> 2;
+  const int lane_off = a.c_lo * p.elem_bytes + q * 4 * D;
+  const size_t batch_bytes = (size_t)p.N * p.H * p.W * p.C * p.elem_bytes;
+  const unsigned char* fbase = reinterpret_cast<const unsigned char*>(p.feat) + (size_t)b * batch_bytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(fbase), 0, (int)batch_bytes, 0x00020000);
+  const int pix_bytes = p.C * p.elem_bytes;
+  const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 1;
+
+  // this wave's cells: wid, wid + 4, ...; items run over (cell, block of bins)
+  const int my_cells = (n_cells > wid) ? (n_cells - wid + kWaves - 1) / kWaves : 0;
+  const int total_items = my_cells * items_per_cell;
+  float acc[kVec];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
+  for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
 
-    for (int zc = 0; zc < p.Z; zc += zpc) {
-      int z, cnt;
-      bool writer;
-      const int nvalid = geometry_pass(sP, rec, px, py, p.oz, p.dz, zc, zpc, p.Z, p.N, p.H, p.W, pix_bytes,
-                                       group_off, lane, z, cnt, writer);
-      if (a.counts != nullptr && g == 0 && writer)
-        a.counts[(((size_t)b * p.X + x) * p.Y + y) * p.Z + z] = (uint8_t)cnt;
-      wave_lds_sync();
-      const int nrec = 4 * nvalid;
-      if (gather_lane) {
-        const int lane_off = q * VB;
-        int r = slot;
-        for (; r + S < nrec; r += 2 * S) {
-          const Rec r0 = rec[r], r1 = rec[r + S];
-          Ch::fma_into(acc, rs, r0.off + lane_off, r0.w);
-          Ch::fma_into(acc, rs, r1.off + lane_off, r1.w);
-        }
-        if (r < nrec) {
-          const Rec r0 = rec[r];
-          Ch::fma_into(acc, rs, r0.off + lane_off, r0.w);
-        }
+  int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin
+  while (it < total_items) {
+    // ---- phase A: list the valid samples of up to kItems items
+    int pending = 0, nitems = 0;
+    while (it < total_items && nitems < kItems && pending < kPend - kWave) {
+      const int cl = wid + ci * kWaves;
+      const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
+      const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, lane_ok, p.Z, p.N, Wm1, Hm1);
+      if (a.write_counts && pa.writer)
+        a.counts[(((size_t)b * p.X + x) * p.Y + y_base + cl) * p.Z + pa.z] = (uint8_t)pa.cnt;
+      if ((pa.mask >> lane) & 1ull)
+        pend[pending + rank_below(pa.mask)] = make_int2(pa.z, cl | (ln << 8) | (pa.cnt << 16));
+      const int nv = (int)__popcll(pa.mask);
+      const bool last = (zc + zpc >= p.Z);
+      if (lane == 0) items[nitems] = make_int2(pending | ((pending + nv) << 12) | (last ? (1 << 24) : 0), cl);
+      pending += nv;
+      ++nitems;
+      ++it;
+      zc += zpc;
+      if (last) {
+        zc = 0;
+        ++ci;
       }
-      wave_lds_sync();
     }
-
-    // Sum the slots into slot 0 (lanes 0 .. Qg-1).
-    if (S > 1) {
-      if ((Qg & (Qg - 1)) == 0) {
-        for (int off = Qg; off < kWave; off <<= 1) {
+    wave_lds_sync();
+    // ---- phase B: taps of the listed samples
+    for (int s = lane; s < pending; s += kWave) {
+      const int2 d = pend[s];
+      const int cl = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = d.y >> 16;
+      const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
+      const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
+      const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) acc[i] += __shfl_xor(acc[i], off);
+      for (int k = 0; k < 4; ++k) rec[4 * s + k] = Rec{tp.pix[k] * pix_bytes, tp.w[k]};
+    }
+    wave_lds_sync();
+    // ---- phase C: gather, item by item
+    for (int k = 0; k < nitems; ++k) {
+      const int i0 = uniform(items[k].x);
+      const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
+      if constexpr (T == 1) {
+        const Rec* rp = rec + tap;
+        int j = t0;
+        for (; j + kUnroll <= t1; j += kUnroll) {
+          typename Ln::Raw v[kUnroll];
+          float w[kUnroll];
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            const Rec rr = rp[4 * (j + u)];
+            w[u] = rr.w;
+            v[u] = Ln::load(rs, rr.off + lane_off);
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
+        }
+        for (; j < t1; ++j) {
+          const Rec rr = rp[4 * j];
+          Ln::fma_into(acc, Ln::load(rs, rr.off + lane_off), rr.w);
         }
       } else {
-        float part[kVec];
+        for (int jb = t0; jb < t1; jb += T * kUnroll) {
+          typename Ln::Raw v[kUnroll];
+          float w[kUnroll];
 #pragma unroll
-        for (int i = 0; i < kVec; ++i) part[i] = acc[i];
-        for (int s = 1; s < S; ++s) {
-          const int src = min(lane + s * Qg, kWave - 1);
+          for (int u = 0; u < kUnroll; ++u) {
+            const int j = jb + u * T + j_off;
+            const bool in = j < t1;
+            const Rec rr = rec[4 * min(j, kPend - 1) + tap];
+            w[u] = in ? rr.w : 0.f;
+            v[u] = Ln::load(rs, in ? rr.off + lane_off : kOutOfRange);
+          }
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) part[i] += __shfl(acc[i], src);
+          for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
+        }
+      }
+      if ((i0 >> 24) & 1) {
+        // last item of its cell: sum the slots and park the channels in the output tile
+        const int cl = uniform(items[k].y);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          float s = acc[i];
+#pragma unroll
+          for (int off = L; off < 16; off <<= 1) s += __shfl_xor(s, off);
+          s = sum_xor16(s);
+          s = sum_xor32(s);
+          acc[i] = s;
+        }
+        if (slot == 0) {
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) sOut[(q * kVec + i) * kTileLd + cl] = acc[i];
         }
 #pragma unroll
-        for (int i = 0; i < kVec; ++i) acc[i] = part[i];
+        for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
       }
     }
-    if (slot == 0) {
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) sOut[(q * kVec + i) * kTileLd + cl] = acc[i];
-    }
+    wave_lds_sync();
   }
   __syncthreads();
 
   // Coalesced write-out of the tile: rows of n_cells consecutive y per channel.
-  if (Cg > 0) {
-    float* ob = a.out + (((size_t)b * p.C + c_lo) * p.X + x) * p.Y + y_base;
+  {
     const size_t c_stride = (size_t)p.X * p.Y;
-    for (int e = threadIdx.x; e < Cg * n_cells; e += kBlock) {
-      const int c = e / n_cells, yl = e - c * n_cells;
-      __builtin_nontemporal_store(sOut[c * kTileLd + yl], ob + c * c_stride + yl);
+    float* ob = a.out + (((size_t)b * p.C + a.c_lo) * p.X + x) * p.Y + y_base;
+    const int yl = threadIdx.x & (kTileY - 1);
+    if (yl < n_cells) {
+      for (int c = threadIdx.x / kTileY; c < a.Cg; c += kBlock / kTileY)
+        __builtin_nontemporal_store(sOut[c * kTileLd + yl], ob + c * c_stride + yl);
     }
   }
 }
@@ -333,85 +456,278 @@ struct BwdArgs {
   Problem p;
   const float* grad;
   float* dF;
-  int Cg;        // channels per group
-  int tiles_y;
+  int tiles_x, tiles_y;
 };
 
+// Hash-table slot of pixel `pix` (inserted if absent), or -1 when the probe
+// sequence finds no room.  Integer compare-and-swap only.
+__device__ __forceinline__ int table_slot(int* sTag, int pix) {
+  uint32_t h = ((uint32_t)pix * 2654435761u) >> (32 - kSlotBits);
+#pragma unroll 1
+  for (int probe = 0; probe < kProbes; ++probe) {
+    const int old = atomicCAS(&sTag[h], -1, pix);
+    if (old == -1 || old == pix) return (int)h;
+    h = (h + 1) & (kSlots - 1);
+  }
+  return -1;
+}
+
 __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
-  constexpr int kV = kBwdMaxCh / kBwdLanes;  // channels per lane, upper bound
+  static_assert(kSlots == (1 << kSlotBits), "table size matches the hash width");
   const Problem& p = a.p;
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
-  Rec* sRec = reinterpret_cast<Rec*>(smem + sizeof(double) * 12 * p.N);
-  float* sG = reinterpret_cast<float*>(smem + sizeof(double) * 12 * p.N + sizeof(Rec) * kRecPerWave * kWaves);
+  unsigned char* cur = smem + sizeof(double) * 12 * p.N;
+  float* sG = reinterpret_cast<float*>(cur);                 // [kBwdCg][kBwdGLd] grad tile
+  cur += sizeof(float) * kBwdCg * kBwdGLd;
+  int* sTag = reinterpret_cast<int*>(cur);                   // pixel of each slot, -1 = free
+  cur += sizeof(int) * kSlots;
+  int* sCnt = reinterpret_cast<int*>(cur);                   // taps per slot
+  cur += sizeof(int) * kSlots;
+  int* sStart = reinterpret_cast<int*>(cur);                 // first sorted position per slot
+  cur += sizeof(int) * kSlots;
+  int2* sPend = reinterpret_cast<int2*>(cur);                // [kWaves][kPend] listed samples
+  cur += sizeof(int2) * kPend * kWaves;
+  int2* sRegion = reinterpret_cast<int2*>(cur);              // [kWaves][kBwdRegion] (slot | rank << 8 | cell << 24, w)
+  cur += sizeof(int2) * kBwdRegion * kWaves;
+  int2* sSorted = reinterpret_cast<int2*>(cur);              // [kWaves * kBwdRegion] (cell, w)
+  cur += sizeof(int2) * kBwdRegion * kWaves;
+  int4* sOver = reinterpret_cast<int4*>(cur);               // [kWaves][kOver] (pix, cell, w)
+  cur += sizeof(int4) * kOver * kWaves;
+  int* sOverN = reinterpret_cast<int*>(cur);                 // [kWaves] queue lengths
+  cur += sizeof(int) * kWaves;
+  int* sFlag = reinterpret_cast<int*>(cur);
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int yt = tile % a.tiles_y;
-  const int bx = tile / a.tiles_y;
-  const int x = bx % p.X;
-  const int b = bx / p.X;
-  const int y_base = yt * kTileY;
-  const int n_cells = min(kTileY, p.Y - y_base);
-  const int c_lo = blockIdx.y * a.Cg;
-  const int Cg = min(a.Cg, p.C - c_lo);
+  const int r1 = tile / a.tiles_y;
+  const int xt = r1 % a.tiles_x;
+  const int b = r1 / a.tiles_x;
+  const int x_base = xt * kBwdTX, y_base = yt * kBwdTY;
+  const int ncx = min(kBwdTX, p.X - x_base), ncy = min(kBwdTY, p.Y - y_base);
+  const int n_cells = ncx * ncy;
+  const int c_lo = blockIdx.y * kBwdCg;
+  const int Cg = min(kBwdCg, p.C - c_lo);
 
   stage_cameras(sP, p.K, p.R, p.t, b, p.N);
+  for (int e = threadIdx.x; e < kSlots; e += kBlock) {
+    sTag[e] = -1;
+    sCnt[e] = 0;
+  }
+  if (threadIdx.x < kWaves) sOverN[threadIdx.x] = 0;
   {
-    const float* gb = a.grad + (((size_t)b * p.C + c_lo) * p.X + x) * p.Y + y_base;
+    // grad tile [Cg][n_cells], read as rows of ncy consecutive y
     const size_t c_stride = (size_t)p.X * p.Y;
+    const float* gb = a.grad + (((size_t)b * p.C + c_lo) * p.X + x_base) * p.Y + y_base;
     for (int e = threadIdx.x; e < Cg * n_cells; e += kBlock) {
-      const int c = e / n_cells, yl = e - c * n_cells;
-      sG[c * kTileLd + yl] = __builtin_nontemporal_load(gb + c * c_stride + yl);
+      const int c = e / n_cells, k = e - c * n_cells;
+      const int dx = k / ncy, dy = k - dx * ncy;
+      sG[c * kBwdGLd + k] = __builtin_nontemporal_load(gb + c * c_stride + (size_t)dx * p.Y + dy);
     }
   }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  Rec* rec = sRec + wid * kRecPerWave;
-  const int slot = lane / kBwdLanes;    // tap slot 0..3
-  const int l = lane - slot * kBwdLanes;
-  float* db = a.dF + (size_t)b * p.N * p.H * p.W * p.C;
-  const int zpc = (p.N > 0) ? kWave / p.N : kWave;
-  const double px = p.ox + ((double)x + 0.5) * p.dx;
-  const int nv = (Cg + kBwdLanes - 1) / kBwdLanes;
+  const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
+  int2* region = sRegion + wid * kBwdRegion;
+  int2* pend = sPend + wid * kPend;
+  const int Nn = (p.N > 0) ? p.N : 1;
+  const int zpc = kWave / Nn;
+  const int zl = lane / Nn;
+  const int ln = lane - zl * Nn;
+  const bool lane_ok = lane < zpc * Nn;
+  const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
+  const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 0;
+  const int my_cells = (n_cells > wid) ? (n_cells - wid + kWaves - 1) / kWaves : 0;
+  const int total_items = my_cells * items_per_cell;
+  const size_t batch_elems = (size_t)p.N * p.H * p.W * p.C;
+  float* db = a.dF + (size_t)b * batch_elems + c_lo;
+  const bool ch_lane = lane < Cg;
 
-  for (int cl = wid; cl < n_cells; cl += kWaves) {
-    const int y = y_base + cl;
-    const double py = p.oy + ((double)y + 0.5) * p.dy;
-    float gv[kV];
-#pragma unroll
-    for (int i = 0; i < kV; ++i) {
-      const int c = l + i * kBwdLanes;
-      gv[i] = (i < nv && c < Cg) ? sG[c * kTileLd + cl] : 0.f;
-    }
-    for (int zc = 0; zc < p.Z; zc += zpc) {
-      int z, cnt;
-      bool writer;
-      const int nvalid = geometry_pass(sP, rec, px, py, p.oz, p.dz, zc, zpc, p.Z, p.N, p.H, p.W, p.C, c_lo,
-                                       lane, z, cnt, writer);
-      wave_lds_sync();
-      const int nrec = 4 * nvalid;
-      for (int r = slot; r < nrec; r += 4) {
-        const Rec rr = rec[r];
-        float* dst = db + rr.off + l;
-#pragma unroll
-        for (int i = 0; i < kV; ++i) {
-          if (i < nv && l + i * kBwdLanes < Cg) unsafeAtomicAdd(dst + i * kBwdLanes, gv[i] * rr.w);
+  int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin
+  for (;;) {
+    // ---- list taps in batches until this wave's region could overflow
+    int used = 0;
+    for (;;) {
+      // phase A: valid samples of several items
+      int pending = 0;
+      while (it < total_items && pending < kPend - kWave && used + 4 * (pending + kWave) <= kBwdRegion) {
+        const int k = wid + ci * kWaves;               // cell within the tile
+        const int dx = k / ncy, dy = k - dx * ncy;
+        const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
+        const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
+        const LaneCam lc = lane_camera(sP, ln, p.N, px);
+        const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, lane_ok, p.Z, p.N, Wm1, Hm1);
+        if ((pa.mask >> lane) & 1ull)
+          pend[pending + rank_below(pa.mask)] = make_int2(pa.z, k | (ln << 8) | (pa.cnt << 16));
+        pending += (int)__popcll(pa.mask);
+        ++it;
+        zc += zpc;
+        if (zc >= p.Z) {
+          zc = 0;
+          ++ci;
         }
       }
+      if (pending == 0) break;
       wave_lds_sync();
+      // phase B: taps -> table slot and rank; a tap with no slot is scattered by its lane
+      for (int s = lane; s < pending; s += kWave) {
+        const int2 d = pend[s];
+        const int k = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = d.y >> 16;
+        const int dx = k / ncy, dy = k - dx * ncy;
+        const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
+        const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
+        const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
+        const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int sl = table_slot(sTag, tp.pix[t]);
+          if (sl >= 0) {
+            const int rank = atomicAdd(&sCnt[sl], 1);
+            region[used + 4 * s + t] = make_int2(sl | (rank << kSlotBits) | (k << 24), __float_as_int(tp.w[t]));
+          } else {
+            // no slot: queue the tap for a lanes-=-channels scatter below, or (queue full) scatter it here
+            region[used + 4 * s + t] = make_int2(-1, 0);
+            const int qpos = atomicAdd(&sOverN[wid], 1);
+            if (qpos < kOver) {
+              sOver[wid * kOver + qpos] = make_int4(tp.pix[t], k, __float_as_int(tp.w[t]), 0);
+            } else {
+              for (int c = 0; c < Cg; ++c)
+                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * sG[c * kBwdGLd + k]);
+            }
+          }
+        }
+      }
+      used += 4 * pending;
+      wave_lds_sync();
+      const int n_over = min(uniform(sOverN[wid]), kOver);
+      if (n_over > 0) {
+        for (int r = 0; r < n_over; ++r) {
+          const int4 e = sOver[wid * kOver + r];
+          if (ch_lane) unsafeAtomicAdd(db + (size_t)e.x * p.C + lane, __int_as_float(e.z) * sG[lane * kBwdGLd + e.y]);
+        }
+        wave_lds_sync();
+        if (lane == 0) sOverN[wid] = 0;
+        wave_lds_sync();
+      }
     }
+    __syncthreads();
+    // ---- counting sort by slot: exclusive prefix sum of the per-slot counts (wave 0)
+    if (wid == 0) {
+      constexpr int kPer = kSlots / kWave;
+      int c4[kPer];
+      int run = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        c4[i] = sCnt[lane * kPer + i];
+        run += c4[i];
+      }
+      int incl = run;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      int excl = incl - run;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        sStart[lane * kPer + i] = excl;
+        excl += c4[i];
+      }
+      if (lane == 0) sFlag[0] = 0;
+    }
+    __syncthreads();
+    for (int r = lane; r < used; r += kWave) {
+      const int2 e = region[r];
+      if (e.x >= 0)
+        sSorted[sStart[e.x & (kSlots - 1)] + ((e.x >> kSlotBits) & ((1 << (24 - kSlotBits)) - 1))] =
+            make_int2(e.x >> 24, e.y);
+    }
+    if (it < total_items && lane == 0) atomicOr(&sFlag[0], 1);
+    __syncthreads();
+    // ---- per-pixel sums in registers, one global atomic per (pixel, channel)
+    for (int s = wid; s < kSlots; s += kWaves) {
+      const int pix = sTag[s];
+      if (pix < 0) continue;
+      const int r0 = sStart[s], r1e = r0 + sCnt[s];
+      float acc = 0.f;
+      int r = r0;
+      for (; r + 4 <= r1e; r += 4) {
+        const int2 e0 = sSorted[r], e1 = sSorted[r + 1], e2 = sSorted[r + 2], e3 = sSorted[r + 3];
+        if (ch_lane) {
+          acc = fmaf(__int_as_float(e0.y), sG[lane * kBwdGLd + e0.x], acc);
+          acc = fmaf(__int_as_float(e1.y), sG[lane * kBwdGLd + e1.x], acc);
+          acc = fmaf(__int_as_float(e2.y), sG[lane * kBwdGLd + e2.x], acc);
+          acc = fmaf(__int_as_float(e3.y), sG[lane * kBwdGLd + e3.x], acc);
+        }
+      }
+      for (; r < r1e; ++r) {
+        const int2 e = sSorted[r];
+        if (ch_lane) acc = fmaf(__int_as_float(e.y), sG[lane * kBwdGLd + e.x], acc);
+      }
+      if (ch_lane) unsafeAtomicAdd(db + (size_t)pix * p.C + lane, acc);
+    }
+    const int more = sFlag[0];
+    __syncthreads();
+    if (!more) break;
+    for (int e = threadIdx.x; e < kSlots; e += kBlock) {
+      sTag[e] = -1;
+      sCnt[e] = 0;
+    }
+    __syncthreads();
   }
 }
 
 __global__ void fill_zero_f32(float* __restrict__ dst, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t n4 = ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) ? n / 4 : 0;
   float4* d4 = reinterpret_cast<float4*>(dst);
   for (size_t k = i; k < n4; k += stride) d4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (size_t k = n4 * 4 + i; k < n; k += stride) dst[k] = 0.f;
+}
+
+template <int D, int L, bool BF16>
+void launch_fwd_group(const FwdArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
+  hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16>), grid, dim3(kBlock), shmem, stream, a);
+}
+
+// Supported lane layouts (dwords per lane D, lanes per tap L).
+#define FBEV_FWD_LAYOUTS(X)                                                                                  \
+  X(1, 16) X(2, 16) X(3, 16) X(4, 16) X(5, 16) X(6, 16) X(8, 16) X(16, 16) X(1, 8) X(2, 8) X(3, 8) X(5, 8)     \
+  X(6, 8) X(7, 8) X(1, 4) X(2, 4) X(3, 4) X(5, 4) X(6, 4) X(7, 4) X(1, 2) X(3, 2) X(5, 2) X(7, 2) X(1, 1)      \
+  X(2, 1) X(3, 1) X(4, 1) X(5, 1) X(6, 1) X(7, 1)
+
+bool layout_supported(int D, int L) {
+#define FBEV_IS(d, l) if (D == d && L == l) return true;
+  FBEV_FWD_LAYOUTS(FBEV_IS)
+#undef FBEV_IS
+  return false;
+}
+
+template <bool BF16>
+bool dispatch_fwd(int D, int L, const FwdArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
+#define FBEV_CASE(d, l) \
+  if (D == d && L == l) { launch_fwd_group<d, l, BF16>(a, grid, shmem, stream); return true; }
+  FBEV_FWD_LAYOUTS(FBEV_CASE)
+#undef FBEV_CASE
+  return false;
+}
+
+// Lane layout for a channel group of `bytes` per pixel: the widest L (lanes
+// per tap) that divides it into a supported D (dwords per lane).
+void pick_layout(int bytes, int& D, int& L) {
+  static const int kL[] = {16, 8, 4, 2, 1};
+  for (int l : kL) {
+    if (bytes % (4 * l) != 0) continue;
+    if (layout_supported(bytes / (4 * l), l)) {
+      D = bytes / (4 * l);
+      L = l;
+      return;
+    }
+  }
+  D = 0;
+  L = 0;
 }
 
 }  // namespace
@@ -421,29 +737,44 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
   a.p = p;
   a.out = out;
   a.counts = counts;
-  const int pix_bytes = p.C * p.elem_bytes;
-  a.Q = pix_bytes / p.vec_bytes;
-  const int vec = p.vec_bytes / p.elem_bytes;
-  a.Gq = kMaxGroupCh / vec;
-  if (a.Gq > kWave) a.Gq = kWave;
   a.tiles_y = (p.Y + kTileY - 1) / kTileY;
-  const int groups = (a.Q > 0) ? (a.Q + a.Gq - 1) / a.Gq : 1;
   const long long tiles = (long long)p.B * p.X * a.tiles_y;
   if (tiles == 0) return hipSuccess;
-  const int group_ch = (a.Q > 0) ? ((a.Q < a.Gq) ? a.Q : a.Gq) * vec : 0;
-  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(Rec) * kRecPerWave * kWaves +
-                       sizeof(float) * (size_t)(group_ch > 0 ? group_ch : 1) * kTileLd;
-  const dim3 grid((unsigned)tiles, (unsigned)groups);
-  const dim3 block(kBlock);
-  if (p.elem_bytes == 4 && p.vec_bytes == 16)
-    hipLaunchKernelGGL((sampling_vt_fwd<16, false>), grid, block, shmem, stream, a);
-  else if (p.elem_bytes == 4)
-    hipLaunchKernelGGL((sampling_vt_fwd<4, false>), grid, block, shmem, stream, a);
-  else if (p.vec_bytes == 16)
-    hipLaunchKernelGGL((sampling_vt_fwd<16, true>), grid, block, shmem, stream, a);
-  else
-    hipLaunchKernelGGL((sampling_vt_fwd<4, true>), grid, block, shmem, stream, a);
-  return hipGetLastError();
+  const int es = p.elem_bytes;
+  // channel groups of at most 1 KiB per pixel (16 lanes x 16 dwords), each
+  // shrunk until its byte size maps onto a supported lane layout
+  const int max_group_ch = 1024 / es;
+  int c = 0;
+  bool first = true;
+  do {
+    int Cg = p.C - c;
+    if (Cg > max_group_ch) Cg = max_group_ch;
+    int D = 0, L = 0;
+    while (Cg > 0) {
+      pick_layout(Cg * es, D, L);
+      if (L > 0) break;
+      --Cg;
+    }
+    if (Cg == 0) {
+      if (p.C > 0) return hipErrorInvalidValue;      // unreachable for 4-byte-multiple channel rows
+      D = 1;                                          // C == 0: counts only, no channel reads
+      L = 16;
+    }
+    a.c_lo = c;
+    a.Cg = Cg;
+    a.write_counts = (first && counts != nullptr) ? 1 : 0;
+    const size_t shmem = sizeof(double) * 12 * p.N + sizeof(int2) * kPend * kWaves + sizeof(Rec) * kRec * kWaves +
+                         sizeof(int2) * kItems * kWaves + sizeof(float) * (size_t)(Cg > 0 ? Cg : 1) * kTileLd;
+    const dim3 grid((unsigned)tiles);
+    const bool ok = (es == 2) ? dispatch_fwd<true>(D, L, a, grid, shmem, stream)
+                              : dispatch_fwd<false>(D, L, a, grid, shmem, stream);
+    if (!ok) return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    c += Cg;
+    first = false;
+  } while (c < p.C);
+  return hipSuccess;
 }
 
 hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream) {
@@ -460,14 +791,14 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   a.p = p;
   a.grad = grad_out;
   a.dF = grad_feat;
-  a.Cg = kBwdMaxCh;
-  a.tiles_y = (p.Y + kTileY - 1) / kTileY;
-  const long long tiles = (long long)p.B * p.X * a.tiles_y;
+  a.tiles_x = (p.X + kBwdTX - 1) / kBwdTX;
+  a.tiles_y = (p.Y + kBwdTY - 1) / kBwdTY;
+  const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.Z == 0 || p.C == 0) return hipSuccess;
-  const int groups = (p.C + a.Cg - 1) / a.Cg;
-  const int group_ch = (p.C < a.Cg) ? p.C : a.Cg;
-  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(Rec) * kRecPerWave * kWaves +
-                       sizeof(float) * (size_t)group_ch * kTileLd;
+  const int groups = (p.C + kBwdCg - 1) / kBwdCg;
+  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCg * kBwdGLd + sizeof(int) * kSlots * 3 +
+                       sizeof(int2) * kPend * kWaves + sizeof(int2) * kBwdRegion * kWaves +
+                       sizeof(int2) * kBwdRegion * kWaves + sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + 16;
   hipLaunchKernelGGL(sampling_vt_bwd, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }

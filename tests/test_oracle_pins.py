@@ -104,3 +104,18 @@ def test_backward_row_restriction_is_exact(small):
     part = ovt.oracle_backward(small.grad_out, small.K, small.R, small.t, small.rng6, small.X, small.Y, small.Z,
                                H, W, rows=rows)
     np.testing.assert_allclose(part, full, rtol=0, atol=1e-13)
+
+
+def test_near_edge_band_on_golden_cases():
+    """The exclusion band flags exactly the golden samples that sit on an image edge."""
+    g = P._golden()
+    K, R, t, H, W = P._axis_camera(g)
+    expect = {"optical_axis": False, "integer_pixel": False, "right_edge_inside": True,
+              "past_last_pixel_centre": False, "behind_camera": False}
+    for case in g["cases"]:
+        d, u, v = ovt.project(ovt.voxel_grid(case["range"], 1, 1, 1), K[0], R[0], t[0])
+        assert bool(ovt.near_edge_mask(d, u, v, H, W).any()) == expect[case["name"]], case["name"]
+    # just inside / just outside the band along u
+    for du, want in [(0.5e-4, True), (2e-4, False)]:
+        u_ = np.array([W - 1 - du]); v_ = np.array([3.5]); d_ = np.array([10.0])
+        assert bool(ovt.near_edge_mask(d_, u_, v_, H, W)[0]) == want
