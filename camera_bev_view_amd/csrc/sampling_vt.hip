@@ -58,19 +58,19 @@ constexpr int kBlock = kWave * kWaves;
 constexpr int kOutOfRange = 0x7ffffff0;  // buffer offset the range check turns into a zero load
 
 // forward
-constexpr int kTileY = 32;               // cells per workgroup (one x row)
+constexpr int kTileY = 16;               // cells per workgroup (one x row)
 constexpr int kTileLd = kTileY + 1;      // padded LDS row of the output tile
 constexpr int kPend = 96;                // listed valid samples per wave
 constexpr int kItems = 16;               // items per batch
 constexpr int kRec = 4 * kPend;          // tap records per wave
-constexpr int kUnroll = 8;               // loads in flight per lane and step
+constexpr int kUnroll = 4;               // loads in flight per lane and step
 
 // backward
 constexpr int kBwdTX = 4;                // tile rows along x
 constexpr int kBwdTY = 8;                // tile cells along y
 constexpr int kBwdCells = kBwdTX * kBwdTY;
-constexpr int kBwdGLd = kBwdCells + 1;   // padded grad-tile row
 constexpr int kBwdCg = 64;               // channels per group (one per lane)
+constexpr int kBwdGLd = kBwdCg + 4;      // grad tile row: one cell's channels (16-byte aligned, padded)
 constexpr int kSlots = 256;              // hash-table entries (power of two)
 constexpr int kSlotBits = 8;
 constexpr int kOver = 64;                // per-wave queue of taps that found no table slot
@@ -478,13 +478,15 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
   unsigned char* cur = smem + sizeof(double) * 12 * p.N;
-  float* sG = reinterpret_cast<float*>(cur);                 // [kBwdCg][kBwdGLd] grad tile
-  cur += sizeof(float) * kBwdCg * kBwdGLd;
+  float* sG = reinterpret_cast<float*>(cur);                 // [kBwdCells][kBwdGLd] grad tile, channels last
+  cur += sizeof(float) * kBwdCells * kBwdGLd;
   int* sTag = reinterpret_cast<int*>(cur);                   // pixel of each slot, -1 = free
   cur += sizeof(int) * kSlots;
   int* sCnt = reinterpret_cast<int*>(cur);                   // taps per slot
   cur += sizeof(int) * kSlots;
   int* sStart = reinterpret_cast<int*>(cur);                 // first sorted position per slot
+  cur += sizeof(int) * kSlots;
+  int* sOcc = reinterpret_cast<int*>(cur);                   // occupied slots, compacted
   cur += sizeof(int) * kSlots;
   int2* sPend = reinterpret_cast<int2*>(cur);                // [kWaves][kPend] listed samples
   cur += sizeof(int2) * kPend * kWaves;
@@ -509,21 +511,32 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int c_lo = blockIdx.y * kBwdCg;
   const int Cg = min(kBwdCg, p.C - c_lo);
 
+  // grad tile [Cg][n_cells] (rows of ncy consecutive y): issue the loads first so their
+  // latency overlaps the camera staging and table set-up
+  constexpr int kGPer = kBwdCg * kBwdCells / kBlock;
+  float gpre[kGPer];
+  {
+    const size_t c_stride = (size_t)p.X * p.Y;
+    const float* gb = a.grad + (((size_t)b * p.C + c_lo) * p.X + x_base) * p.Y + y_base;
+#pragma unroll
+    for (int i = 0; i < kGPer; ++i) {
+      const int e = threadIdx.x + i * kBlock;
+      const int c = e / n_cells, k = e - c * n_cells;
+      const int dx = k / ncy, dy = k - dx * ncy;
+      gpre[i] = (e < Cg * n_cells) ? __builtin_nontemporal_load(gb + c * c_stride + (size_t)dx * p.Y + dy) : 0.f;
+    }
+  }
   stage_cameras(sP, p.K, p.R, p.t, b, p.N);
   for (int e = threadIdx.x; e < kSlots; e += kBlock) {
     sTag[e] = -1;
     sCnt[e] = 0;
   }
   if (threadIdx.x < kWaves) sOverN[threadIdx.x] = 0;
-  {
-    // grad tile [Cg][n_cells], read as rows of ncy consecutive y
-    const size_t c_stride = (size_t)p.X * p.Y;
-    const float* gb = a.grad + (((size_t)b * p.C + c_lo) * p.X + x_base) * p.Y + y_base;
-    for (int e = threadIdx.x; e < Cg * n_cells; e += kBlock) {
-      const int c = e / n_cells, k = e - c * n_cells;
-      const int dx = k / ncy, dy = k - dx * ncy;
-      sG[c * kBwdGLd + k] = __builtin_nontemporal_load(gb + c * c_stride + (size_t)dx * p.Y + dy);
-    }
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int e = threadIdx.x + i * kBlock;
+    const int c = e / n_cells, k = e - c * n_cells;
+    if (e < Cg * n_cells) sG[k * kBwdGLd + c] = gpre[i];
   }
   __syncthreads();
 
@@ -579,11 +592,25 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
         const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
         const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
+        // first probes of the four taps issued together; collisions take the probe loop
+        int sl4[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int sl = table_slot(sTag, tp.pix[t]);
+          const int h = (int)(((uint32_t)tp.pix[t] * 2654435761u) >> (32 - kSlotBits));
+          const int old = atomicCAS(&sTag[h], -1, tp.pix[t]);
+          sl4[t] = (old == -1 || old == tp.pix[t]) ? h : -2;
+        }
+        int rk4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (sl4[t] == -2) sl4[t] = table_slot(sTag, tp.pix[t]);
+          rk4[t] = (sl4[t] >= 0) ? atomicAdd(&sCnt[sl4[t]], 1) : 0;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int sl = sl4[t];
           if (sl >= 0) {
-            const int rank = atomicAdd(&sCnt[sl], 1);
+            const int rank = rk4[t];
             region[used + 4 * s + t] = make_int2(sl | (rank << kSlotBits) | (k << 24), __float_as_int(tp.w[t]));
           } else {
             // no slot: queue the tap for a lanes-=-channels scatter below, or (queue full) scatter it here
@@ -593,7 +620,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
               sOver[wid * kOver + qpos] = make_int4(tp.pix[t], k, __float_as_int(tp.w[t]), 0);
             } else {
               for (int c = 0; c < Cg; ++c)
-                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * sG[c * kBwdGLd + k]);
+                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * sG[k * kBwdGLd + c]);
             }
           }
         }
@@ -604,7 +631,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       if (n_over > 0) {
         for (int r = 0; r < n_over; ++r) {
           const int4 e = sOver[wid * kOver + r];
-          if (ch_lane) unsafeAtomicAdd(db + (size_t)e.x * p.C + lane, __int_as_float(e.z) * sG[lane * kBwdGLd + e.y]);
+          if (ch_lane) unsafeAtomicAdd(db + (size_t)e.x * p.C + lane, __int_as_float(e.z) * sG[e.y * kBwdGLd + lane]);
         }
         wave_lds_sync();
         if (lane == 0) sOverN[wid] = 0;
@@ -634,38 +661,73 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         sStart[lane * kPer + i] = excl;
         excl += c4[i];
       }
+      // compact list of occupied slots (slot order)
+      int occ_base = 0;
+      {
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) mine += (c4[i] > 0);
+        int inc = mine;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_up(inc, off);
+          if (lane >= off) inc += o;
+        }
+        occ_base = inc - mine;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (c4[i] > 0) sOcc[occ_base++] = lane * kPer + i;
+        if (lane == kWave - 1) sFlag[1] = inc;
+      }
       if (lane == 0) sFlag[0] = 0;
     }
     __syncthreads();
     for (int r = lane; r < used; r += kWave) {
       const int2 e = region[r];
-      if (e.x >= 0)
-        sSorted[sStart[e.x & (kSlots - 1)] + ((e.x >> kSlotBits) & ((1 << (24 - kSlotBits)) - 1))] =
-            make_int2(e.x >> 24, e.y);
+      if (e.x >= 0) {
+        const int sl = e.x & (kSlots - 1);
+        sSorted[sStart[sl] + ((e.x >> kSlotBits) & ((1 << (24 - kSlotBits)) - 1))] =
+            make_int2(sl | ((e.x >> 24) << kSlotBits), e.y);
+      }
     }
     if (it < total_items && lane == 0) atomicOr(&sFlag[0], 1);
     __syncthreads();
-    // ---- per-pixel sums in registers, one global atomic per (pixel, channel)
-    for (int s = wid; s < kSlots; s += kWaves) {
-      const int pix = sTag[s];
-      if (pix < 0) continue;
-      const int r0 = sStart[s], r1e = r0 + sCnt[s];
-      float acc = 0.f;
-      int r = r0;
-      for (; r + 4 <= r1e; r += 4) {
-        const int2 e0 = sSorted[r], e1 = sSorted[r + 1], e2 = sSorted[r + 2], e3 = sSorted[r + 3];
-        if (ch_lane) {
-          acc = fmaf(__int_as_float(e0.y), sG[lane * kBwdGLd + e0.x], acc);
-          acc = fmaf(__int_as_float(e1.y), sG[lane * kBwdGLd + e1.x], acc);
-          acc = fmaf(__int_as_float(e2.y), sG[lane * kBwdGLd + e2.x], acc);
-          acc = fmaf(__int_as_float(e3.y), sG[lane * kBwdGLd + e3.x], acc);
+    // ---- per-pixel sums in registers, one global atomic per (pixel, channel).
+    // lane = (record sub-slot rs, channel quad q): four of a pixel's taps per step,
+    // 4 channels per lane read as one 16-byte LDS load of the cell's grad row.
+    {
+      const int n_occ = sFlag[1];
+      const int rs = lane >> 4, q = lane & 15;
+      const bool q_ok = 4 * q < Cg;
+      for (int k = wid; k < n_occ; k += kWaves) {
+        const int sl = sOcc[k];
+        const int pix = sTag[sl];
+        const int r0 = sStart[sl], r1e = r0 + sCnt[sl];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = r0 + rs; r < r1e; r += 8) {
+          const int2 e0 = sSorted[r];
+          const bool has1 = r + 4 < r1e;
+          const int2 e1 = sSorted[has1 ? r + 4 : r];
+          const float4 g0 = *reinterpret_cast<const float4*>(sG + (e0.x >> kSlotBits) * kBwdGLd + 4 * q);
+          const float4 g1 = *reinterpret_cast<const float4*>(sG + (e1.x >> kSlotBits) * kBwdGLd + 4 * q);
+          const float w0 = __int_as_float(e0.y), w1 = has1 ? __int_as_float(e1.y) : 0.f;
+          acc.x = fmaf(w0, g0.x, acc.x);
+          acc.y = fmaf(w0, g0.y, acc.y);
+          acc.z = fmaf(w0, g0.z, acc.z);
+          acc.w = fmaf(w0, g0.w, acc.w);
+          acc.x = fmaf(w1, g1.x, acc.x);
+          acc.y = fmaf(w1, g1.y, acc.y);
+          acc.z = fmaf(w1, g1.z, acc.z);
+          acc.w = fmaf(w1, g1.w, acc.w);
         }
+        acc.x = sum_xor32(sum_xor16(acc.x));
+        acc.y = sum_xor32(sum_xor16(acc.y));
+        acc.z = sum_xor32(sum_xor16(acc.z));
+        acc.w = sum_xor32(sum_xor16(acc.w));
+        const float v = rs == 0 ? acc.x : rs == 1 ? acc.y : rs == 2 ? acc.z : acc.w;
+        const int c = 4 * q + rs;
+        if (q_ok && c < Cg) unsafeAtomicAdd(db + (size_t)pix * p.C + c, v);
       }
-      for (; r < r1e; ++r) {
-        const int2 e = sSorted[r];
-        if (ch_lane) acc = fmaf(__int_as_float(e.y), sG[lane * kBwdGLd + e.x], acc);
-      }
-      if (ch_lane) unsafeAtomicAdd(db + (size_t)pix * p.C + lane, acc);
     }
     const int more = sFlag[0];
     __syncthreads();
@@ -796,7 +858,7 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.Z == 0 || p.C == 0) return hipSuccess;
   const int groups = (p.C + kBwdCg - 1) / kBwdCg;
-  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCg * kBwdGLd + sizeof(int) * kSlots * 3 +
+  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int) * kSlots * 4 +
                        sizeof(int2) * kPend * kWaves + sizeof(int2) * kBwdRegion * kWaves +
                        sizeof(int2) * kBwdRegion * kWaves + sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + 16;
   hipLaunchKernelGGL(sampling_vt_bwd, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
