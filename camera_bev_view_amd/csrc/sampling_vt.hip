@@ -35,14 +35,17 @@
 // LDS tile, and the tile leaves as coalesced rows of the [B,C,X,Y] output.
 //
 // Backward (gradient with respect to the features; the map is linear in
-// them): one workgroup = a 4 x 8 block of cells and one group of <= 64
+// them): one workgroup = a 4 x 4 block of cells and one group of <= 64
 // channels.  Each tap's pixel is inserted into a workgroup-private hash table
 // in LDS (integer compare-and-swap) and gets a rank within its pixel from an
 // integer LDS atomic; a counting sort then makes every pixel's contributions
-// contiguous, a wave sums them per channel in registers (grad * weight /
-// count, grad read from an LDS tile), and each distinct pixel leaves the
-// workgroup with one fp32 global atomic per channel.  LDS float atomics are
-// avoided on purpose: on this chip they are far slower than integer ones.
+// contiguous.  Each 16-lane group of a wave sums one pixel's contributions
+// (grad * weight / count, grad rows read from an LDS tile, 4 channels per
+// lane), lane permutes transpose the four groups' sums, and each distinct
+// pixel leaves the workgroup as one fp32 global atomic over its 64 consecutive
+// channels.  A round ends when a wave's record buffer or the table is full;
+// the remaining items go to the next round.  LDS float atomics are avoided on
+// purpose: on this chip they are far slower than integer ones.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,15 +70,20 @@ constexpr int kUnroll = 4;               // loads in flight per lane and step
 
 // backward
 constexpr int kBwdTX = 4;                // tile rows along x
-constexpr int kBwdTY = 8;                // tile cells along y
+constexpr int kBwdTY = 4;                // tile cells along y
 constexpr int kBwdCells = kBwdTX * kBwdTY;
+static_assert(kBwdTX <= 4 && kBwdTY <= 8, "a cell's place in the tile packs into 2 + 3 bits");
 constexpr int kBwdCg = 64;               // channels per group (one per lane)
 constexpr int kBwdGLd = kBwdCg + 4;      // grad tile row: one cell's channels (16-byte aligned, padded)
-constexpr int kSlots = 256;              // hash-table entries (power of two)
-constexpr int kSlotBits = 8;
-constexpr int kOver = 64;                // per-wave queue of taps that found no table slot
+constexpr int kSlotBits = 9;
+constexpr int kSlots = 1 << kSlotBits;   // hash-table entries
+constexpr int kFillMax = kSlots / 2;     // taken slots past which a round stops listing
 constexpr int kProbes = 32;
-constexpr int kBwdRegion = 512;          // tap records per wave and round
+constexpr int kOver = 16;                // per-wave queue of taps that found no table slot
+constexpr int kBwdPend = 64;             // listed valid samples per wave
+constexpr int kBwdRegion = 256;          // tap records per wave and round
+constexpr int kRed = 8;                  // records per reduction step and lane group
+static_assert(kBwdRegion >= 4 * kWave && kBwdPend >= kWave, "an item of a full wave of valid samples fits an empty batch");
 
 struct Rec {
   int off;   // forward: byte offset of the tap's pixel
@@ -91,22 +99,33 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblk) {
   return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
 
-// P_n = K_n [R_n | t_n] in double, 12 entries per camera, row-major 3x4.
-__device__ void stage_cameras(double* sP, const float* K, const float* R, const float* t, int b, int N) {
-  for (int e = threadIdx.x; e < N * 12; e += kBlock) {
-    const int n = e / 12, rc = e - n * 12, r = rc >> 2, c = rc & 3;
-    const size_t bn = (size_t)b * N + n;
-    const float* Kn = K + bn * 9;
-    const float* Rn = R + bn * 9;
-    const float* tn = t + bn * 3;
-    double acc = 0.0;
+// P_n = K_n [R_n | t_n] in double, 12 entries per camera, row-major 3x4.  Entry
+// e = 12 n + 4 r + c is the dot product of row r of K_n with column c of [R_n | t_n].
+struct CamEntry {
+  float k[3], m[3];
+};
+
+__device__ __forceinline__ CamEntry cam_load(const float* K, const float* R, const float* t, int b, int N, int e) {
+  const int n = e / 12, rc = e - n * 12, r = rc >> 2, c = rc & 3;
+  const size_t bn = (size_t)b * N + n;
+  CamEntry ce;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const double m = (c < 3) ? (double)Rn[k * 3 + c] : (double)tn[k];
-      acc = fma((double)Kn[r * 3 + k], m, acc);
-    }
-    sP[e] = acc;
+  for (int k = 0; k < 3; ++k) {
+    ce.k[k] = K[bn * 9 + r * 3 + k];
+    ce.m[k] = (c < 3) ? R[bn * 9 + k * 3 + c] : t[bn * 3 + k];
   }
+  return ce;
+}
+
+__device__ __forceinline__ void cam_store(double* sP, int e, const CamEntry& ce) {
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) acc = fma((double)ce.k[k], (double)ce.m[k], acc);
+  sP[e] = acc;
+}
+
+__device__ void stage_cameras(double* sP, const float* K, const float* R, const float* t, int b, int N) {
+  for (int e = threadIdx.x; e < N * 12; e += kBlock) cam_store(sP, e, cam_load(K, R, t, b, N, e));
 }
 
 __device__ __forceinline__ int rank_below(uint64_t mask) {
@@ -460,12 +479,14 @@ struct BwdArgs {
 };
 
 // Hash-table slot of pixel `pix` (inserted if absent), or -1 when the probe
-// sequence finds no room.  Integer compare-and-swap only.
-__device__ __forceinline__ int table_slot(int* sTag, int pix) {
+// sequence finds no room.  Integer compare-and-swap only; `fresh` is set when
+// this call took a free slot.
+__device__ __forceinline__ int table_slot(int* sTag, int pix, int& fresh) {
   uint32_t h = ((uint32_t)pix * 2654435761u) >> (32 - kSlotBits);
 #pragma unroll 1
   for (int probe = 0; probe < kProbes; ++probe) {
     const int old = atomicCAS(&sTag[h], -1, pix);
+    if (old == -1) ++fresh;
     if (old == -1 || old == pix) return (int)h;
     h = (h + 1) & (kSlots - 1);
   }
@@ -474,31 +495,30 @@ __device__ __forceinline__ int table_slot(int* sTag, int pix) {
 
 __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   static_assert(kSlots == (1 << kSlotBits), "table size matches the hash width");
+  static_assert(4 * kWaves * kBwdRegion < (1 << 16), "sorted positions and per-slot counts fit 16 bits");
   const Problem& p = a.p;
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
   unsigned char* cur = smem + sizeof(double) * 12 * p.N;
   float* sG = reinterpret_cast<float*>(cur);                 // [kBwdCells][kBwdGLd] grad tile, channels last
   cur += sizeof(float) * kBwdCells * kBwdGLd;
+  int2* sMeta = reinterpret_cast<int2*>(cur);                // occupied slots, compacted: (pixel, first | count << 16)
+  cur += sizeof(int2) * kSlots;
   int* sTag = reinterpret_cast<int*>(cur);                   // pixel of each slot, -1 = free
   cur += sizeof(int) * kSlots;
-  int* sCnt = reinterpret_cast<int*>(cur);                   // taps per slot
+  int* sCnt = reinterpret_cast<int*>(cur);                   // taps per slot; after the prefix sum, first sorted position
   cur += sizeof(int) * kSlots;
-  int* sStart = reinterpret_cast<int*>(cur);                 // first sorted position per slot
-  cur += sizeof(int) * kSlots;
-  int* sOcc = reinterpret_cast<int*>(cur);                   // occupied slots, compacted
-  cur += sizeof(int) * kSlots;
-  int2* sPend = reinterpret_cast<int2*>(cur);                // [kWaves][kPend] listed samples
-  cur += sizeof(int2) * kPend * kWaves;
-  int2* sRegion = reinterpret_cast<int2*>(cur);              // [kWaves][kBwdRegion] (slot | rank << 8 | cell << 24, w)
+  int2* sPend = reinterpret_cast<int2*>(cur);                // [kWaves][kBwdPend] listed samples
+  cur += sizeof(int2) * kBwdPend * kWaves;
+  int2* sRegion = reinterpret_cast<int2*>(cur);              // [kWaves][kBwdRegion] (slot | rank << kSlotBits | cell << 24, w)
   cur += sizeof(int2) * kBwdRegion * kWaves;
-  int2* sSorted = reinterpret_cast<int2*>(cur);              // [kWaves * kBwdRegion] (cell, w)
+  int2* sSorted = reinterpret_cast<int2*>(cur);              // [kWaves * kBwdRegion] (grad row offset, w)
   cur += sizeof(int2) * kBwdRegion * kWaves;
-  int4* sOver = reinterpret_cast<int4*>(cur);               // [kWaves][kOver] (pix, cell, w)
+  int4* sOver = reinterpret_cast<int4*>(cur);                // [kWaves][kOver] (pix, cell, w)
   cur += sizeof(int4) * kOver * kWaves;
   int* sOverN = reinterpret_cast<int*>(cur);                 // [kWaves] queue lengths
   cur += sizeof(int) * kWaves;
-  int* sFlag = reinterpret_cast<int*>(cur);
+  int* sFlag = reinterpret_cast<int*>(cur);                  // [0] more rounds, [1] occupied slots, [2] slots taken
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int yt = tile % a.tiles_y;
@@ -511,9 +531,14 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int c_lo = blockIdx.y * kBwdCg;
   const int Cg = min(kBwdCg, p.C - c_lo);
 
-  // grad tile [Cg][n_cells] (rows of ncy consecutive y): issue the loads first so their
-  // latency overlaps the camera staging and table set-up
+  // grad tile [Cg][n_cells] (rows of ncy consecutive y): the loads are issued first and
+  // the values parked in LDS only before the first reduction, so their latency overlaps
+  // the set-up and the first listing
   constexpr int kGPer = kBwdCg * kBwdCells / kBlock;
+  // camera entries first: waiting for them then leaves the grad loads in flight
+  const bool cam0 = threadIdx.x < p.N * 12;
+  CamEntry ce0;
+  if (cam0) ce0 = cam_load(p.K, p.R, p.t, b, p.N, threadIdx.x);
   float gpre[kGPer];
   {
     const size_t c_stride = (size_t)p.X * p.Y;
@@ -526,24 +551,20 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       gpre[i] = (e < Cg * n_cells) ? __builtin_nontemporal_load(gb + c * c_stride + (size_t)dx * p.Y + dy) : 0.f;
     }
   }
-  stage_cameras(sP, p.K, p.R, p.t, b, p.N);
+  if (cam0) cam_store(sP, threadIdx.x, ce0);
+  for (int e = threadIdx.x + kBlock; e < p.N * 12; e += kBlock) cam_store(sP, e, cam_load(p.K, p.R, p.t, b, p.N, e));
   for (int e = threadIdx.x; e < kSlots; e += kBlock) {
     sTag[e] = -1;
     sCnt[e] = 0;
   }
   if (threadIdx.x < kWaves) sOverN[threadIdx.x] = 0;
-#pragma unroll
-  for (int i = 0; i < kGPer; ++i) {
-    const int e = threadIdx.x + i * kBlock;
-    const int c = e / n_cells, k = e - c * n_cells;
-    if (e < Cg * n_cells) sG[k * kBwdGLd + c] = gpre[i];
-  }
+  if (threadIdx.x == 0) sFlag[2] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
   int2* region = sRegion + wid * kBwdRegion;
-  int2* pend = sPend + wid * kPend;
+  int2* pend = sPend + wid * kBwdPend;
   const int Nn = (p.N > 0) ? p.N : 1;
   const int zpc = kWave / Nn;
   const int zl = lane / Nn;
@@ -556,38 +577,78 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const size_t batch_elems = (size_t)p.N * p.H * p.W * p.C;
   float* db = a.dF + (size_t)b * batch_elems + c_lo;
   const bool ch_lane = lane < Cg;
+  // grad value of cell k, channel c of the group, from global memory (for taps that
+  // found no table slot; such taps can be listed before the LDS tile is written)
+  auto grad_at = [&](int k, int c) -> float {
+    const int dx = k / ncy, dy = k - dx * ncy;
+    return a.grad[(((size_t)b * p.C + c_lo + c) * p.X + x_base + dx) * p.Y + y_base + dy];
+  };
 
   int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin
+  int cdx = wid / ncy, cdy = wid - (wid / ncy) * ncy;   // the cell's place in the tile
+  bool grad_staged = false;
   for (;;) {
-    // ---- list taps in batches until this wave's region could overflow
+    // ---- list taps in batches until this wave's region is full or the table is
+    // loaded past kFillMax (the pixels of the remaining items go to a later round)
     int used = 0;
+    // phase-A camera rows of this lane's camera, in registers for the round's items
+    // (h = (P0 px + P3) + P1 py + P2 pz); re-read each round so they are not live
+    // through the reduction
+    double cp0[3], cp3[3];
+    LaneCam lc;
+    {
+      const double* P = sP + (p.N > 0 ? ln : 0) * 12;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        cp0[i] = (p.N > 0) ? P[4 * i] : 0.0;
+        lc.Bc[i] = (p.N > 0) ? P[4 * i + 1] : 0.0;
+        lc.Cc[i] = (p.N > 0) ? P[4 * i + 2] : 0.0;
+        cp3[i] = (p.N > 0) ? P[4 * i + 3] : 0.0;
+      }
+    }
     for (;;) {
-      // phase A: valid samples of several items
+      // phase A: valid samples of as many items as fit; an item that does not fit
+      // is left for the next batch (or round) and its validity pass repeated there
       int pending = 0;
-      while (it < total_items && pending < kPend - kWave && used + 4 * (pending + kWave) <= kBwdRegion) {
+      bool round_full = uniform(sFlag[2]) > kFillMax;
+      while (!round_full && it < total_items) {
         const int k = wid + ci * kWaves;               // cell within the tile
-        const int dx = k / ncy, dy = k - dx * ncy;
-        const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
-        const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
-        const LaneCam lc = lane_camera(sP, ln, p.N, px);
+        const double px = p.ox + ((double)(x_base + cdx) + 0.5) * p.dx;
+        const double py = p.oy + ((double)(y_base + cdy) + 0.5) * p.dy;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) lc.A[i] = fma(cp0[i], px, cp3[i]);
         const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, lane_ok, p.Z, p.N, Wm1, Hm1);
+        const int nv = (int)__popcll(pa.mask);
+        if (used + 4 * (pending + nv) > kBwdRegion) {
+          round_full = true;
+          break;
+        }
+        if (pending + nv > kBwdPend) break;
         if ((pa.mask >> lane) & 1ull)
-          pend[pending + rank_below(pa.mask)] = make_int2(pa.z, k | (ln << 8) | (pa.cnt << 16));
-        pending += (int)__popcll(pa.mask);
+          pend[pending + rank_below(pa.mask)] =
+              make_int2(pa.z, k | (ln << 8) | (pa.cnt << 16) | (cdx << 23) | (cdy << 25));
+        pending += nv;
         ++it;
         zc += zpc;
         if (zc >= p.Z) {
           zc = 0;
           ++ci;
+          cdy += kWaves;
+          while (cdy >= ncy) {
+            cdy -= ncy;
+            ++cdx;
+          }
         }
       }
       if (pending == 0) break;
       wave_lds_sync();
-      // phase B: taps -> table slot and rank; a tap with no slot is scattered by its lane
+      // phase B: taps -> table slot and rank; a tap with no slot is queued for a
+      // lanes-=-channels scatter (or, queue full, scattered by its lane)
+      int fresh = 0;
       for (int s = lane; s < pending; s += kWave) {
         const int2 d = pend[s];
-        const int k = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = d.y >> 16;
-        const int dx = k / ncy, dy = k - dx * ncy;
+        const int k = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = (d.y >> 16) & 0x7f;
+        const int dx = (d.y >> 23) & 3, dy = (d.y >> 25) & 7;
         const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
         const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
         const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
@@ -598,12 +659,13 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         for (int t = 0; t < 4; ++t) {
           const int h = (int)(((uint32_t)tp.pix[t] * 2654435761u) >> (32 - kSlotBits));
           const int old = atomicCAS(&sTag[h], -1, tp.pix[t]);
+          fresh += (old == -1);
           sl4[t] = (old == -1 || old == tp.pix[t]) ? h : -2;
         }
         int rk4[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          if (sl4[t] == -2) sl4[t] = table_slot(sTag, tp.pix[t]);
+          if (sl4[t] == -2) sl4[t] = table_slot(sTag, tp.pix[t], fresh);
           rk4[t] = (sl4[t] >= 0) ? atomicAdd(&sCnt[sl4[t]], 1) : 0;
         }
 #pragma unroll
@@ -613,72 +675,73 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
             const int rank = rk4[t];
             region[used + 4 * s + t] = make_int2(sl | (rank << kSlotBits) | (k << 24), __float_as_int(tp.w[t]));
           } else {
-            // no slot: queue the tap for a lanes-=-channels scatter below, or (queue full) scatter it here
             region[used + 4 * s + t] = make_int2(-1, 0);
+            fresh = kSlots;                            // table full: end the round after this batch
             const int qpos = atomicAdd(&sOverN[wid], 1);
             if (qpos < kOver) {
               sOver[wid * kOver + qpos] = make_int4(tp.pix[t], k, __float_as_int(tp.w[t]), 0);
             } else {
               for (int c = 0; c < Cg; ++c)
-                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * sG[k * kBwdGLd + c]);
+                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * grad_at(k, c));
             }
           }
         }
       }
+      if (fresh > 0) atomicAdd(&sFlag[2], fresh);
       used += 4 * pending;
       wave_lds_sync();
       const int n_over = min(uniform(sOverN[wid]), kOver);
       if (n_over > 0) {
         for (int r = 0; r < n_over; ++r) {
           const int4 e = sOver[wid * kOver + r];
-          if (ch_lane) unsafeAtomicAdd(db + (size_t)e.x * p.C + lane, __int_as_float(e.z) * sG[e.y * kBwdGLd + lane]);
+          if (ch_lane) unsafeAtomicAdd(db + (size_t)e.x * p.C + lane, __int_as_float(e.z) * grad_at(e.y, lane));
         }
         wave_lds_sync();
         if (lane == 0) sOverN[wid] = 0;
         wave_lds_sync();
       }
+      if (round_full || it >= total_items) break;
+    }
+    if (!grad_staged) {
+#pragma unroll
+      for (int i = 0; i < kGPer; ++i) {
+        const int e = threadIdx.x + i * kBlock;
+        const int c = e / n_cells, k = e - c * n_cells;
+        if (e < Cg * n_cells) sG[k * kBwdGLd + c] = gpre[i];
+      }
+      grad_staged = true;
     }
     __syncthreads();
-    // ---- counting sort by slot: exclusive prefix sum of the per-slot counts (wave 0)
+    // ---- counting sort by slot: exclusive prefix sum of the per-slot counts and a
+    // compact list of the occupied slots with their pixel and sorted range (wave 0)
     if (wid == 0) {
       constexpr int kPer = kSlots / kWave;
       int c4[kPer];
-      int run = 0;
+      int run = 0, mine = 0;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         c4[i] = sCnt[lane * kPer + i];
         run += c4[i];
+        mine += (c4[i] > 0);
       }
-      int incl = run;
+      int incl = run, inc = mine;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
+        const int oo = __shfl_up(inc, off);
+        if (lane >= off) {
+          incl += o;
+          inc += oo;
+        }
       }
-      int excl = incl - run;
+      int first = incl - run, occ = inc - mine;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        sStart[lane * kPer + i] = excl;
-        excl += c4[i];
+        sCnt[lane * kPer + i] = first;
+        if (c4[i] > 0) sMeta[occ++] = make_int2(sTag[lane * kPer + i], first | (c4[i] << 16));
+        first += c4[i];
       }
-      // compact list of occupied slots (slot order)
-      int occ_base = 0;
-      {
-        int mine = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) mine += (c4[i] > 0);
-        int inc = mine;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int o = __shfl_up(inc, off);
-          if (lane >= off) inc += o;
-        }
-        occ_base = inc - mine;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-          if (c4[i] > 0) sOcc[occ_base++] = lane * kPer + i;
-        if (lane == kWave - 1) sFlag[1] = inc;
-      }
+      if (lane == kWave - 1) sFlag[1] = inc;
       if (lane == 0) sFlag[0] = 0;
     }
     __syncthreads();
@@ -686,47 +749,62 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       const int2 e = region[r];
       if (e.x >= 0) {
         const int sl = e.x & (kSlots - 1);
-        sSorted[sStart[sl] + ((e.x >> kSlotBits) & ((1 << (24 - kSlotBits)) - 1))] =
-            make_int2(sl | ((e.x >> 24) << kSlotBits), e.y);
+        sSorted[sCnt[sl] + ((e.x >> kSlotBits) & ((1 << (24 - kSlotBits)) - 1))] = make_int2((e.x >> 24) * kBwdGLd, e.y);
       }
     }
     if (it < total_items && lane == 0) atomicOr(&sFlag[0], 1);
     __syncthreads();
     // ---- per-pixel sums in registers, one global atomic per (pixel, channel).
-    // lane = (record sub-slot rs, channel quad q): four of a pixel's taps per step,
-    // 4 channels per lane read as one 16-byte LDS load of the cell's grad row.
+    // lane = (group g, channel quad q): each 16-lane group sums one occupied slot,
+    // kRed records per step, 4 channels per lane read as one 16-byte LDS load of
+    // the record's grad row; four slots per wave at a time.
     {
       const int n_occ = sFlag[1];
-      const int rs = lane >> 4, q = lane & 15;
-      const bool q_ok = 4 * q < Cg;
-      for (int k = wid; k < n_occ; k += kWaves) {
-        const int sl = sOcc[k];
-        const int pix = sTag[sl];
-        const int r0 = sStart[sl], r1e = r0 + sCnt[sl];
+      const int g = lane >> 4, c0 = 4 * (lane & 15);
+      for (int kb = 4 * wid; kb < n_occ; kb += 4 * kWaves) {
+        const int k = kb + g;
+        const int2 m = (k < n_occ) ? sMeta[k] : make_int2(0, 0);
+        const int first = m.y & 0xffff, count = m.y >> 16;
+        const int2* srt = sSorted + first;
+        const int last = max(count - 1, 0);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int r = r0 + rs; r < r1e; r += 8) {
-          const int2 e0 = sSorted[r];
-          const bool has1 = r + 4 < r1e;
-          const int2 e1 = sSorted[has1 ? r + 4 : r];
-          const float4 g0 = *reinterpret_cast<const float4*>(sG + (e0.x >> kSlotBits) * kBwdGLd + 4 * q);
-          const float4 g1 = *reinterpret_cast<const float4*>(sG + (e1.x >> kSlotBits) * kBwdGLd + 4 * q);
-          const float w0 = __int_as_float(e0.y), w1 = has1 ? __int_as_float(e1.y) : 0.f;
-          acc.x = fmaf(w0, g0.x, acc.x);
-          acc.y = fmaf(w0, g0.y, acc.y);
-          acc.z = fmaf(w0, g0.z, acc.z);
-          acc.w = fmaf(w0, g0.w, acc.w);
-          acc.x = fmaf(w1, g1.x, acc.x);
-          acc.y = fmaf(w1, g1.y, acc.y);
-          acc.z = fmaf(w1, g1.z, acc.z);
-          acc.w = fmaf(w1, g1.w, acc.w);
+        // records of step j are read while step j - 8 is summed
+        int2 e[kRed];
+#pragma unroll
+        for (int u = 0; u < kRed; ++u) e[u] = srt[min(u, last)];
+        for (int j = 0; j < count; j += kRed) {
+          float4 gv[kRed];
+          float w[kRed];
+#pragma unroll
+          for (int u = 0; u < kRed; ++u) {
+            gv[u] = *reinterpret_cast<const float4*>(sG + e[u].x + c0);
+            w[u] = (j + u < count) ? __int_as_float(e[u].y) : 0.f;
+          }
+          if (j + kRed < count) {
+#pragma unroll
+            for (int u = 0; u < kRed; ++u) e[u] = srt[min(j + kRed + u, last)];
+          }
+#pragma unroll
+          for (int u = 0; u < kRed; ++u) {
+            acc.x = fmaf(w[u], gv[u].x, acc.x);
+            acc.y = fmaf(w[u], gv[u].y, acc.y);
+            acc.z = fmaf(w[u], gv[u].z, acc.z);
+            acc.w = fmaf(w[u], gv[u].w, acc.w);
+          }
         }
-        acc.x = sum_xor32(sum_xor16(acc.x));
-        acc.y = sum_xor32(sum_xor16(acc.y));
-        acc.z = sum_xor32(sum_xor16(acc.z));
-        acc.w = sum_xor32(sum_xor16(acc.w));
-        const float v = rs == 0 ? acc.x : rs == 1 ? acc.y : rs == 2 ? acc.z : acc.w;
-        const int c = 4 * q + rs;
-        if (q_ok && c < Cg) unsafeAtomicAdd(db + (size_t)pix * p.C + c, v);
+        // transpose through lane permutes so that each slot leaves as one atomic over
+        // 64 consecutive channels (one request per cache line instead of four)
+        const int r = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kb + i >= n_occ) break;
+          const int src = 16 * i + (lane >> 2);
+          const float v0 = __shfl(acc.x, src), v1 = __shfl(acc.y, src);
+          const float v2 = __shfl(acc.z, src), v3 = __shfl(acc.w, src);
+          const float v = r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3;
+          const int pix = __builtin_amdgcn_readlane(m.x, 16 * i);
+          if (ch_lane) unsafeAtomicAdd(db + (size_t)pix * p.C + lane, v);
+        }
       }
     }
     const int more = sFlag[0];
@@ -736,6 +814,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       sTag[e] = -1;
       sCnt[e] = 0;
     }
+    if (threadIdx.x == 0) sFlag[2] = 0;
     __syncthreads();
   }
 }
@@ -858,9 +937,9 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.Z == 0 || p.C == 0) return hipSuccess;
   const int groups = (p.C + kBwdCg - 1) / kBwdCg;
-  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int) * kSlots * 4 +
-                       sizeof(int2) * kPend * kWaves + sizeof(int2) * kBwdRegion * kWaves +
-                       sizeof(int2) * kBwdRegion * kWaves + sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + 16;
+  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int2) * kSlots +
+                       sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
+                       sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
   hipLaunchKernelGGL(sampling_vt_bwd, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }
