@@ -63,7 +63,7 @@ constexpr int kOutOfRange = 0x7ffffff0;  // buffer offset the range check turns 
 // forward
 constexpr int kTileY = 16;               // cells per workgroup (one x row)
 constexpr int kTileLd = kTileY + 1;      // padded LDS row of the output tile
-constexpr int kPend = 96;                // listed valid samples per wave
+constexpr int kPend = 64;                // listed valid samples per wave (one per lane)
 constexpr int kItems = 16;               // items per batch
 constexpr int kRec = 4 * kPend;          // tap records per wave
 constexpr int kUnroll = 4;               // loads in flight per lane and step
@@ -83,7 +83,7 @@ constexpr int kOver = 16;                // per-wave queue of taps that found no
 constexpr int kBwdPend = 64;             // listed valid samples per wave
 constexpr int kBwdRegion = 256;          // tap records per wave and round
 constexpr int kRed = 8;                  // records per reduction step and lane group
-static_assert(kBwdRegion >= 4 * kWave && kBwdPend >= kWave, "an item of a full wave of valid samples fits an empty batch");
+static_assert(kBwdRegion >= 4 * kWave && kBwdPend == kWave, "an item of a full wave of valid samples fits an empty batch");
 
 struct Rec {
   int off;   // forward: byte offset of the tap's pixel
@@ -166,10 +166,12 @@ __device__ __forceinline__ LaneCam lane_camera(const double* sP, int n, int N, d
   return lc;
 }
 
-// Phase A for one item: lane = (zl, n).  Validity by sign tests on
+// Phase A for one item: lane = n * zpc + zl (camera-major, so the listed
+// samples of one camera come out in height order).  Validity by sign tests on
 // h = P [p; 1] (SparseDriveV2 notes, "Deformable Aggregation" step 2:
 // [u, v, 1]^T ~ K (R p + t); depth > 0 and the closed pixel-centre box),
-// and one ballot for the valid-camera count of every bin.
+// and one ballot for the valid-camera count of every bin (`bin_lanes` = the
+// lanes of this lane's bin).
 struct PassA {
   uint64_t mask;
   int z, cnt;
@@ -177,7 +179,8 @@ struct PassA {
 };
 
 __device__ __forceinline__ PassA validity_pass(const LaneCam& lc, double py, double oz, double dz, int zc, int zl,
-                                               int n, bool lane_ok, int Z, int N, double Wm1, double Hm1) {
+                                               int n, bool lane_ok, int Z, int N, double Wm1, double Hm1,
+                                               uint64_t bin_lanes) {
   PassA a;
   a.z = zc + zl;
   const bool in_range = lane_ok && a.z < Z;
@@ -190,12 +193,78 @@ __device__ __forceinline__ PassA validity_pass(const LaneCam& lc, double py, dou
     valid = (h2 > 0.0) && (h0 >= 0.0) && (fma(Wm1, h2, -h0) >= 0.0) && (h1 >= 0.0) && (fma(Hm1, h2, -h1) >= 0.0);
   }
   a.mask = __ballot(valid);
-  const int Nn = (N > 0) ? N : 1;
-  const uint64_t grp = (Nn >= 64) ? ~0ull : ((1ull << Nn) - 1ull);
-  const int shift = zl * Nn;
-  a.cnt = (in_range && N > 0 && shift < 64) ? (int)__popcll((a.mask >> shift) & grp) : 0;
+  a.cnt = (in_range && N > 0) ? (int)__popcll(a.mask & bin_lanes) : 0;
   a.writer = in_range && n == 0;
   return a;
+}
+
+// Phase-A lane roles: lane = n * zpc + zl for N cameras and zpc = 64 / N bins
+// per item; bin_lanes = the lanes that hold bin zl.
+struct LaneRole {
+  int zpc, zl, ln;
+  bool ok;
+  uint64_t bin_lanes;
+};
+
+__device__ __forceinline__ LaneRole lane_role(int lane, int N) {
+  LaneRole r;
+  const int Nn = (N > 0) ? N : 1;
+  r.zpc = kWave / Nn;
+  r.ln = lane / r.zpc;
+  r.zl = lane - r.ln * r.zpc;
+  r.ok = lane < r.zpc * Nn;
+  uint64_t g = 0;
+  for (int n = 0; n < Nn; ++n) g |= 1ull << (n * r.zpc);
+  r.bin_lanes = g << r.zl;
+  return r;
+}
+
+// Merging of a listed sample's taps with those of its neighbours in the list.
+// Samples of one cell and camera are listed in height order, and along the
+// vertical line through a cell centre the image row of the projection is
+// monotone, so consecutive samples often share a row of pixels (the same quad
+// when they fall in the same pixel square).  Row r of sample s (top: taps 0-1,
+// bottom: taps 2-3) is kept by s only when the previous listed sample of the
+// same cell does not have that row; s then adds the weights of the row from the
+// following samples, for as long as each of them has it.  Every tap's weight
+// is counted exactly once, whatever the order of the rows.  raw[4 t + k] holds
+// the taps of listed sample t (key = pixel or its byte offset), cell(t) =
+// pend[t].y & 0xff.
+__device__ __forceinline__ bool row_of(const Rec* raw, int t, int key, float& wl, float& wr) {
+  const Rec q0 = raw[4 * t], q2 = raw[4 * t + 2];
+  if (q0.off == key) {
+    wl += q0.w;
+    wr += raw[4 * t + 1].w;
+    return true;
+  }
+  if (q2.off == key) {
+    wl += q2.w;
+    wr += raw[4 * t + 3].w;
+    return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ void merge_rows(const Rec* raw, const int2* pend, int s, int pending, Rec (&m)[4],
+                                           bool& top, bool& bot) {
+  const int cell = pend[s].y & 0xff;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) m[k] = raw[4 * s + k];
+  top = true;
+  bot = m[2].off != m[0].off;   // equal only at the clamped last row, whose weights are 0
+  if (s > 0 && (pend[s - 1].y & 0xff) == cell) {
+    const int pt = raw[4 * (s - 1)].off, pb = raw[4 * (s - 1) + 2].off;
+    top = m[0].off != pt && m[0].off != pb;
+    bot = bot && m[2].off != pt && m[2].off != pb;
+  }
+  if (top) {
+    for (int t = s + 1; t < pending && (pend[t].y & 0xff) == cell; ++t)
+      if (!row_of(raw, t, m[0].off, m[0].w, m[1].w)) break;
+  }
+  if (bot) {
+    for (int t = s + 1; t < pending && (pend[t].y & 0xff) == cell; ++t)
+      if (!row_of(raw, t, m[2].off, m[2].w, m[3].w)) break;
+  }
 }
 
 // Phase B for one valid sample: exact division, taps and weights.
@@ -287,6 +356,7 @@ struct FwdArgs {
   float* out;
   uint8_t* counts;
   int c_lo;          // first channel of this launch's group
+  int merge;         // merge rows shared by consecutive samples of a cell (merge_rows)
   int Cg;            // channels of the group
   int tiles_y;       // ceil(Y / kTileY)
   int write_counts;
@@ -299,8 +369,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
   using Ln = Lane<D, BF16>;
   constexpr int kVec = Ln::kVec;
   constexpr int S = kWave / L;
-  constexpr int T = S / 4;
-  static_assert(S >= 4 && (S & 3) == 0, "a step covers whole samples");
+  static_assert(S >= 4 && (S & 3) == 0, "lanes per tap divide the wave");
   const Problem& p = a.p;
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
@@ -331,20 +400,14 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
   int2* items = sItem + wid * kItems;
 
   // phase-A lane role
-  const int Nn = (p.N > 0) ? p.N : 1;
-  const int zpc = kWave / Nn;                       // height bins per item
-  const int zl = lane / Nn;
-  const int ln = lane - zl * Nn;
-  const bool lane_ok = lane < zpc * Nn;
+  const LaneRole role = lane_role(lane, p.N);
+  const int zpc = role.zpc, zl = role.zl, ln = role.ln;
   const double px = p.ox + ((double)x + 0.5) * p.dx;
-  const LaneCam lc = lane_camera(sP, ln, p.N, px);
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
 
   // gather lane role
   const int slot = lane / L;
   const int q = lane - slot * L;
-  const int tap = slot & 3;
-  const int j_off = slot >> 2;
   const int lane_off = a.c_lo * p.elem_bytes + q * 4 * D;
   const size_t batch_bytes = (size_t)p.N * p.H * p.W * p.C * p.elem_bytes;
   const unsigned char* fbase = reinterpret_cast<const unsigned char*>(p.feat) + (size_t)b * batch_bytes;
@@ -360,19 +423,24 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
 
+  // phase-A camera rows of this lane's camera; re-read at the end of every batch so
+  // they are not live through phases B and C
+  LaneCam lc = lane_camera(sP, ln, p.N, px);
   int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin
   while (it < total_items) {
-    // ---- phase A: list the valid samples of up to kItems items
+    // ---- phase A: list the valid samples of as many items as fit (an item that
+    // does not fit is left for the next batch and its validity pass repeated there)
     int pending = 0, nitems = 0;
-    while (it < total_items && nitems < kItems && pending < kPend - kWave) {
+    while (it < total_items && nitems < kItems) {
       const int cl = wid + ci * kWaves;
       const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
-      const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, lane_ok, p.Z, p.N, Wm1, Hm1);
+      const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, role.ok, p.Z, p.N, Wm1, Hm1, role.bin_lanes);
+      const int nv = (int)__popcll(pa.mask);
+      if (pending + nv > kPend) break;
       if (a.write_counts && pa.writer)
         a.counts[(((size_t)b * p.X + x) * p.Y + y_base + cl) * p.Z + pa.z] = (uint8_t)pa.cnt;
       if ((pa.mask >> lane) & 1ull)
         pend[pending + rank_below(pa.mask)] = make_int2(pa.z, cl | (ln << 8) | (pa.cnt << 16));
-      const int nv = (int)__popcll(pa.mask);
       const bool last = (zc + zpc >= p.Z);
       if (lane == 0) items[nitems] = make_int2(pending | ((pending + nv) << 12) | (last ? (1 << 24) : 0), cl);
       pending += nv;
@@ -385,55 +453,84 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
       }
     }
     wave_lds_sync();
-    // ---- phase B: taps of the listed samples
-    for (int s = lane; s < pending; s += kWave) {
-      const int2 d = pend[s];
+    // ---- phase B: taps of the listed samples (lane = sample), then rows shared
+    // by consecutive samples of a cell merged and the kept taps compacted
+    if (lane < pending) {
+      const int2 d = pend[lane];
       const int cl = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = d.y >> 16;
       const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
       const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
       const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) rec[4 * s + k] = Rec{tp.pix[k] * pix_bytes, tp.w[k]};
+      for (int k = 0; k < 4; ++k) rec[4 * lane + k] = Rec{tp.pix[k] * pix_bytes, tp.w[k]};
     }
     wave_lds_sync();
-    // ---- phase C: gather, item by item
+    {
+      if (a.merge) {
+        Rec m[4];
+        bool top = false, bot = false;
+        if (lane < pending) merge_rows(rec, pend, lane, pending, m, top, bot);
+        const uint64_t mt = __ballot(top), mb = __ballot(bot);
+        const int pos = 2 * (rank_below(mt) + rank_below(mb));
+        const int nrec = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
+        wave_lds_sync();                              // every lane has read the raw taps
+        if (top) {
+          rec[pos] = m[0];
+          rec[pos + 1] = m[1];
+        }
+        if (bot) {
+          rec[pos + (top ? 2 : 0)] = m[2];
+          rec[pos + (top ? 3 : 1)] = m[3];
+        }
+        if (lane < pending) pend[lane].x = pos;      // first kept tap of the sample
+        wave_lds_sync();
+        // items: sample ranges -> ranges of kept taps
+        if (lane < nitems) {
+          const int i0 = items[lane].x;
+          const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
+          const int r0 = (t0 < pending) ? pend[t0].x : nrec;
+          const int r1 = (t1 < pending) ? pend[t1].x : nrec;
+          items[lane].x = r0 | (r1 << 12) | (i0 & (1 << 24));
+        }
+      } else if (lane < nitems) {
+        // every tap kept: tap ranges are 4x the sample ranges
+        const int i0 = items[lane].x;
+        const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
+        items[lane].x = (4 * t0) | ((4 * t1) << 12) | (i0 & (1 << 24));
+      }
+      wave_lds_sync();
+    }
+    // ---- phase C: gather, item by item; a step takes S consecutive kept taps
     for (int k = 0; k < nitems; ++k) {
       const int i0 = uniform(items[k].x);
       const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
-      if constexpr (T == 1) {
-        const Rec* rp = rec + tap;
-        int j = t0;
-        for (; j + kUnroll <= t1; j += kUnroll) {
-          typename Ln::Raw v[kUnroll];
-          float w[kUnroll];
+      int jb = t0;
+      for (; jb + S * kUnroll <= t1; jb += S * kUnroll) {
+        typename Ln::Raw v[kUnroll];
+        float w[kUnroll];
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const Rec rr = rp[4 * (j + u)];
-            w[u] = rr.w;
-            v[u] = Ln::load(rs, rr.off + lane_off);
-          }
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
+        for (int u = 0; u < kUnroll; ++u) {
+          const Rec rr = rec[jb + u * S + slot];
+          w[u] = rr.w;
+          v[u] = Ln::load(rs, rr.off + lane_off);
         }
-        for (; j < t1; ++j) {
-          const Rec rr = rp[4 * j];
-          Ln::fma_into(acc, Ln::load(rs, rr.off + lane_off), rr.w);
-        }
-      } else {
-        for (int jb = t0; jb < t1; jb += T * kUnroll) {
-          typename Ln::Raw v[kUnroll];
-          float w[kUnroll];
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const int j = jb + u * T + j_off;
-            const bool in = j < t1;
-            const Rec rr = rec[4 * min(j, kPend - 1) + tap];
-            w[u] = in ? rr.w : 0.f;
-            v[u] = Ln::load(rs, in ? rr.off + lane_off : kOutOfRange);
-          }
+        for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
+      }
+      if (jb < t1) {
+        // last, partial step: taps past the item's end load nothing and weigh 0
+        typename Ln::Raw v[kUnroll];
+        float w[kUnroll];
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = jb + u * S + slot;
+          const bool in = j < t1;
+          const Rec rr = rec[min(j, kRec - 1)];
+          w[u] = in ? rr.w : 0.f;
+          v[u] = Ln::load(rs, in ? rr.off + lane_off : kOutOfRange);
         }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) Ln::fma_into(acc, v[u], w[u]);
       }
       if ((i0 >> 24) & 1) {
         // last item of its cell: sum the slots and park the channels in the output tile
@@ -455,6 +552,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
         for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
       }
     }
+    lc = lane_camera(sP, ln, p.N, px);
     wave_lds_sync();
   }
   __syncthreads();
@@ -565,13 +663,11 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
   int2* region = sRegion + wid * kBwdRegion;
   int2* pend = sPend + wid * kBwdPend;
-  const int Nn = (p.N > 0) ? p.N : 1;
-  const int zpc = kWave / Nn;
-  const int zl = lane / Nn;
-  const int ln = lane - zl * Nn;
-  const bool lane_ok = lane < zpc * Nn;
+  const LaneRole role = lane_role(lane, p.N);
+  const int zpc = role.zpc, zl = role.zl, ln = role.ln;
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 0;
+  Rec* raw = reinterpret_cast<Rec*>(sSorted) + wid * kBwdRegion;   // raw taps while listing (sorted area is free then)
   const int my_cells = (n_cells > wid) ? (n_cells - wid + kWaves - 1) / kWaves : 0;
   const int total_items = my_cells * items_per_cell;
   const size_t batch_elems = (size_t)p.N * p.H * p.W * p.C;
@@ -617,7 +713,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         const double py = p.oy + ((double)(y_base + cdy) + 0.5) * p.dy;
 #pragma unroll
         for (int i = 0; i < 3; ++i) lc.A[i] = fma(cp0[i], px, cp3[i]);
-        const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, lane_ok, p.Z, p.N, Wm1, Hm1);
+        const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, role.ok, p.Z, p.N, Wm1, Hm1, role.bin_lanes);
         const int nv = (int)__popcll(pa.mask);
         if (used + 4 * (pending + nv) > kBwdRegion) {
           round_full = true;
@@ -642,53 +738,79 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       }
       if (pending == 0) break;
       wave_lds_sync();
-      // phase B: taps -> table slot and rank; a tap with no slot is queued for a
+      // phase B: taps of the listed samples (lane = sample); rows shared by
+      // consecutive samples of a cell are merged (merge_rows), and each kept tap
+      // gets a table slot and a rank within it; a tap with no slot is queued for a
       // lanes-=-channels scatter (or, queue full, scattered by its lane)
-      int fresh = 0;
-      for (int s = lane; s < pending; s += kWave) {
-        const int2 d = pend[s];
-        const int k = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = (d.y >> 16) & 0x7f;
+      if (lane < pending) {
+        const int2 d = pend[lane];
+        const int n = (d.y >> 8) & 0xff, cnt = (d.y >> 16) & 0x7f;
         const int dx = (d.y >> 23) & 3, dy = (d.y >> 25) & 7;
         const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
         const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
         const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
         const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
-        // first probes of the four taps issued together; collisions take the probe loop
+#pragma unroll
+        for (int t = 0; t < 4; ++t) raw[4 * lane + t] = Rec{tp.pix[t], tp.w[t]};
+      }
+      wave_lds_sync();
+      int fresh = 0;
+      int nrec;
+      {
+        Rec m[4];
+        bool top = false, bot = false;
+        if (lane < pending) merge_rows(raw, pend, lane, pending, m, top, bot);
+        const uint64_t mt = __ballot(top), mb = __ballot(bot);
+        const int pos = used + 2 * (rank_below(mt) + rank_below(mb));
+        nrec = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
+        const int k = pend[min(lane, kBwdPend - 1)].y & 0xff;
+        bool keep[4];
+        int idx[4];
+        keep[0] = keep[1] = top;
+        keep[2] = keep[3] = bot;
+        idx[0] = pos;
+        idx[1] = pos + 1;
+        idx[2] = pos + (top ? 2 : 0);
+        idx[3] = pos + (top ? 3 : 1);
+        // first probes of the kept taps issued together; collisions take the probe loop
         int sl4[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int h = (int)(((uint32_t)tp.pix[t] * 2654435761u) >> (32 - kSlotBits));
-          const int old = atomicCAS(&sTag[h], -1, tp.pix[t]);
-          fresh += (old == -1);
-          sl4[t] = (old == -1 || old == tp.pix[t]) ? h : -2;
+          sl4[t] = -3;
+          if (keep[t]) {
+            const int h = (int)(((uint32_t)m[t].off * 2654435761u) >> (32 - kSlotBits));
+            const int old = atomicCAS(&sTag[h], -1, m[t].off);
+            fresh += (old == -1);
+            sl4[t] = (old == -1 || old == m[t].off) ? h : -2;
+          }
         }
         int rk4[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          if (sl4[t] == -2) sl4[t] = table_slot(sTag, tp.pix[t], fresh);
+          if (sl4[t] == -2) sl4[t] = table_slot(sTag, m[t].off, fresh);
           rk4[t] = (sl4[t] >= 0) ? atomicAdd(&sCnt[sl4[t]], 1) : 0;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+          if (!keep[t]) continue;
           const int sl = sl4[t];
           if (sl >= 0) {
-            const int rank = rk4[t];
-            region[used + 4 * s + t] = make_int2(sl | (rank << kSlotBits) | (k << 24), __float_as_int(tp.w[t]));
+            region[idx[t]] = make_int2(sl | (rk4[t] << kSlotBits) | (k << 24), __float_as_int(m[t].w));
           } else {
-            region[used + 4 * s + t] = make_int2(-1, 0);
+            region[idx[t]] = make_int2(-1, 0);
             fresh = kSlots;                            // table full: end the round after this batch
             const int qpos = atomicAdd(&sOverN[wid], 1);
             if (qpos < kOver) {
-              sOver[wid * kOver + qpos] = make_int4(tp.pix[t], k, __float_as_int(tp.w[t]), 0);
+              sOver[wid * kOver + qpos] = make_int4(m[t].off, k, __float_as_int(m[t].w), 0);
             } else {
               for (int c = 0; c < Cg; ++c)
-                unsafeAtomicAdd(db + (size_t)tp.pix[t] * p.C + c, tp.w[t] * grad_at(k, c));
+                unsafeAtomicAdd(db + (size_t)m[t].off * p.C + c, m[t].w * grad_at(k, c));
             }
           }
         }
       }
       if (fresh > 0) atomicAdd(&sFlag[2], fresh);
-      used += 4 * pending;
+      used += nrec;
       wave_lds_sync();
       const int n_over = min(uniform(sOverN[wid]), kOver);
       if (n_over > 0) {
@@ -882,6 +1004,11 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
   const long long tiles = (long long)p.B * p.X * a.tiles_y;
   if (tiles == 0) return hipSuccess;
   const int es = p.elem_bytes;
+  // Merging shared pixel rows pays when a cell's height bins span more than one
+  // item (many samples per cell and camera); with fewer bins its cost in the tap
+  // pass outweighs the gather it saves.
+  const int zpc = kWave / (p.N > 0 ? p.N : 1);
+  const int merge = (p.Z > zpc) ? 1 : 0;
   // channel groups of at most 1 KiB per pixel (16 lanes x 16 dwords), each
   // shrunk until its byte size maps onto a supported lane layout
   const int max_group_ch = 1024 / es;
@@ -903,6 +1030,7 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
     }
     a.c_lo = c;
     a.Cg = Cg;
+    a.merge = merge;
     a.write_counts = (first && counts != nullptr) ? 1 : 0;
     const size_t shmem = sizeof(double) * 12 * p.N + sizeof(int2) * kPend * kWaves + sizeof(Rec) * kRec * kWaves +
                          sizeof(int2) * kItems * kWaves + sizeof(float) * (size_t)(Cg > 0 ? Cg : 1) * kTileLd;
