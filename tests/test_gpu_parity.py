@@ -29,11 +29,11 @@ def run_forward(inp, with_counts=True):
     return out, cnt
 
 
-def forward_parity(inp, label, rows=None):
+def forward_parity(inp, label, rows=None, exact_edges=False):
     say(f"[case] {label}: B,N,C,H,W={inp.F.shape} X,Y,Z={inp.X},{inp.Y},{inp.Z} dtype={inp.dtype}")
     out, cnt = run_forward(inp)
     ref = oracle.oracle_forward(inp.F, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, rows=rows)
-    check_forward(out, cnt, ref, rows=rows, label=label)
+    check_forward(out, cnt, ref, rows=rows, label=label, exact_edges=exact_edges)
     return out, cnt, ref
 
 
@@ -163,6 +163,61 @@ def test_degenerate_cases():
     inp.t = inp.t - np.einsum("bnij,j->bni", inp.R, np.array([0, 0, 1e4], np.float32)).astype(np.float32)
     out, cnt = run_forward(inp)
     assert not out.any() and not cnt.any()
+
+
+def backward_parity(inp, label):
+    B, N, C, H, W = inp.F.shape
+    say(f"[case] backward {label}: B,N,C,H,W={inp.F.shape} X,Y,Z={inp.X},{inp.Y},{inp.Z}")
+    _, K, R, t = to_device(inp)
+    gF = ops.backward(torch.from_numpy(inp.grad_out).cuda(), (B, N, H, W, C), K, R, t, inp.rng6,
+                      inp.X, inp.Y, inp.Z)
+    torch.cuda.synchronize()
+    got = gF.cpu().numpy().transpose(0, 1, 4, 2, 3)
+    ref = oracle.oracle_backward(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, H, W)
+    err = rel_l2(got, ref)
+    say(f"[parity] backward {label}: rel L2 = {err:.3e}")
+    assert err <= BWD_REL_L2
+    assert np.abs(got - ref).max() <= 1e-4 + 1e-5 * np.abs(ref).max()
+
+
+def pitched(inp, pitch_deg):
+    """The same ring rig with every camera tilted by ``pitch_deg`` (the projected column
+    then moves along a cell's vertical line, so consecutive height samples change quad)."""
+    B, N = inp.K.shape[:2]
+    for b in range(B):
+        for n in range(N):
+            yaw = np.degrees(np.arctan2(inp.R[b, n, 0, 0], -inp.R[b, n, 0, 1]))
+            inp.R[b, n], inp.t[b, n] = wl.extrinsics_from_yaw(float(yaw), pitch_deg=pitch_deg)
+    return inp
+
+
+# Row merging (consecutive height samples of a cell sharing pixel rows) runs in the
+# backward always and in the forward when Z exceeds the bins of one item (64 / N).
+MERGE_CASES = [
+    ("fine bins, shared quads", dict(C=24, H=16, W=44, X=12, Y=40, Z=48), 0.0),
+    ("pitched rig, moving column", dict(C=24, H=16, W=44, X=12, Y=40, Z=24), 12.0),
+    ("pitched down", dict(C=16, H=16, W=44, X=10, Y=36, Z=20), -8.0),
+    # a zero intrinsics row puts every projection on image row (column) 0, the only one a
+    # 1-pixel-high (wide) map has: the bottom (right) tap is then the clamped duplicate
+    ("height-1 map", dict(C=16, H=1, W=22, X=12, Y=33, Z=24), 0.0),
+    ("width-1 map", dict(C=16, H=8, W=1, X=12, Y=33, Z=24), 0.0),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=lambda c: c[0].replace(" ", "_").replace(",", ""))
+def test_row_merging(case):
+    label, d, pitch = case
+    inp = wl.random_case(40 + len(label), 1, 6, d["C"], d["H"], d["W"], d["X"], d["Y"], d["Z"],
+                         rng6=(-20.0, 20.0, -20.0, 20.0, -5.0, 3.0))
+    if pitch:
+        inp = pitched(inp, pitch)
+    if d["H"] == 1:
+        inp.K[..., 1, :] = 0.0
+    if d["W"] == 1:
+        inp.K[..., 0, :] = 0.0
+    _, _, ref = forward_parity(inp, label, exact_edges=(d["H"] == 1 or d["W"] == 1))
+    assert (ref["counts"] > 0).mean() > 0.05, "the case must have samples in view"
+    backward_parity(inp, label)
 
 
 def test_gpu_invariants():
