@@ -90,3 +90,45 @@ def brute_forward(F, K, R, t, rng6, X: int, Y: int, Z: int):
                     out[b][c][i][j] = vals[c]
                 cnt[b][i][j] = cs
     return out, cnt
+
+
+def cell_value_levels(levels, K, R, t, rng6: Sequence[float], X: int, Y: int, Z: int,
+                      b: int, i: int, j: int) -> Tuple[List[float], List[int]]:
+    """Multi-level variant of ``cell_value``: levels[l][b][n][c][y][x] are the
+    maps of level l (level 0 the finest; its size is an integer multiple r_l of
+    level l's).  A camera that sees the point at level 0 contributes the mean,
+    over levels, of the bilinear value at u_l = (u + 1/2)/r_l - 1/2 (v likewise),
+    each clamped into the level's pixel-centre box."""
+    N = len(levels[0][b])
+    C = len(levels[0][b][0])
+    H0 = len(levels[0][b][0][0])
+    W0 = len(levels[0][b][0][0][0])
+    xmin, xmax, ymin, ymax, zmin, zmax = (float(r) for r in rng6)
+    px = _centre(xmin, xmax, X, i)
+    py = _centre(ymin, ymax, Y, j)
+    acc = [0.0] * C
+    counts = []
+    for k in range(Z):
+        p = (px, py, _centre(zmin, zmax, Z, k))
+        seen = []
+        for n in range(N):
+            d, u, v = _to_pixel(K[b][n], R[b][n], t[b][n], p)
+            if d > 0.0 and 0.0 <= u <= W0 - 1 and 0.0 <= v <= H0 - 1:
+                seen.append((n, u, v))
+        counts.append(len(seen))
+        if not seen:
+            continue
+        for c in range(C):
+            s = 0.0
+            for (n, u, v) in seen:
+                lv = 0.0
+                for lev in levels:
+                    H = len(lev[b][n][c])
+                    W = len(lev[b][n][c][0])
+                    r = H0 // H
+                    ul = min(max((u + 0.5) / r - 0.5, 0.0), W - 1.0)
+                    vl = min(max((v + 0.5) / r - 0.5, 0.0), H - 1.0)
+                    lv += _sample(lev[b][n][c], H, W, ul, vl)
+                s += lv / len(levels)
+            acc[c] += s / len(seen)
+    return acc, counts
