@@ -18,8 +18,11 @@ FBEV_ERR_DEVICE = 3
 FBEV_DTYPE_F32 = 0
 FBEV_DTYPE_BF16 = 1
 FBEV_MAX_CAMERAS = 64
+FBEV_MAX_LEVELS = 4
+ABI_VERSION = 2
 
-EXPORTED = ("fbev_forward", "fbev_backward", "fbev_status_string", "fbev_last_error", "fbev_abi_version")
+EXPORTED = ("fbev_forward", "fbev_backward", "fbev_forward_levels", "fbev_backward_levels", "fbev_status_string",
+            "fbev_last_error", "fbev_abi_version")
 
 
 class FeatDesc(ctypes.Structure):
@@ -58,6 +61,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fbev_backward.argtypes = [f32p, FeatDesc, f32p, f32p, f32p, BevRange,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, f32p, vp]
         lib.fbev_backward.restype = ctypes.c_int
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.fbev_forward_levels.argtypes = [vp, ctypes.c_int, FeatDesc, ctypes.c_int32, i32p, f32p, f32p, f32p,
+                                            BevRange, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, f32p, vp, vp]
+        lib.fbev_forward_levels.restype = ctypes.c_int
+        lib.fbev_backward_levels.argtypes = [f32p, FeatDesc, ctypes.c_int32, i32p, f32p, f32p, f32p, BevRange,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, f32p, vp]
+        lib.fbev_backward_levels.restype = ctypes.c_int
         lib.fbev_status_string.argtypes = [ctypes.c_int]
         lib.fbev_status_string.restype = ctypes.c_char_p
         lib.fbev_last_error.argtypes = []
@@ -81,3 +91,9 @@ def feat_desc(B: int, N: int, C: int, H: int, W: int) -> FeatDesc:
 
 def bev_range(rng6) -> BevRange:
     return BevRange(*(float(v) for v in rng6))
+
+
+def int32_array(values):
+    """A ctypes int32 array (host memory) of ``values``, or None when empty."""
+    values = [int(v) for v in values]
+    return (ctypes.c_int32 * len(values))(*values) if values else None

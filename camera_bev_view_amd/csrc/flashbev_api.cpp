@@ -69,31 +69,61 @@ fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* 
   return FBEV_OK;
 }
 
+// Feature levels: level l is (H / r_l) x (W / r_l), packed after the earlier
+// levels in each camera's pixel axis.  Fills the level fields of `p`.
+fbev_status check_levels(const fbev_feat_desc& fd, int32_t L, const int32_t* ratios, fbev::Problem& p) {
+  if (L < 1 || L > FBEV_MAX_LEVELS)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "L=%d feature levels outside [1, %d]", L, FBEV_MAX_LEVELS);
+  if (L > 1 && ratios == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "ratios is NULL with L=%d levels", L);
+  if ((int64_t)fd.N * L > 64)
+    return fail(FBEV_ERR_UNSUPPORTED, "N*L = %d*%d cameras x levels exceeds 64", fd.N, L);
+  int64_t P = 0;
+  for (int l = 0; l < L; ++l) {
+    const int r = (L == 1 && ratios == nullptr) ? 1 : ratios[l];
+    if (l == 0 && r != 1) return fail(FBEV_ERR_INVALID_ARGUMENT, "ratios[0] must be 1 (got %d)", r);
+    if (r < 1 || (fd.H > 0 && fd.H % r != 0) || (fd.W > 0 && fd.W % r != 0))
+      return fail(FBEV_ERR_INVALID_ARGUMENT, "level %d ratio %d does not divide the %dx%d level-0 map", l, r, fd.H,
+                  fd.W);
+    p.lvl_H[l] = fd.H / r;
+    p.lvl_W[l] = fd.W / r;
+    p.lvl_off[l] = (int)P;
+    p.lvl_inv_r[l] = 1.0 / (double)r;
+    P += (int64_t)p.lvl_H[l] * p.lvl_W[l];
+  }
+  for (int l = L; l < fbev::kMaxLevels; ++l) {
+    p.lvl_H[l] = p.lvl_H[0];
+    p.lvl_W[l] = p.lvl_W[0];
+    p.lvl_off[l] = 0;
+    p.lvl_inv_r[l] = 1.0;
+  }
+  p.L = L;
+  p.P = (int)P;
+  return FBEV_OK;
+}
+
 fbev_status device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FBEV_OK;
   return fail(FBEV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K, const float* R,
-                         const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out,
-                         uint8_t* counts, void* stream) {
+fbev_status forward_impl(const void* features, fbev_dtype dtype, fbev_feat_desc fd, int32_t L, const int32_t* ratios,
+                         const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                         int32_t Z, float* out, uint8_t* counts, void* stream) {
   fbev::Problem p{};
   fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  s = check_levels(fd, L, ratios, p);
   if (s != FBEV_OK) return s;
   if (dtype != FBEV_DTYPE_F32 && dtype != FBEV_DTYPE_BF16)
     return fail(FBEV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   const int es = (dtype == FBEV_DTYPE_F32) ? 4 : 2;
-  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  const int64_t n_feat = (int64_t)fd.B * fd.N * p.P * fd.C;
   const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
   const int64_t n_cnt = (int64_t)fd.B * X * Y * Z;
   if (n_feat > 0 && features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "features is NULL");
   if (n_out > 0 && out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
   if ((fd.C * es) % 4 != 0) return fail(FBEV_ERR_UNSUPPORTED, "bf16 features need an even C (got %d)", fd.C);
-  const int64_t batch_bytes = (int64_t)fd.N * fd.H * fd.W * fd.C * es;
+  const int64_t batch_bytes = (int64_t)fd.N * p.P * fd.C * es;
   if (batch_bytes >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld bytes (limit 2^31 - 1)",
                 (long long)batch_bytes);
@@ -108,17 +138,19 @@ fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc 
                        "fbev_forward launch");
 }
 
-fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R, const float* t,
-                          fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* grad_features,
-                          void* stream) {
+fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios, const float* K,
+                          const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z,
+                          float* grad_features, void* stream) {
   fbev::Problem p{};
   fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
   if (s != FBEV_OK) return s;
-  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  s = check_levels(fd, L, ratios, p);
+  if (s != FBEV_OK) return s;
+  const int64_t n_feat = (int64_t)fd.B * fd.N * p.P * fd.C;
   const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
   if (n_feat > 0 && grad_features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_features is NULL");
   if (n_out > 0 && n_feat > 0 && grad_out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
-  const int64_t batch_elems = (int64_t)fd.N * fd.H * fd.W * fd.C;
+  const int64_t batch_elems = (int64_t)fd.N * p.P * fd.C;
   if (batch_elems >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's gradient spans %lld elements (limit 2^31 - 1)",
                 (long long)batch_elems);
@@ -128,6 +160,35 @@ fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float*
   if (n_feat == 0) return FBEV_OK;
   return device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
                        "fbev_backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K, const float* R,
+                         const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out,
+                         uint8_t* counts, void* stream) {
+  return forward_impl(features, dtype, fd, 1, nullptr, K, R, t, bev_range, X, Y, Z, out, counts, stream);
+}
+
+fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R, const float* t,
+                          fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* grad_features,
+                          void* stream) {
+  return backward_impl(grad_out, fd, 1, nullptr, K, R, t, bev_range, X, Y, Z, grad_features, stream);
+}
+
+fbev_status fbev_forward_levels(const void* features, fbev_dtype dtype, fbev_feat_desc fd, int32_t L,
+                                const int32_t* ratios, const float* K, const float* R, const float* t,
+                                fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out, uint8_t* counts,
+                                void* stream) {
+  return forward_impl(features, dtype, fd, L, ratios, K, R, t, bev_range, X, Y, Z, out, counts, stream);
+}
+
+fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios,
+                                 const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X,
+                                 int32_t Y, int32_t Z, float* grad_features, void* stream) {
+  return backward_impl(grad_out, fd, L, ratios, K, R, t, bev_range, X, Y, Z, grad_features, stream);
 }
 
 const char* fbev_status_string(fbev_status s) {

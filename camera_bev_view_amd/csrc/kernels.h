@@ -6,17 +6,24 @@
 
 namespace fbev {
 
+constexpr int kMaxLevels = 4;
+
 // Everything a launch needs, already validated by the host layer.
 struct Problem {
-  const void* feat;       // [B,N,H,W,C] channels-last (fp32 or bf16 bits)
+  const void* feat;       // [B,N,P,C] channels-last (fp32 or bf16 bits); P pixels per camera
   const float* K;         // [B,N,3,3]
   const float* R;         // [B,N,3,3]
   const float* t;         // [B,N,3]
-  int B, N, C, H, W;
+  int B, N, C, H, W;      // H, W: the level-0 map (the in-view test)
   int X, Y, Z;
   double ox, dx, oy, dy, oz, dz;   // voxel centre i -> o + (i + 1/2) d
   int elem_bytes;         // 4 (fp32) or 2 (bf16)
   int vec_bytes;          // bytes one lane moves per tap: 16 or 4
+  // feature levels: level l is lvl_H[l] x lvl_W[l] at pixel lvl_off[l] of a camera's
+  // P = sum of H_l W_l pixels, level coordinate u_l = (u + 1/2) lvl_inv_r[l] - 1/2
+  int L, P;
+  int lvl_H[kMaxLevels], lvl_W[kMaxLevels], lvl_off[kMaxLevels];
+  double lvl_inv_r[kMaxLevels];
 };
 
 hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream);

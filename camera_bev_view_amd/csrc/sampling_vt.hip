@@ -198,18 +198,19 @@ __device__ __forceinline__ PassA validity_pass(const LaneCam& lc, double py, dou
   return a;
 }
 
-// Phase-A lane roles: lane = n * zpc + zl for N cameras and zpc = 64 / N bins
-// per item; bin_lanes = the lanes that hold bin zl.
+// Phase-A lane roles: lane = n * zpc + zl for N cameras and zpc = 64 / (N L)
+// bins per item (an item's samples, one per feature level each, then fill at
+// most one wave); bin_lanes = the lanes that hold bin zl.
 struct LaneRole {
   int zpc, zl, ln;
   bool ok;
   uint64_t bin_lanes;
 };
 
-__device__ __forceinline__ LaneRole lane_role(int lane, int N) {
+__device__ __forceinline__ LaneRole lane_role(int lane, int N, int L) {
   LaneRole r;
   const int Nn = (N > 0) ? N : 1;
-  r.zpc = kWave / Nn;
+  r.zpc = kWave / (Nn * L);
   r.ln = lane / r.zpc;
   r.zl = lane - r.ln * r.zpc;
   r.ok = lane < r.zpc * Nn;
@@ -227,9 +228,9 @@ __device__ __forceinline__ LaneRole lane_role(int lane, int N) {
 // bottom: taps 2-3) is kept by s only when the previous listed sample of the
 // same cell does not have that row; s then adds the weights of the row from the
 // following samples, for as long as each of them has it.  Every tap's weight
-// is counted exactly once, whatever the order of the rows.  raw[4 t + k] holds
-// the taps of listed sample t (key = pixel or its byte offset), cell(t) =
-// pend[t].y & 0xff.
+// is counted exactly once, whatever the order of the rows.  raw[4 (t L + l) + k]
+// holds the taps of listed sample t at feature level l (key = pixel or its byte
+// offset), cell(t) = pend[t].y & 0xff; rows merge only within one level.
 __device__ __forceinline__ bool row_of(const Rec* raw, int t, int key, float& wl, float& wr) {
   const Rec q0 = raw[4 * t], q2 = raw[4 * t + 2];
   if (q0.off == key) {
@@ -245,25 +246,26 @@ __device__ __forceinline__ bool row_of(const Rec* raw, int t, int key, float& wl
   return false;
 }
 
-__device__ __forceinline__ void merge_rows(const Rec* raw, const int2* pend, int s, int pending, Rec (&m)[4],
-                                           bool& top, bool& bot) {
+__device__ __forceinline__ void merge_rows(const Rec* raw, const int2* pend, int s, int l, int L, int pending,
+                                           Rec (&m)[4], bool& top, bool& bot) {
+  const int v = s * L + l;                       // taps of (sample s, level l) start at raw[4 v]
   const int cell = pend[s].y & 0xff;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) m[k] = raw[4 * s + k];
+  for (int k = 0; k < 4; ++k) m[k] = raw[4 * v + k];
   top = true;
   bot = m[2].off != m[0].off;   // equal only at the clamped last row, whose weights are 0
   if (s > 0 && (pend[s - 1].y & 0xff) == cell) {
-    const int pt = raw[4 * (s - 1)].off, pb = raw[4 * (s - 1) + 2].off;
+    const int pt = raw[4 * (v - L)].off, pb = raw[4 * (v - L) + 2].off;
     top = m[0].off != pt && m[0].off != pb;
     bot = bot && m[2].off != pt && m[2].off != pb;
   }
   if (top) {
     for (int t = s + 1; t < pending && (pend[t].y & 0xff) == cell; ++t)
-      if (!row_of(raw, t, m[0].off, m[0].w, m[1].w)) break;
+      if (!row_of(raw, t * L + l, m[0].off, m[0].w, m[1].w)) break;
   }
   if (bot) {
     for (int t = s + 1; t < pending && (pend[t].y & 0xff) == cell; ++t)
-      if (!row_of(raw, t, m[2].off, m[2].w, m[3].w)) break;
+      if (!row_of(raw, t * L + l, m[2].off, m[2].w, m[3].w)) break;
   }
 }
 
@@ -273,22 +275,44 @@ struct Taps {
   float w[4];
 };
 
-__device__ __forceinline__ Taps tap_geometry(const double* sP, int n, double px, double py, double pz, int cnt,
-                                             int H, int W) {
+template <class T>
+__device__ __forceinline__ T level_pick(const T (&a)[kMaxLevels], int l) {
+  return l == 0 ? a[0] : l == 1 ? a[1] : l == 2 ? a[2] : a[3];
+}
+
+// Phase B for one valid sample at feature level `lvl`: exact division, the
+// level's coordinates (u_l = (u + 1/2) / r_l - 1/2, clamped to the level's
+// pixel-centre box), taps and weights; `rc` = 1 / (count * levels).
+template <bool ML>
+__device__ __forceinline__ Taps tap_geometry(const double* sP, int n, double px, double py, double pz, float rc,
+                                             int lvl, const Problem& p) {
   const double* P = sP + n * 12;
   const double h0 = fma(P[0], px, fma(P[1], py, fma(P[2], pz, P[3])));
   const double h1 = fma(P[4], px, fma(P[5], py, fma(P[6], pz, P[7])));
   const double h2 = fma(P[8], px, fma(P[9], py, fma(P[10], pz, P[11])));
   const double r = recip(h2);
-  const double u = h0 * r, v = h1 * r;
-  // validity was decided in phase A; clamping only guards rounding at the edges
+  double u = h0 * r, v = h1 * r;
+  int H = p.H, W = p.W, base = n * p.P;
+  if (ML && lvl > 0) {
+    const double ir = level_pick(p.lvl_inv_r, lvl);
+    H = level_pick(p.lvl_H, lvl);
+    W = level_pick(p.lvl_W, lvl);
+    base += level_pick(p.lvl_off, lvl);
+    u = fma(u + 0.5, ir, -0.5);
+    v = fma(v + 0.5, ir, -0.5);
+  }
+  // validity was decided in phase A at level 0; clamping guards rounding at the
+  // edges there and is the border rule at coarser levels
+  if (ML) {
+    u = fmin(fmax(u, 0.0), (double)(W - 1));
+    v = fmin(fmax(v, 0.0), (double)(H - 1));
+  }
   const double fu = fmin(fmax(floor(u), 0.0), (double)(W - 1));
   const double fv = fmin(fmax(floor(v), 0.0), (double)(H - 1));
   const int x0 = (int)fu, y0 = (int)fv;
   const float fa = (float)(u - fu), fb = (float)(v - fv);
-  const float rc = __builtin_amdgcn_rcpf((float)cnt);
   Taps t;
-  const int p00 = (n * H + y0) * W + x0;
+  const int p00 = base + y0 * W + x0;
   const int dxp = (x0 + 1 < W) ? 1 : 0;      // the clamped tap has weight 0
   const int dyp = (y0 + 1 < H) ? W : 0;
   t.pix[0] = p00;
@@ -362,10 +386,19 @@ struct FwdArgs {
   int write_counts;
 };
 
+// Occupancy floor the forward asks the register allocator for: six waves per
+// SIMD for single-level launches whose lanes accumulate at most 10 channels
+// (they then fit without spilling), no constraint otherwise.
+template <int D, bool BF16, bool ML>
+struct FwdWaves {
+  static constexpr int value = (!ML && (BF16 ? 2 * D : D) <= 10) ? 6 : 1;
+};
+
 // Forward kernel.  L lanes cover one tap's channel group with D dwords each
 // (L * D * 4 == group bytes); S = 64 / L slots; T = S / 4 samples per step.
-template <int D, int L, bool BF16>
-__global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
+template <int D, int L, bool BF16, bool ML>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FwdWaves<D, BF16, ML>::value)))
+void sampling_vt_fwd(FwdArgs a) {
   using Ln = Lane<D, BF16>;
   constexpr int kVec = Ln::kVec;
   constexpr int S = kWave / L;
@@ -400,8 +433,10 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
   int2* items = sItem + wid * kItems;
 
   // phase-A lane role
-  const LaneRole role = lane_role(lane, p.N);
+  const int nlev = ML ? p.L : 1;                  // feature levels (1 unless ML)
+  const LaneRole role = lane_role(lane, p.N, nlev);
   const int zpc = role.zpc, zl = role.zl, ln = role.ln;
+  const int vs = ML ? lane / nlev : lane, vl = lane - vs * nlev;  // phase-B lane role: (sample, level)
   const double px = p.ox + ((double)x + 0.5) * p.dx;
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
 
@@ -409,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
   const int slot = lane / L;
   const int q = lane - slot * L;
   const int lane_off = a.c_lo * p.elem_bytes + q * 4 * D;
-  const size_t batch_bytes = (size_t)p.N * p.H * p.W * p.C * p.elem_bytes;
+  const size_t batch_bytes = (size_t)p.N * p.P * p.C * p.elem_bytes;
   const unsigned char* fbase = reinterpret_cast<const unsigned char*>(p.feat) + (size_t)b * batch_bytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(fbase), 0, (int)batch_bytes, 0x00020000);
@@ -436,7 +471,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
       const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
       const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, role.ok, p.Z, p.N, Wm1, Hm1, role.bin_lanes);
       const int nv = (int)__popcll(pa.mask);
-      if (pending + nv > kPend) break;
+      if ((pending + nv) * nlev > kPend) break;
       if (a.write_counts && pa.writer)
         a.counts[(((size_t)b * p.X + x) * p.Y + y_base + cl) * p.Z + pa.z] = (uint8_t)pa.cnt;
       if ((pa.mask >> lane) & 1ull)
@@ -453,14 +488,16 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
       }
     }
     wave_lds_sync();
-    // ---- phase B: taps of the listed samples (lane = sample), then rows shared
-    // by consecutive samples of a cell merged and the kept taps compacted
-    if (lane < pending) {
-      const int2 d = pend[lane];
+    // ---- phase B: taps of the listed samples (lane = (sample, feature level)),
+    // then rows shared by consecutive samples of a cell merged and the kept taps
+    // compacted
+    const int nvirt = pending * nlev;
+    if (lane < nvirt) {
+      const int2 d = pend[vs];
       const int cl = d.y & 0xff, n = (d.y >> 8) & 0xff, cnt = d.y >> 16;
       const double py = p.oy + ((double)(y_base + cl) + 0.5) * p.dy;
       const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
-      const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
+      const Taps tp = tap_geometry<ML>(sP, n, px, py, pz, __builtin_amdgcn_rcpf((float)(cnt * nlev)), vl, p);
 #pragma unroll
       for (int k = 0; k < 4; ++k) rec[4 * lane + k] = Rec{tp.pix[k] * pix_bytes, tp.w[k]};
     }
@@ -469,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
       if (a.merge) {
         Rec m[4];
         bool top = false, bot = false;
-        if (lane < pending) merge_rows(rec, pend, lane, pending, m, top, bot);
+        if (lane < nvirt) merge_rows(rec, pend, vs, vl, nlev, pending, m, top, bot);
         const uint64_t mt = __ballot(top), mb = __ballot(bot);
         const int pos = 2 * (rank_below(mt) + rank_below(mb));
         const int nrec = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
@@ -482,21 +519,21 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_fwd(FwdArgs a) {
           rec[pos + (top ? 2 : 0)] = m[2];
           rec[pos + (top ? 3 : 1)] = m[3];
         }
-        if (lane < pending) pend[lane].x = pos;      // first kept tap of the sample
+        if (lane < nvirt) pend[lane].x = pos;        // first kept tap of (sample, level) number `lane`
         wave_lds_sync();
         // items: sample ranges -> ranges of kept taps
         if (lane < nitems) {
           const int i0 = items[lane].x;
           const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
-          const int r0 = (t0 < pending) ? pend[t0].x : nrec;
-          const int r1 = (t1 < pending) ? pend[t1].x : nrec;
+          const int r0 = (t0 < pending) ? pend[t0 * nlev].x : nrec;
+          const int r1 = (t1 < pending) ? pend[t1 * nlev].x : nrec;
           items[lane].x = r0 | (r1 << 12) | (i0 & (1 << 24));
         }
       } else if (lane < nitems) {
-        // every tap kept: tap ranges are 4x the sample ranges
+        // every tap kept: tap ranges are 4 L x the sample ranges
         const int i0 = items[lane].x;
         const int t0 = i0 & 0xfff, t1 = (i0 >> 12) & 0xfff;
-        items[lane].x = (4 * t0) | ((4 * t1) << 12) | (i0 & (1 << 24));
+        items[lane].x = (4 * nlev * t0) | ((4 * nlev * t1) << 12) | (i0 & (1 << 24));
       }
       wave_lds_sync();
     }
@@ -591,6 +628,7 @@ __device__ __forceinline__ int table_slot(int* sTag, int pix, int& fresh) {
   return -1;
 }
 
+template <bool ML>
 __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   static_assert(kSlots == (1 << kSlotBits), "table size matches the hash width");
   static_assert(4 * kWaves * kBwdRegion < (1 << 16), "sorted positions and per-slot counts fit 16 bits");
@@ -663,14 +701,16 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
   int2* region = sRegion + wid * kBwdRegion;
   int2* pend = sPend + wid * kBwdPend;
-  const LaneRole role = lane_role(lane, p.N);
+  const int nlev = ML ? p.L : 1;                  // feature levels (1 unless ML)
+  const LaneRole role = lane_role(lane, p.N, nlev);
   const int zpc = role.zpc, zl = role.zl, ln = role.ln;
+  const int vs = ML ? lane / nlev : lane, vl = lane - vs * nlev;  // phase-B lane role: (sample, level)
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 0;
   Rec* raw = reinterpret_cast<Rec*>(sSorted) + wid * kBwdRegion;   // raw taps while listing (sorted area is free then)
   const int my_cells = (n_cells > wid) ? (n_cells - wid + kWaves - 1) / kWaves : 0;
   const int total_items = my_cells * items_per_cell;
-  const size_t batch_elems = (size_t)p.N * p.H * p.W * p.C;
+  const size_t batch_elems = (size_t)p.N * p.P * p.C;
   float* db = a.dF + (size_t)b * batch_elems + c_lo;
   const bool ch_lane = lane < Cg;
   // grad value of cell k, channel c of the group, from global memory (for taps that
@@ -715,11 +755,11 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         for (int i = 0; i < 3; ++i) lc.A[i] = fma(cp0[i], px, cp3[i]);
         const PassA pa = validity_pass(lc, py, p.oz, p.dz, zc, zl, ln, role.ok, p.Z, p.N, Wm1, Hm1, role.bin_lanes);
         const int nv = (int)__popcll(pa.mask);
-        if (used + 4 * (pending + nv) > kBwdRegion) {
+        if (used + 4 * nlev * (pending + nv) > kBwdRegion) {
           round_full = true;
           break;
         }
-        if (pending + nv > kBwdPend) break;
+        if ((pending + nv) * nlev > kBwdPend) break;
         if ((pa.mask >> lane) & 1ull)
           pend[pending + rank_below(pa.mask)] =
               make_int2(pa.z, k | (ln << 8) | (pa.cnt << 16) | (cdx << 23) | (cdy << 25));
@@ -742,14 +782,15 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       // consecutive samples of a cell are merged (merge_rows), and each kept tap
       // gets a table slot and a rank within it; a tap with no slot is queued for a
       // lanes-=-channels scatter (or, queue full, scattered by its lane)
-      if (lane < pending) {
-        const int2 d = pend[lane];
+      const int nvirt = pending * nlev;
+      if (lane < nvirt) {
+        const int2 d = pend[vs];
         const int n = (d.y >> 8) & 0xff, cnt = (d.y >> 16) & 0x7f;
         const int dx = (d.y >> 23) & 3, dy = (d.y >> 25) & 7;
         const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
         const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
         const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
-        const Taps tp = tap_geometry(sP, n, px, py, pz, cnt, p.H, p.W);
+        const Taps tp = tap_geometry<ML>(sP, n, px, py, pz, __builtin_amdgcn_rcpf((float)(cnt * nlev)), vl, p);
 #pragma unroll
         for (int t = 0; t < 4; ++t) raw[4 * lane + t] = Rec{tp.pix[t], tp.w[t]};
       }
@@ -759,11 +800,11 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       {
         Rec m[4];
         bool top = false, bot = false;
-        if (lane < pending) merge_rows(raw, pend, lane, pending, m, top, bot);
+        if (lane < nvirt) merge_rows(raw, pend, vs, vl, nlev, pending, m, top, bot);
         const uint64_t mt = __ballot(top), mb = __ballot(bot);
         const int pos = used + 2 * (rank_below(mt) + rank_below(mb));
         nrec = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
-        const int k = pend[min(lane, kBwdPend - 1)].y & 0xff;
+        const int k = pend[min(vs, kBwdPend - 1)].y & 0xff;
         bool keep[4];
         int idx[4];
         keep[0] = keep[1] = top;
@@ -952,7 +993,10 @@ __global__ void fill_zero_f32(float* __restrict__ dst, size_t n) {
 
 template <int D, int L, bool BF16>
 void launch_fwd_group(const FwdArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
-  hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16>), grid, dim3(kBlock), shmem, stream, a);
+  if (a.p.L > 1)
+    hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16, true>), grid, dim3(kBlock), shmem, stream, a);
+  else
+    hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16, false>), grid, dim3(kBlock), shmem, stream, a);
 }
 
 // Supported lane layouts (dwords per lane D, lanes per tap L).
@@ -1007,7 +1051,7 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
   // Merging shared pixel rows pays when a cell's height bins span more than one
   // item (many samples per cell and camera); with fewer bins its cost in the tap
   // pass outweighs the gather it saves.
-  const int zpc = kWave / (p.N > 0 ? p.N : 1);
+  const int zpc = kWave / ((p.N > 0 ? p.N : 1) * p.L);
   const int merge = (p.Z > zpc) ? 1 : 0;
   // channel groups of at most 1 KiB per pixel (16 lanes x 16 dwords), each
   // shrunk until its byte size maps onto a supported lane layout
@@ -1047,7 +1091,7 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
 }
 
 hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream) {
-  const size_t nF = (size_t)p.B * p.N * p.H * p.W * p.C;
+  const size_t nF = (size_t)p.B * p.N * p.P * p.C;
   if (nF == 0) return hipSuccess;
   {
     const size_t blocks = (nF / 4 + 255) / 256;
@@ -1068,7 +1112,11 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int2) * kSlots +
                        sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
                        sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
-  hipLaunchKernelGGL(sampling_vt_bwd, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
+  if (p.L > 1)
+    hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
+  else
+    hipLaunchKernelGGL(sampling_vt_bwd<false>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream,
+                       a);
   return hipGetLastError();
 }
 

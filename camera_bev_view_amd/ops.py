@@ -101,3 +101,81 @@ def bev_sample(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torc
     if not channels_last:
         features = features.permute(0, 1, 3, 4, 2).contiguous()
     return SamplingVT.apply(features, K, R, t, tuple(bev_range), X, Y, Z)
+
+
+# ---- feature pyramids (fbev_forward_levels / fbev_backward_levels)
+
+def level_ratios(H: int, W: int, shapes: Sequence[Sequence[int]]) -> Tuple[int, ...]:
+    """Integer ratios r_l of level shapes [(H_l, W_l), ...] to the level-0 map H x W."""
+    ratios = []
+    for (h, w) in shapes:
+        if h <= 0 or w <= 0 or H % h or W % w or H // h != W // w:
+            raise ValueError(f"level {h}x{w} is not an integer downscale of {H}x{W}")
+        ratios.append(H // h)
+    return tuple(ratios)
+
+
+def pack_levels(levels: Sequence[torch.Tensor]) -> torch.Tensor:
+    """[B,N,H_l,W_l,C] level maps -> the packed [B,N,P,C] layout (one copy)."""
+    B, N, _, _, C = levels[0].shape
+    return torch.cat([lv.reshape(B, N, -1, C) for lv in levels], dim=2).contiguous()
+
+
+def unpack_levels(packed: torch.Tensor, shapes: Sequence[Sequence[int]]) -> list:
+    """The packed [B,N,P,C] layout -> views [B,N,H_l,W_l,C]."""
+    B, N, _, C = packed.shape
+    out, off = [], 0
+    for (h, w) in shapes:
+        out.append(packed[:, :, off:off + h * w].reshape(B, N, h, w, C))
+        off += h * w
+    return out
+
+
+def forward_levels(packed: torch.Tensor, shapes: Sequence[Sequence[int]], K: torch.Tensor, R: torch.Tensor,
+                   t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, Z: int, *,
+                   with_counts: bool = False, out: Optional[torch.Tensor] = None):
+    """fbev_forward_levels on packed level features [B,N,P,C]; ``shapes`` lists (H_l, W_l),
+    level 0 first.  Returns (out [B,C,X,Y] fp32, counts or None)."""
+    if packed.dim() != 4:
+        raise ValueError("packed features must be [B,N,P,C]")
+    if packed.dtype not in _DTYPES:
+        raise ValueError(f"unsupported feature dtype {packed.dtype}")
+    if not packed.is_cuda or not packed.is_contiguous():
+        raise ValueError("features must be a contiguous device tensor")
+    B, N, P, C = packed.shape
+    H, W = (int(v) for v in shapes[0])
+    ratios = level_ratios(H, W, shapes)
+    if P != sum(int(h) * int(w) for (h, w) in shapes):
+        raise ValueError(f"packed pixel axis {P} does not match the level shapes {list(shapes)}")
+    dev = packed.device
+    _check_cams(K, R, t, B, N, dev)
+    if out is None:
+        out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
+    lib = _lib.load()
+    _lib.check(lib.fbev_forward_levels(_ptr(packed), _DTYPES[packed.dtype], _lib.feat_desc(B, N, C, H, W),
+                                       len(ratios), _lib.int32_array(ratios), _ptr(K), _ptr(R), _ptr(t),
+                                       _lib.bev_range(bev_range), X, Y, Z, _ptr(out), _ptr(counts), _stream(dev)))
+    return out, counts
+
+
+def backward_levels(grad_out: torch.Tensor, B: int, N: int, C: int, shapes: Sequence[Sequence[int]],
+                    K: torch.Tensor, R: torch.Tensor, t: torch.Tensor, bev_range: Sequence[float],
+                    X: int, Y: int, Z: int) -> torch.Tensor:
+    """fbev_backward_levels: dL/dF as fp32 packed [B,N,P,C] from grad_out [B,C,X,Y]."""
+    if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32 [B,C,X,Y]")
+    grad_out = grad_out.contiguous()
+    H, W = (int(v) for v in shapes[0])
+    ratios = level_ratios(H, W, shapes)
+    P = sum(int(h) * int(w) for (h, w) in shapes)
+    dev = grad_out.device
+    _check_cams(K, R, t, B, N, dev)
+    gF = torch.empty((B, N, P, C), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.fbev_backward_levels(_ptr(grad_out), _lib.feat_desc(B, N, C, H, W), len(ratios),
+                                        _lib.int32_array(ratios), _ptr(K), _ptr(R), _ptr(t),
+                                        _lib.bev_range(bev_range), X, Y, Z, _ptr(gF), _stream(dev)))
+    return gF

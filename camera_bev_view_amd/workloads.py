@@ -198,3 +198,71 @@ def random_case(seed: int, B: int, N: int, C: int, H: int, W: int, X: int, Y: in
     F = make_features(1000 + seed, B, N, C, H, W, dtype)
     g = make_grad_out(1000 + seed, B, C, X, Y) if with_grad else None
     return Inputs(F, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y, Z, dtype, g)
+
+
+# ---- feature pyramids (multi-level inputs)
+#
+# The pyramid stands in for FPN outputs at growing strides (the SparseDriveV2
+# notes' "Multi-scale features": P2-P5).  Level 0 is the finest map; level l
+# is smaller by an integer ratio r_l in both directions, and K is in level-0
+# pixels.  The nuScenes-shaped pyramid takes strides 8, 16 and 32 of a
+# 256 x 704 image: 32 x 88, 16 x 44 and 8 x 22 maps.
+
+PYRAMIDS: Dict[str, dict] = {
+    "pyramid": dict(cid=5, B=1, N=6, C=64, H=32, W=88, ratios=(1, 2, 4), X=200, Y=200, Z=8, rng6=_R50,
+                    dtype="f32", per_sample=False),
+}
+
+
+def make_level_features(cid: int, B: int, N: int, C: int, shapes, dtype: str = "f32"):
+    """Logical per-level features [B,N,C,H_l,W_l] ~ N(0,1); level l from ``default_rng([cid, 1, l])``."""
+    out = []
+    for l, (H, W) in enumerate(shapes):
+        g = np.random.default_rng([cid, 1, l])
+        F = g.standard_normal((B, N, C, H, W), dtype=np.float32)
+        if dtype == "bf16":
+            F = bf16_bits_to_f32(to_bf16_bits(F))
+        elif dtype != "f32":
+            raise ValueError(f"unknown dtype {dtype!r}")
+        out.append(F)
+    return out
+
+
+@dataclasses.dataclass
+class LevelInputs:
+    levels: list             # logical [B,N,C,H_l,W_l] per level
+    shapes: Tuple[Tuple[int, int], ...]
+    K: np.ndarray            # [B,N,3,3] in level-0 pixels
+    R: np.ndarray
+    t: np.ndarray
+    rng6: Tuple[float, ...]
+    X: int
+    Y: int
+    Z: int
+    dtype: str
+    grad_out: Optional[np.ndarray] = None
+
+
+def level_shapes(H: int, W: int, ratios) -> Tuple[Tuple[int, int], ...]:
+    return tuple((H // r, W // r) for r in ratios)
+
+
+def make_level_inputs(name: str = "pyramid", dtype: Optional[str] = None, with_grad: bool = False) -> LevelInputs:
+    w = PYRAMIDS[name]
+    dt = dtype or w["dtype"]
+    shapes = level_shapes(w["H"], w["W"], w["ratios"])
+    K, R, t = make_rig(w["cid"], w["B"], w["N"], w["H"], w["W"], w["per_sample"])
+    levels = make_level_features(w["cid"], w["B"], w["N"], w["C"], shapes, dt)
+    g = make_grad_out(w["cid"], w["B"], w["C"], w["X"], w["Y"]) if with_grad else None
+    return LevelInputs(levels, shapes, K, R, t, tuple(float(np.float32(r)) for r in w["rng6"]), w["X"], w["Y"],
+                       w["Z"], dt, g)
+
+
+def random_level_case(seed: int, B: int, N: int, C: int, H: int, W: int, ratios, X: int, Y: int, Z: int,
+                      rng6=(-50.0, 50.0, -50.0, 50.0, -5.0, 3.0), dtype: str = "f32") -> LevelInputs:
+    """An arbitrary-size seeded pyramid case (ragged / edge-case parity runs)."""
+    shapes = level_shapes(H, W, ratios)
+    K, R, t = make_rig(2000 + seed, B, N, H, W, True)
+    levels = make_level_features(2000 + seed, B, N, C, shapes, dtype)
+    g = make_grad_out(2000 + seed, B, C, X, Y)
+    return LevelInputs(levels, shapes, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y, Z, dtype, g)

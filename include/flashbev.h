@@ -45,14 +45,17 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 1
+#define FBEV_ABI_VERSION 2
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
+#define FBEV_MAX_LEVELS 4
 
 typedef enum {
   FBEV_OK = 0,
-  FBEV_ERR_INVALID_ARGUMENT = 1, /* negative size, NULL pointer for a non-empty buffer, bad range, N > FBEV_MAX_CAMERAS */
-  FBEV_ERR_UNSUPPORTED = 2,      /* unknown dtype, odd C for bf16, misaligned features, per-sample features >= 2 GiB */
+  FBEV_ERR_INVALID_ARGUMENT = 1, /* negative size, NULL pointer for a non-empty buffer, bad range, N > FBEV_MAX_CAMERAS,
+                                    bad feature levels */
+  FBEV_ERR_UNSUPPORTED = 2,      /* unknown dtype, odd C for bf16, misaligned features, per-sample features >= 2 GiB,
+                                    cameras x levels > 64 */
   FBEV_ERR_DEVICE = 3            /* the HIP runtime reported an error when enqueueing */
 } fbev_status;
 
@@ -107,6 +110,47 @@ fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc 
 fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,
                           const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z,
                           float* grad_features, void* stream);
+
+/*
+ * Multi-level (feature-pyramid) variants.  The pages name a multi-scale fused
+ * view transform as the next step (FlashBEV notes, "Limitation" item 4 and
+ * "Takeaway" item 4) and describe the FPN pyramid it would read
+ * (SparseDriveV2 notes, "Multi-scale features": P2-P5 at growing strides);
+ * they do not define the fused operator, so this library fixes it as the
+ * single-level operator with each camera's sample replaced by the mean of its
+ * L level samples:
+ *   - level l is (H / r_l) x (W / r_l) with integer ratios r_l, r_0 = 1; K maps
+ *     to level-0 pixels; validity and the camera count are decided at level 0
+ *     exactly as in fbev_forward;
+ *   - level l is sampled at u_l = (u + 1/2) / r_l - 1/2 (v likewise): a level
+ *     pixel centre sits at the centre of the r_l x r_l level-0 block it covers;
+ *     u_l, v_l are clamped to the level's pixel-centre box (border replication);
+ *   - camera sample = (1/L) sum_l bilinear_l; then the valid-camera mean and
+ *     the height sum as in fbev_forward.  L = 1 is fbev_forward.
+ *
+ *   features : [B, N, P, C] with P = sum_l (H/r_l)(W/r_l): per camera, level 0's
+ *              pixels row-major, then level 1's, ... (dtype and alignment as for
+ *              fbev_forward).  fd.H, fd.W describe level 0.
+ *   L        : 1..FBEV_MAX_LEVELS levels, with N * L <= 64.
+ *   ratios   : host array of L ratios (ratios[0] = 1, each divides H and W), read
+ *              during the call only; may be NULL when L = 1.
+ * Other arguments, outputs and errors as for fbev_forward.
+ */
+fbev_status fbev_forward_levels(const void* features, fbev_dtype dtype, fbev_feat_desc fd, int32_t L,
+                                const int32_t* ratios, const float* K, const float* R, const float* t,
+                                fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out, uint8_t* counts,
+                                void* stream);
+
+/*
+ * Gradient of fbev_forward_levels with respect to the packed level features:
+ * grad_features is [B, N, P, C] fp32 in the same packing, fully overwritten
+ * (zeroed on `stream`, then accumulated with fp32 atomics).  The adjoint of the
+ * level mean scales each level's taps by 1/L.  Other arguments as for
+ * fbev_forward_levels and fbev_backward.
+ */
+fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios,
+                                 const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X,
+                                 int32_t Y, int32_t Z, float* grad_features, void* stream);
 
 /* Static text for a status code. */
 const char* fbev_status_string(fbev_status s);

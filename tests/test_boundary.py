@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fbev_abi_version() == 1
+    assert lib.fbev_abi_version() == _lib.ABI_VERSION
     assert lib.fbev_status_string(0) == b"ok"
     assert lib.fbev_status_string(1) == b"invalid argument"
     assert lib.fbev_status_string(2) == b"unsupported"
@@ -94,6 +94,42 @@ def test_backward_validation(lib, kwargs, status, msg):
     assert msg in lib.fbev_last_error().decode()
 
 
+def fwd_levels(lib, L=3, ratios=(1, 2, 4), desc=(1, 6, 64, 32, 88), feat=FAKE, X=8, Y=8, Z=4, out=FAKE):
+    return lib.fbev_forward_levels(feat, 0, _lib.feat_desc(*desc), L, _lib.int32_array(ratios), FAKE, FAKE, FAKE,
+                                   _lib.bev_range(RNG), X, Y, Z, out, None, None)
+
+
+def bwd_levels(lib, L=3, ratios=(1, 2, 4), desc=(1, 6, 64, 32, 88), gF=FAKE):
+    return lib.fbev_backward_levels(FAKE, _lib.feat_desc(*desc), L, _lib.int32_array(ratios), FAKE, FAKE, FAKE,
+                                    _lib.bev_range(RNG), 8, 8, 4, gF, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(L=0, ratios=()), 1, "feature levels outside"),
+    (dict(L=5, ratios=(1, 2, 4, 8, 16)), 1, "feature levels outside"),
+    (dict(L=2, ratios=()), 1, "ratios is NULL"),
+    (dict(ratios=(2, 4, 8)), 1, "ratios[0] must be 1"),
+    (dict(ratios=(1, 3, 4)), 1, "does not divide"),
+    (dict(ratios=(1, 0, 4)), 1, "does not divide"),
+    (dict(desc=(1, 6, 64, 32, 90), ratios=(1, 2, 4)), 1, "does not divide"),
+    (dict(desc=(1, 22, 64, 32, 88)), 2, "cameras x levels exceeds 64"),
+    (dict(feat=None), 1, "features is NULL"),
+])
+def test_forward_levels_validation(lib, kwargs, status, msg):
+    assert fwd_levels(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(L=9, ratios=(1,) * 9), 1, "feature levels outside"),
+    (dict(ratios=(1, 2, 5)), 1, "does not divide"),
+    (dict(gF=None), 1, "grad_features is NULL"),
+])
+def test_backward_levels_validation(lib, kwargs, status, msg):
+    assert bwd_levels(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
 def test_empty_problems_return_ok_without_device_work(lib):
     # nothing to write: no launch happens, so these succeed on a host without a GPU
     assert fwd(lib, desc=(0, 6, 64, 16, 44), feat=None, K=None, R=None, t=None, out=None) == 0
@@ -101,6 +137,8 @@ def test_empty_problems_return_ok_without_device_work(lib):
     assert fwd(lib, desc=(1, 6, 0, 16, 44), out=None, counts=None) == 0
     assert bwd(lib, desc=(0, 6, 64, 16, 44), grad=None, gF=None, K=None, R=None, t=None) == 0
     assert bwd(lib, desc=(1, 6, 0, 16, 44), grad=None, gF=None) == 0
+    assert fwd_levels(lib, desc=(0, 6, 64, 32, 88), feat=None, out=None) == 0
+    assert fwd_levels(lib, L=1, ratios=(), X=0, out=None) == 0
 
 
 def test_binding_refuses_missing_library(tmp_path):
