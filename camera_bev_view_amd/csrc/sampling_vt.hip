@@ -611,6 +611,7 @@ struct BwdArgs {
   const float* grad;
   float* dF;
   int tiles_x, tiles_y;
+  int level;         // feature level this launch scatters (multi-level: one launch per level)
 };
 
 // Hash-table slot of pixel `pix` (inserted if absent), or -1 when the probe
@@ -701,10 +702,14 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
   int2* region = sRegion + wid * kBwdRegion;
   int2* pend = sPend + wid * kBwdPend;
-  const int nlev = ML ? p.L : 1;                  // feature levels (1 unless ML)
-  const LaneRole role = lane_role(lane, p.N, nlev);
+  // A multi-level backward runs one launch per level: every lane then works on
+  // that level (tap pass, merging and table as in a single-level launch), and a
+  // tap's weight carries the 1/L of the level mean.
+  const int nlev = 1;
+  const LaneRole role = lane_role(lane, p.N, 1);
   const int zpc = role.zpc, zl = role.zl, ln = role.ln;
-  const int vs = ML ? lane / nlev : lane, vl = lane - vs * nlev;  // phase-B lane role: (sample, level)
+  const int vs = lane, vl = ML ? a.level : 0;        // phase-B lane role: (sample, level)
+  const float lmean = ML ? (float)p.L : 1.0f;
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 0;
   Rec* raw = reinterpret_cast<Rec*>(sSorted) + wid * kBwdRegion;   // raw taps while listing (sorted area is free then)
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
         const double px = p.ox + ((double)(x_base + dx) + 0.5) * p.dx;
         const double py = p.oy + ((double)(y_base + dy) + 0.5) * p.dy;
         const double pz = p.oz + ((double)d.x + 0.5) * p.dz;
-        const Taps tp = tap_geometry<ML>(sP, n, px, py, pz, __builtin_amdgcn_rcpf((float)(cnt * nlev)), vl, p);
+        const Taps tp = tap_geometry<ML>(sP, n, px, py, pz, __builtin_amdgcn_rcpf((float)cnt * lmean), vl, p);
 #pragma unroll
         for (int t = 0; t < 4; ++t) raw[4 * lane + t] = Rec{tp.pix[t], tp.w[t]};
       }
@@ -800,7 +805,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
       {
         Rec m[4];
         bool top = false, bot = false;
-        if (lane < nvirt) merge_rows(raw, pend, vs, vl, nlev, pending, m, top, bot);
+        if (lane < nvirt) merge_rows(raw, pend, vs, 0, 1, pending, m, top, bot);
         const uint64_t mt = __ballot(top), mb = __ballot(bot);
         const int pos = used + 2 * (rank_below(mt) + rank_below(mb));
         nrec = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
@@ -1112,12 +1117,19 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int2) * kSlots +
                        sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
                        sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
-  if (p.L > 1)
-    hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
-  else
+  if (p.L == 1) {
+    a.level = 0;
     hipLaunchKernelGGL(sampling_vt_bwd<false>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream,
                        a);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
+  for (int l = 0; l < p.L; ++l) {
+    a.level = l;
+    hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fbev
