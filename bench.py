@@ -14,6 +14,10 @@ steps; per-pass figures (output elems/s, bilinear samples/s, algorithmic
 HBM GB/s) follow in ``forward`` / ``backward``; ``roofline`` covers the
 dominant kernel; ``cpu_baseline`` times the fp64 CPU oracle on the same
 workload (a reported baseline, not a target).
+
+``--workload`` selects another seeded workload: tiny, batched, large, fwdbwd
+(single-level), or pyramid (the multi-level path, fbev_forward_levels +
+fbev_backward_levels on 32x88 / 16x44 / 8x22 levels of a 6-camera rig).
 """
 from __future__ import annotations
 
@@ -42,18 +46,40 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic(kernel: str, algo_bytes: float):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
-    they were taken on a different kernel source (or never)."""
+    they were taken on a different kernel source or workload (or never)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k or rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash():
         return None
-    return k.get("bytes_per_launch")
+    k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
+    return k.get("bytes_per_launch") if k else None
+
+
+def cpu_baseline_levels(inp, rows):
+    """Time the multi-level fp64 oracle (forward + backward) on the first ``rows`` X-rows."""
+    import oracle.multilevel as ml
+    sel = list(range(rows))
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    ml.oracle_forward_levels(inp.levels, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, rows=sel)
+    ml.oracle_backward_levels(inp.grad_out, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z, inp.shapes, rows=sel)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    B, C = inp.levels[0].shape[0], inp.levels[0].shape[2]
+    return {
+        "value": B * C * rows * inp.Y / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy multi-level oracle, forward + backward over X-rows 0..{rows - 1} of {inp.X} "
+                  f"({B * C * rows * inp.Y} outputs), wall {wall:.2f} s, process CPU {cpu:.2f} s, "
+                  f"{len(os.sched_getaffinity(0))} cores available",
+    }
 
 
 def cpu_baseline(inp, rows):
@@ -103,29 +129,50 @@ def main():
     from camera_bev_view_amd import ops
     from camera_bev_view_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
-    inp = wl.make_inputs(args.workload, dtype=args.dtype, with_grad=True)
-    B, N, C, H, W = inp.F.shape
-    X, Y, Z = inp.X, inp.Y, inp.Z
     dev = torch.device("cuda:0")
-    Fcl = torch.from_numpy(np.ascontiguousarray(inp.F.transpose(0, 1, 3, 4, 2)))
-    if inp.dtype == "bf16":
-        Fcl = Fcl.to(torch.bfloat16)
-    Fcl = Fcl.to(dev)
-    K, R, t = (torch.from_numpy(a).to(dev) for a in (inp.K, inp.R, inp.t))
-    g = torch.from_numpy(inp.grad_out).to(dev)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    if args.workload in wl.PYRAMIDS:
+        # multi-level (feature-pyramid) path: packed level features [B,N,P,C]
+        inp = wl.make_level_inputs(args.workload, dtype=args.dtype, with_grad=True)
+        B, N, C = inp.levels[0].shape[:3]
+        H, W = inp.shapes[0]
+        nlev = len(inp.shapes)
+        lv = [torch.from_numpy(np.ascontiguousarray(F.transpose(0, 1, 3, 4, 2))) for F in inp.levels]
+        if inp.dtype == "bf16":
+            lv = [x.to(torch.bfloat16) for x in lv]
+        Fdev = ops.pack_levels([x.to(dev) for x in lv])
+        P = Fdev.shape[2]
+        desc = f"levels {'/'.join(f'{h}x{w}' for h, w in inp.shapes)}"
+        fwd_call = lambda **kw: ops.forward_levels(Fdev, inp.shapes, K, R, t, inp.rng6, X, Y, Z, **kw)
+        bwd_call = lambda: ops.backward_levels(g, B, N, C, inp.shapes, K, R, t, inp.rng6, X, Y, Z)
+        baseline = cpu_baseline_levels
+    else:
+        inp = wl.make_inputs(args.workload, dtype=args.dtype, with_grad=True)
+        B, N, C, H, W = inp.F.shape
+        nlev, P = 1, H * W
+        Fdev = torch.from_numpy(np.ascontiguousarray(inp.F.transpose(0, 1, 3, 4, 2)))
+        if inp.dtype == "bf16":
+            Fdev = Fdev.to(torch.bfloat16)
+        Fdev = Fdev.to(dev)
+        desc = f"HxW={H}x{W}"
+        fwd_call = lambda **kw: ops.forward(Fdev, K, R, t, inp.rng6, X, Y, Z, **kw)
+        bwd_call = lambda: ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+        baseline = cpu_baseline
+    X, Y, Z = inp.X, inp.Y, inp.Z
+    K, R, t = (to_dev(a) for a in (inp.K, inp.R, inp.t))
+    g = to_dev(inp.grad_out)
     out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
-    es = Fcl.element_size()
+    es = Fdev.element_size()
 
     # valid (cell, z, camera) samples, for the samples/s figures (outside the timed region)
-    _, cnt = ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, with_counts=True)
+    _, cnt = fwd_call(with_counts=True)
     torch.cuda.synchronize()
     valid_tuples = int(cnt.to(torch.int64).sum().item())
     del cnt
 
     def step():
-        ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, out=out)
-        return ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+        fwd_call(out=out)
+        return bwd_call()
 
     log(f"[bench] warmup {args.warmup} steps on {args.workload}")
     for _ in range(args.warmup):
@@ -152,9 +199,9 @@ def main():
     t_start.record(stream)
     for k in range(args.steps):
         ev[k][0].record(stream)
-        ops.forward(Fcl, K, R, t, inp.rng6, X, Y, Z, out=out)
+        fwd_call(out=out)
         ev[k][1].record(stream)
-        ops.backward(g, (B, N, H, W, C), K, R, t, inp.rng6, X, Y, Z)
+        bwd_call()
         ev[k][2].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -165,11 +212,11 @@ def main():
 
     out_elems = B * C * X * Y
     cam_bytes = B * N * 21 * 4
-    feat_bytes = B * N * H * W * C * es
+    feat_bytes = B * N * P * C * es
     fwd_bytes = feat_bytes + out_elems * 4 + cam_bytes            # features once, output once
-    bwd_bytes = out_elems * 4 + B * N * H * W * C * 4 + cam_bytes  # grad_out once, dL/dF once
-    samples = valid_tuples * C
-    logical = B * N * C * X * Y * Z
+    bwd_bytes = out_elems * 4 + B * N * P * C * 4 + cam_bytes      # grad_out once, dL/dF once
+    samples = valid_tuples * C * nlev                              # one bilinear sample per level
+    logical = B * N * C * X * Y * Z * nlev
 
     def rates(ms, nbytes):
         s = ms * 1e-3
@@ -183,7 +230,7 @@ def main():
         ("sampling_vt_bwd", bwd, bwd_bytes)
     achieved = dom["hbm_gbps_algorithmic"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, dom_bytes),
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
                 "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
 
     line = {
@@ -199,9 +246,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
         "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
-        "config": {"workload": f"{args.workload}: B={B} N={N} C={C} HxW={H}x{W} {inp.dtype} -> "
+        "config": {"workload": f"{args.workload}: B={B} N={N} C={C} {desc} {inp.dtype} -> "
                                f"X*Y*Z={X}x{Y}x{Z}, one step = forward + backward",
-                   "B": B, "N": N, "C": C, "H": H, "W": W, "X": X, "Y": Y, "Z": Z,
+                   "B": B, "N": N, "C": C, "H": H, "W": W, "levels": nlev, "X": X, "Y": Y, "Z": Z,
                    "valid_samples_per_pass": valid_tuples},
         "bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3),
         "forward": fwd,
@@ -210,7 +257,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows or X)
+        line["cpu_baseline"] = baseline(inp, args.cpu_rows or X)
     print(json.dumps(line), flush=True)
 
 

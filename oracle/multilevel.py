@@ -104,8 +104,9 @@ def oracle_forward_levels(levels: Sequence[np.ndarray], K: np.ndarray, R: np.nda
 
 def oracle_backward_levels(grad_out: np.ndarray, K: np.ndarray, R: np.ndarray, t: np.ndarray,
                            rng6: Sequence[float], X: int, Y: int, Z: int,
-                           shapes: Sequence[Sequence[int]]) -> List[np.ndarray]:
-    """Gradient w.r.t. each level's features, a list of [B,N,C,H_l,W_l] float64.
+                           shapes: Sequence[Sequence[int]], rows: Optional[Sequence[int]] = None) -> List[np.ndarray]:
+    """Gradient w.r.t. each level's features, a list of [B,N,C,H_l,W_l] float64
+    (only the cells of X-rows ``rows`` contribute when given).
 
     The adjoint of each stage in reverse order: the height sum broadcasts the
     gradient over z, the valid mean multiplies by mask / max(cnt, 1), the level
@@ -123,8 +124,9 @@ def oracle_backward_levels(grad_out: np.ndarray, K: np.ndarray, R: np.ndarray, t
     n_idx = np.arange(N).reshape(N, 1, 1, 1)
     for b in range(B):
         accs = [np.zeros((C, N * H * W), np.float64) for (H, W) in shapes]
-        for s in range(0, X, step):
-            r = np.arange(s, min(X, s + step))
+        all_rows = np.arange(X) if rows is None else np.asarray(rows, np.int64)
+        for s in range(0, len(all_rows), step):
+            r = all_rows[s:s + step]
             grid = voxel_grid(rng6, X, Y, Z, r)
             d, u, v = project(grid, K[b], R[b], t[b])
             mask = in_view_mask(d, u, v, H0, W0)
