@@ -132,3 +132,50 @@ def cell_value_levels(levels, K, R, t, rng6: Sequence[float], X: int, Y: int, Z:
                 s += lv / len(levels)
             acc[c] += s / len(seen)
     return acc, counts
+
+
+def _inv3(M):
+    """Inverse of a 3x3 matrix (nested lists) by cofactors."""
+    a, b, c = M[0]
+    d, e, f = M[1]
+    g, h, i = M[2]
+    co = [[e * i - f * h, -(d * i - f * g), d * h - e * g],
+          [-(b * i - c * h), a * i - c * g, -(a * h - b * g)],
+          [b * f - c * e, -(a * f - c * d), a * e - b * d]]
+    det = a * co[0][0] + b * co[0][1] + c * co[0][2]
+    return [[co[col][row] / det for col in range(3)] for row in range(3)]
+
+
+def lss_brute(depth, context, K, R, t, rng6: Sequence[float], X: int, Y: int, d_min: float, d_step: float):
+    """Lift-splat by scalar loops (Lift-Splat-Shoot tutorial, "Lift" and "Splat"): every
+    pixel's D points along its ray (bin k at camera depth d_min + k d_step), each carrying
+    depth[k] * context, moved to the ego frame and summed into its BEV cell.
+    depth[b][n][k][v][u], context[b][n][c][v][u]; returns out[b][c][i][j] as nested lists."""
+    B = len(depth)
+    N = len(depth[0])
+    D = len(depth[0][0])
+    H = len(depth[0][0][0])
+    W = len(depth[0][0][0][0])
+    C = len(context[0][0])
+    xmin, xmax, ymin, ymax = (float(r) for r in rng6[:4])
+    dx = (xmax - xmin) / X
+    dy = (ymax - ymin) / Y
+    out = [[[[0.0] * Y for _ in range(X)] for _ in range(C)] for _ in range(B)]
+    for b in range(B):
+        for n in range(N):
+            Ki = _inv3(K[b][n])
+            Rn, tn = R[b][n], t[b][n]
+            for v in range(H):
+                for u in range(W):
+                    ray = [Ki[r][0] * u + Ki[r][1] * v + Ki[r][2] for r in range(3)]
+                    for k in range(D):
+                        dep = d_min + k * d_step
+                        pc = [dep * ray[r] - tn[r] for r in range(3)]
+                        p = [Rn[0][r] * pc[0] + Rn[1][r] * pc[1] + Rn[2][r] * pc[2] for r in range(3)]
+                        i = math.floor((p[0] - xmin) / dx)
+                        j = math.floor((p[1] - ymin) / dy)
+                        if 0 <= i < X and 0 <= j < Y:
+                            a = depth[b][n][k][v][u]
+                            for c in range(C):
+                                out[b][c][i][j] += a * context[b][n][c][v][u]
+    return out
