@@ -16,8 +16,10 @@ dominant kernel; ``cpu_baseline`` times the fp64 CPU oracle on the same
 workload (a reported baseline, not a target).
 
 ``--workload`` selects another seeded workload: tiny, batched, large, fwdbwd
-(single-level), or pyramid (the multi-level path, fbev_forward_levels +
-fbev_backward_levels on 32x88 / 16x44 / 8x22 levels of a 6-camera rig).
+(single-level), pyramid (the multi-level path, fbev_forward_levels +
+fbev_backward_levels on 32x88 / 16x44 / 8x22 levels of a 6-camera rig), or
+lss / lss_batched (Lift-Splat, the push view transform: fbev_lss_forward +
+fbev_lss_backward with 41 depth bins and 64 context channels per pixel).
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "BEV output elems/s + bilinear samples/s; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "sampling_vt.hip")
+LSS_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "lift_splat.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -41,22 +44,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
-    they were taken on a different kernel source or workload (or never)."""
+    they were taken on a different kernel source or workload (or never).  Each
+    workload's record names the source file its counters were taken on."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash():
+    w = rec.get("workloads", {}).get(workload, {})
+    src = os.path.join(ROOT, w.get("source", os.path.relpath(KERNEL_SRC, ROOT)))
+    sha = w.get("source_sha256", rec.get("source_sha256"))
+    try:
+        if sha != kernel_source_hash(src):
+            return None
+    except OSError:
         return None
-    k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
+    k = w.get("kernels", {}).get(kernel)
     return k.get("bytes_per_launch") if k else None
 
 
@@ -106,6 +116,131 @@ def cpu_baseline(inp, rows):
     }
 
 
+def cpu_baseline_lss(inp, min_seconds=10.0):
+    """Time the fp64 Lift-Splat oracle (forward + backward) on whole steps, repeated for ``min_seconds``."""
+    import oracle.lift_splat as ls
+    reps = 0
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    while True:
+        ls.lss_forward(inp.depth, inp.context, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.d_min, inp.d_step)
+        ls.lss_backward(inp.grad_out, inp.depth, inp.context, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y,
+                        inp.d_min, inp.d_step)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds:
+            break
+    cpu = time.process_time() - c0
+    B, C = inp.context.shape[0], inp.context.shape[2]
+    return {
+        "value": reps * B * C * inp.X * inp.Y / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy Lift-Splat oracle, {reps} whole forward + backward steps of the workload, "
+                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def main_lss(args):
+    """Lift-Splat: one step = fbev_lss_forward + fbev_lss_backward on one batch."""
+    import numpy as np
+    import torch
+    from camera_bev_view_amd import ops
+    from camera_bev_view_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    inp = wl.make_lss_inputs(args.workload, with_grad=True)
+    B, N, D, H, W = inp.depth.shape
+    C = inp.context.shape[2]
+    X, Y = inp.X, inp.Y
+    dep = to_dev(inp.depth.transpose(0, 1, 3, 4, 2))
+    ctx = to_dev(inp.context.transpose(0, 1, 3, 4, 2))
+    K, R, t = (to_dev(a) for a in (inp.K, inp.R, inp.t))
+    g = to_dev(inp.grad_out)
+    out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
+    gd = torch.empty_like(dep)
+    gc = torch.empty_like(ctx)
+    geo = (inp.rng6, X, Y, inp.d_min, inp.d_step)
+    fwd_call = lambda: ops.lss_forward(dep, ctx, K, R, t, *geo, out=out)
+    bwd_call = lambda: ops.lss_backward(g, dep, ctx, K, R, t, *geo, grad_depth=gd, grad_context=gc)
+
+    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
+    for _ in range(args.warmup):
+        fwd_call()
+        bwd_call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd_call()
+        ev[k][1].record(stream)
+        bwd_call()
+        ev[k][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
+
+    out_elems = B * C * X * Y
+    pix = B * N * H * W
+    points = pix * D
+    cam_bytes = B * N * 21 * 4
+    fwd_bytes = pix * (D + C) * 4 + out_elems * 4 + cam_bytes            # alpha and c once, output once
+    bwd_bytes = out_elems * 4 + 2 * pix * (D + C) * 4 + cam_bytes         # grad_out, alpha and c once; both grads once
+
+    def rates(ms, nbytes):
+        s_ = ms * 1e-3
+        return {"ms": ms, "out_elems_per_s": out_elems / s_, "lifted_points_per_s": points / s_,
+                "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": nbytes / s_ / 1e9,
+                "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
+
+    fwd = rates(fwd_ms, fwd_bytes)
+    bwd = rates(bwd_ms, bwd_bytes)
+    dom_name, dom, dom_bytes = ("lift_splat_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        ("lift_splat_bwd", bwd, bwd_bytes)
+    achieved = dom["hbm_gbps_algorithmic"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
+                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+    line = {
+        "metric": METRIC,
+        "value": out_elems / (ms_step * 1e-3),
+        "unit": "BEV output elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded 6-camera ring rig, flat-Dirichlet depth distributions, N(0,1) context and "
+                "upstream gradient",
+        "config": {"workload": f"{args.workload}: Lift-Splat B={B} N={N} HxW={H}x{W} D={D} bins "
+                               f"{inp.d_min}+k*{inp.d_step} m, C={C} -> X*Y={X}x{Y} pillars, "
+                               f"one step = forward + backward",
+                   "B": B, "N": N, "C": C, "H": H, "W": W, "D": D, "X": X, "Y": Y},
+        "lifted_points_per_s": points * 2 / (ms_step * 1e-3),
+        "forward": fwd,
+        "backward": bwd,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline_lss(inp)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +264,8 @@ def main():
     from camera_bev_view_amd import ops
     from camera_bev_view_amd import workloads as wl
 
+    if args.workload in wl.LSS_WORKLOADS:
+        return main_lss(args)
     dev = torch.device("cuda:0")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if args.workload in wl.PYRAMIDS:

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflashbev.so")
-SOURCES = [os.path.join(CSRC, "flashbev_api.cpp"), os.path.join(CSRC, "sampling_vt.hip")]
+SOURCES = [os.path.join(CSRC, "flashbev_api.cpp"), os.path.join(CSRC, "sampling_vt.hip"),
+           os.path.join(CSRC, "lift_splat.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code.

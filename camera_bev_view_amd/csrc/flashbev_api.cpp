@@ -12,6 +12,7 @@
 
 #include "../../include/flashbev.h"
 #include "kernels.h"
+#include "lift_splat.h"
 
 namespace {
 
@@ -162,6 +163,97 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
                        "fbev_backward launch");
 }
 
+
+// Lift-Splat arguments: depth [B,N,H,W,D] and context [B,N,H,W,C], the depth
+// bins, the rig and the x-y extent of the BEV grid (its z fields are unused:
+// a cell is a pillar).  Fills the geometry and size fields of `a`.
+fbev_status check_lss(const fbev_feat_desc& fd, int32_t D, float d_min, float d_step, const float* K, const float* R,
+                      const float* t, const fbev_range& r, int32_t X, int32_t Y, fbev::LssArgs& a) {
+  if (fd.B < 0 || fd.N < 0 || fd.C < 0 || fd.H < 0 || fd.W < 0 || D < 0)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "negative size (B=%d N=%d C=%d H=%d W=%d D=%d)", fd.B, fd.N, fd.C, fd.H,
+                fd.W, D);
+  if (X < 0 || Y < 0) return fail(FBEV_ERR_INVALID_ARGUMENT, "negative grid size (X=%d Y=%d)", X, Y);
+  if (X > FBEV_MAX_GRID || Y > FBEV_MAX_GRID || D > FBEV_MAX_GRID)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "size above %d (X=%d Y=%d D=%d)", FBEV_MAX_GRID, X, Y, D);
+  if (fd.N > FBEV_MAX_CAMERAS)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "N=%d cameras exceeds FBEV_MAX_CAMERAS=%d", fd.N, FBEV_MAX_CAMERAS);
+  if (fd.H > FBEV_MAX_GRID || fd.W > FBEV_MAX_GRID)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "feature map %dx%d above %d", fd.H, fd.W, FBEV_MAX_GRID);
+  if (!finite_range(r.x_min, r.x_max) || !finite_range(r.y_min, r.y_max))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "the x and y BEV ranges need finite min < max");
+  if (!std::isfinite(d_min) || !std::isfinite(d_step) || !(d_step > 0.0f))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "depth bins need a finite d_min and a finite d_step > 0");
+  if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "K, R and t must be non-NULL when B*N > 0");
+  const int64_t pix = (int64_t)fd.N * fd.H * fd.W;
+  const int64_t widest = fd.C > D ? fd.C : D;
+  if (pix * widest >= (int64_t)1 << 31 || pix * 4 >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "one sample's depth or context spans %lld elements (limit 2^31 - 1)",
+                (long long)(pix * widest));
+  a.K = K;
+  a.R = R;
+  a.t = t;
+  a.B = fd.B;
+  a.N = fd.N;
+  a.H = fd.H;
+  a.W = fd.W;
+  a.C = fd.C;
+  a.D = D;
+  a.X = X;
+  a.Y = Y;
+  a.dmin = (double)d_min;
+  a.dstep = (double)d_step;
+  a.x_min = (double)r.x_min;
+  a.y_min = (double)r.y_min;
+  a.cdx = ((double)r.x_max - (double)r.x_min) / (X > 0 ? X : 1);
+  a.cdy = ((double)r.y_max - (double)r.y_min) / (Y > 0 ? Y : 1);
+  return FBEV_OK;
+}
+
+fbev_status lss_forward_impl(const float* depth, const float* context, fbev_feat_desc fd, int32_t D, float d_min,
+                             float d_step, const float* K, const float* R, const float* t, fbev_range bev_range,
+                             int32_t X, int32_t Y, float* out, void* stream) {
+  fbev::LssArgs a{};
+  fbev_status s = check_lss(fd, D, d_min, d_step, K, R, t, bev_range, X, Y, a);
+  if (s != FBEV_OK) return s;
+  const int64_t n_pix = (int64_t)fd.B * fd.N * fd.H * fd.W;
+  const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  if (n_out == 0) return FBEV_OK;
+  if (out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (n_pix * D > 0 && depth == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "depth is NULL");
+  if (n_pix * fd.C > 0 && context == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "context is NULL");
+  a.depth = depth;
+  a.ctx = context;
+  a.out = out;
+  return device_status(fbev::launch_lss_forward(a, static_cast<hipStream_t>(stream)), "fbev_lss_forward launch");
+}
+
+fbev_status lss_backward_impl(const float* grad_out, const float* depth, const float* context, fbev_feat_desc fd,
+                              int32_t D, float d_min, float d_step, const float* K, const float* R, const float* t,
+                              fbev_range bev_range, int32_t X, int32_t Y, float* grad_depth, float* grad_context,
+                              void* stream) {
+  fbev::LssArgs a{};
+  fbev_status s = check_lss(fd, D, d_min, d_step, K, R, t, bev_range, X, Y, a);
+  if (s != FBEV_OK) return s;
+  const int64_t n_pix = (int64_t)fd.B * fd.N * fd.H * fd.W;
+  const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  const bool want_d = n_pix * D > 0, want_c = n_pix * fd.C > 0;
+  if (!want_d && !want_c) return FBEV_OK;
+  if (want_d && grad_depth == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_depth is NULL");
+  if (want_c && grad_context == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_context is NULL");
+  // the gradient of one input needs the other one (the forward is bilinear in them)
+  if (n_out > 0 && want_d && want_c && (depth == nullptr || context == nullptr))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "depth and context must be non-NULL");
+  if (n_out > 0 && want_d && want_c && grad_out == nullptr)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  a.grad = grad_out;
+  a.depth = depth;
+  a.ctx = context;
+  a.gdep = want_d ? grad_depth : nullptr;
+  a.gctx = want_c ? grad_context : nullptr;
+  return device_status(fbev::launch_lss_backward(a, static_cast<hipStream_t>(stream)), "fbev_lss_backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +281,20 @@ fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32
                                  const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X,
                                  int32_t Y, int32_t Z, float* grad_features, void* stream) {
   return backward_impl(grad_out, fd, L, ratios, K, R, t, bev_range, X, Y, Z, grad_features, stream);
+}
+
+fbev_status fbev_lss_forward(const float* depth, const float* context, fbev_feat_desc fd, int32_t D, float d_min,
+                             float d_step, const float* K, const float* R, const float* t, fbev_range bev_range,
+                             int32_t X, int32_t Y, float* out, void* stream) {
+  return lss_forward_impl(depth, context, fd, D, d_min, d_step, K, R, t, bev_range, X, Y, out, stream);
+}
+
+fbev_status fbev_lss_backward(const float* grad_out, const float* depth, const float* context, fbev_feat_desc fd,
+                              int32_t D, float d_min, float d_step, const float* K, const float* R, const float* t,
+                              fbev_range bev_range, int32_t X, int32_t Y, float* grad_depth, float* grad_context,
+                              void* stream) {
+  return lss_backward_impl(grad_out, depth, context, fd, D, d_min, d_step, K, R, t, bev_range, X, Y, grad_depth,
+                           grad_context, stream);
 }
 
 const char* fbev_status_string(fbev_status s) {

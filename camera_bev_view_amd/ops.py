@@ -179,3 +179,66 @@ def backward_levels(grad_out: torch.Tensor, B: int, N: int, C: int, shapes: Sequ
                                         _lib.int32_array(ratios), _ptr(K), _ptr(R), _ptr(t),
                                         _lib.bev_range(bev_range), X, Y, Z, _ptr(gF), _stream(dev)))
     return gF
+
+
+# ---- Lift-Splat (the push view transform)
+
+def _check_lss_inputs(depth: torch.Tensor, context: torch.Tensor):
+    if depth.dim() != 5 or context.dim() != 5:
+        raise ValueError("depth must be [B,N,H,W,D] and context [B,N,H,W,C]")
+    if depth.shape[:4] != context.shape[:4]:
+        raise ValueError(f"depth {tuple(depth.shape)} and context {tuple(context.shape)} disagree on [B,N,H,W]")
+    for name, x in (("depth", depth), ("context", context)):
+        if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if depth.device != context.device:
+        raise ValueError("depth and context must be on the same device")
+
+
+def lss_forward(depth: torch.Tensor, context: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor,
+                bev_range: Sequence[float], X: int, Y: int, d_min: float, d_step: float, *,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fbev_lss_forward: depth alpha [B,N,H,W,D], context c [B,N,H,W,C] (fp32, channels-last);
+    bin k at camera depth d_min + k d_step.  Returns the pillar sums [B,C,X,Y] fp32."""
+    _check_lss_inputs(depth, context)
+    B, N, H, W, D = depth.shape
+    C = context.shape[-1]
+    dev = depth.device
+    _check_cams(K, R, t, B, N, dev)
+    if out is None:
+        out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    lib = _lib.load()
+    _lib.check(lib.fbev_lss_forward(_ptr(depth), _ptr(context), _lib.feat_desc(B, N, C, H, W), D, float(d_min),
+                                    float(d_step), _ptr(K), _ptr(R), _ptr(t), _lib.bev_range(bev_range), X, Y,
+                                    _ptr(out), _stream(dev)))
+    return out
+
+
+def lss_backward(grad_out: torch.Tensor, depth: torch.Tensor, context: torch.Tensor, K: torch.Tensor,
+                 R: torch.Tensor, t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, d_min: float,
+                 d_step: float, *, grad_depth: Optional[torch.Tensor] = None,
+                 grad_context: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fbev_lss_backward: (dL/ddepth [B,N,H,W,D], dL/dcontext [B,N,H,W,C]) from dL/dout [B,C,X,Y]."""
+    _check_lss_inputs(depth, context)
+    B, N, H, W, D = depth.shape
+    C = context.shape[-1]
+    dev = depth.device
+    _check_cams(K, R, t, B, N, dev)
+    if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32 or not grad_out.is_contiguous() \
+            or grad_out.device != dev:
+        raise ValueError(f"grad_out must be a contiguous float32 [{B},{C},{X},{Y}] tensor on {dev}")
+    if grad_depth is None:
+        grad_depth = torch.empty_like(depth)
+    if grad_context is None:
+        grad_context = torch.empty_like(context)
+    for name, g, ref in (("grad_depth", grad_depth, depth), ("grad_context", grad_context, context)):
+        if g.shape != ref.shape or g.dtype != torch.float32 or not g.is_contiguous() or g.device != dev:
+            raise ValueError(f"{name} must be a contiguous float32 tensor shaped like its input")
+    lib = _lib.load()
+    _lib.check(lib.fbev_lss_backward(_ptr(grad_out), _ptr(depth), _ptr(context), _lib.feat_desc(B, N, C, H, W), D,
+                                     float(d_min), float(d_step), _ptr(K), _ptr(R), _ptr(t),
+                                     _lib.bev_range(bev_range), X, Y, _ptr(grad_depth), _ptr(grad_context),
+                                     _stream(dev)))
+    return grad_depth, grad_context

@@ -110,11 +110,12 @@ def extrinsics_from_yaw(yaw_deg: float, radius: float = CAM_RADIUS_M, height: fl
 
 
 def make_rig(cid: int, B: int, N: int, H: int, W: int, per_sample: bool,
-             jitter: bool = True) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             jitter: bool = True, pitch_deg: float = 0.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Seeded ring rig: K [B,N,3,3], R [B,N,3,3], t [B,N,3], all fp32.
 
     Sample b draws its yaw jitter from ``default_rng([cid, b, 0])`` when
     ``per_sample`` is set; otherwise every sample reuses the b = 0 rig.
+    ``pitch_deg`` tilts every camera's optical axis upward by that angle.
     """
     K = np.empty((B, N, 3, 3), np.float32)
     R = np.empty((B, N, 3, 3), np.float32)
@@ -124,7 +125,7 @@ def make_rig(cid: int, B: int, N: int, H: int, W: int, per_sample: bool,
         g = np.random.default_rng([cid, b if per_sample else 0, 0])
         jit = g.uniform(-YAW_JITTER_DEG, YAW_JITTER_DEG, N) if jitter else np.zeros(N)
         for n in range(N):
-            Rn, tn = extrinsics_from_yaw(n * 360.0 / N + float(jit[n]))
+            Rn, tn = extrinsics_from_yaw(n * 360.0 / N + float(jit[n]), pitch_deg=pitch_deg)
             K[b, n], R[b, n], t[b, n] = Kn, Rn, tn
     return K, R, t
 
@@ -266,3 +267,66 @@ def random_level_case(seed: int, B: int, N: int, C: int, H: int, W: int, ratios,
     levels = make_level_features(2000 + seed, B, N, C, shapes, dtype)
     g = make_grad_out(2000 + seed, B, C, X, Y)
     return LevelInputs(levels, shapes, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y, Z, dtype, g)
+
+
+# ---- Lift-Splat (push view transform) inputs
+#
+# Sizes from the Lift-Splat-Shoot tutorial ("Lift" and "Splat"): six cameras,
+# an 8 x 22 feature map (a 128 x 352 image at stride 16), C = 64 context
+# channels, D = 41 depth bins over [4, 45) m at 1 m, and a 200 x 200 BEV grid
+# of 0.5 m cells over +-50 m.  The batched workload doubles the map (a 256 x
+# 704 image at stride 16) at batch 4 for throughput.  The depth distribution
+# of each pixel is a draw from a flat Dirichlet (a point on the probability
+# simplex, like the softmax output it stands for); the context is N(0, 1).
+
+LSS_WORKLOADS: Dict[str, dict] = {
+    "lss": dict(cid=6, B=1, N=6, C=64, H=8, W=22, D=41, d_min=4.0, d_step=1.0, X=200, Y=200, rng6=_R50,
+                per_sample=False),
+    "lss_batched": dict(cid=7, B=4, N=6, C=64, H=16, W=44, D=41, d_min=4.0, d_step=1.0, X=200, Y=200, rng6=_R50,
+                        per_sample=True),
+}
+
+
+def make_depth_dist(cid: int, B: int, N: int, D: int, H: int, W: int) -> np.ndarray:
+    """Logical depth distributions [B,N,D,H,W] fp32 from ``default_rng([cid, 3])`` (flat Dirichlet per pixel)."""
+    g = np.random.default_rng([cid, 3])
+    a = g.dirichlet(np.ones(max(D, 1)), size=(B, N, H, W))[..., :D] if D > 0 else np.zeros((B, N, H, W, 0))
+    return np.ascontiguousarray(a.astype(np.float32).transpose(0, 1, 4, 2, 3))
+
+
+@dataclasses.dataclass
+class LssInputs:
+    depth: np.ndarray        # logical [B,N,D,H,W] fp32
+    context: np.ndarray      # logical [B,N,C,H,W] fp32
+    K: np.ndarray
+    R: np.ndarray
+    t: np.ndarray
+    rng6: Tuple[float, ...]
+    X: int
+    Y: int
+    d_min: float
+    d_step: float
+    grad_out: Optional[np.ndarray] = None
+
+
+def make_lss_inputs(name: str = "lss", with_grad: bool = False, **override) -> LssInputs:
+    """Inputs for a named Lift-Splat workload; keyword overrides replace its sizes (same seeds)."""
+    w = dict(LSS_WORKLOADS[name], **override)
+    K, R, t = make_rig(w["cid"], w["B"], w["N"], w["H"], w["W"], w["per_sample"])
+    depth = make_depth_dist(w["cid"], w["B"], w["N"], w["D"], w["H"], w["W"])
+    ctx = make_features(w["cid"], w["B"], w["N"], w["C"], w["H"], w["W"])
+    g = make_grad_out(w["cid"], w["B"], w["C"], w["X"], w["Y"]) if with_grad else None
+    return LssInputs(depth, ctx, K, R, t, tuple(float(np.float32(r)) for r in w["rng6"]), w["X"], w["Y"],
+                     float(np.float32(w["d_min"])), float(np.float32(w["d_step"])), g)
+
+
+def random_lss_case(seed: int, B: int, N: int, C: int, H: int, W: int, D: int, X: int, Y: int,
+                    rng6=(-50.0, 50.0, -50.0, 50.0, -5.0, 3.0), d_min: float = 4.0, d_step: float = 1.0,
+                    pitch_deg: float = 0.0) -> LssInputs:
+    """An arbitrary-size seeded Lift-Splat case (ragged / edge-case parity runs)."""
+    K, R, t = make_rig(3000 + seed, B, N, H, W, True, pitch_deg=pitch_deg)
+    depth = make_depth_dist(3000 + seed, B, N, D, H, W)
+    ctx = make_features(3000 + seed, B, N, C, H, W)
+    g = make_grad_out(3000 + seed, B, C, X, Y)
+    return LssInputs(depth, ctx, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y,
+                     float(np.float32(d_min)), float(np.float32(d_step)), g)

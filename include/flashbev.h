@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 2
+#define FBEV_ABI_VERSION 3
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
@@ -151,6 +151,64 @@ fbev_status fbev_forward_levels(const void* features, fbev_dtype dtype, fbev_fea
 fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios,
                                  const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X,
                                  int32_t Y, int32_t Z, float* grad_features, void* stream);
+
+/*
+ * Lift-Splat, the push view transform (Lift-Splat-Shoot tutorial, sections
+ * "Lift" and "Splat").  Every feature-map pixel (n, v, u) carries a depth
+ * distribution alpha over D bins and a context vector c of C channels; bin k
+ * puts the point alpha_k * c on the pixel's ray at camera depth
+ * d_k = d_min + k * d_step (the tutorial's nuScenes setting: [4, 45) at 1 m,
+ * 41 bins at 4, 5, ..., 44).  The point moves to the ego frame,
+ *   p = R_n^T (d_k K_n^-1 [u, v, 1]^T - t_n)     ((R, t) maps ego to camera),
+ * and lands in BEV cell (i, j) = (floor((p_x - x_min) / dx), floor((p_y - y_min) / dy)),
+ * dx = (x_max - x_min) / X, dy = (y_max - y_min) / Y, when 0 <= i < X and
+ * 0 <= j < Y; there is no bound on p_z (each cell is a pillar) and
+ * bev_range.z_min / z_max are not used.  Each cell sums its points:
+ *
+ *   out[b, c, i, j] = sum over (n, k, v, u) whose point lands in (i, j) of alpha[b,n,v,u,k] * ctx[b,n,v,u,c]
+ *
+ * The geometry and the cell index are evaluated in double precision; the
+ * products and sums are fp32.  A point within rounding of a cell edge lands in
+ * one of the two cells, never in both or neither.  No point, cell index or
+ * sorted order is stored in device memory.
+ *
+ *   depth    : alpha, [B, N, H, W, D] fp32, device, read only (any values; a
+ *              softmax output in the tutorial's network).
+ *   context  : c, [B, N, H, W, C] fp32 (channels-last), device, read only.
+ *   fd       : B, N, C (context channels), H, W of the feature map.
+ *   D, d_min, d_step : the depth bins, 0 <= D <= FBEV_MAX_GRID, d_step > 0.
+ *   K, R, t  : as for fbev_forward (K in feature-map pixels).
+ *   out      : [B, C, X, Y] fp32, device, fully overwritten (zero where no
+ *              point lands).  Deterministic.
+ * Errors as for fbev_forward; FBEV_ERR_UNSUPPORTED when one sample's depth or
+ * context has 2^31 elements or more.
+ */
+fbev_status fbev_lss_forward(const float* depth, const float* context, fbev_feat_desc fd, int32_t D, float d_min,
+                             float d_step, const float* K, const float* R, const float* t, fbev_range bev_range,
+                             int32_t X, int32_t Y, float* out, void* stream);
+
+/*
+ * Gradients of fbev_lss_forward.  With the geometry fixed the forward is
+ * bilinear in (alpha, c) (tutorial, "Lift": the point features are the outer
+ * product of the two), so for the point of bin k of pixel q landing in cell s:
+ *
+ *   grad_depth[b, q, k]   = <ctx[b, q, :], grad_out[b, :, s]>     (0 for points outside the grid)
+ *   grad_context[b, q, c] = sum over q's landing points of alpha[b, q, k] * grad_out[b, c, s]
+ *
+ *   grad_out     : [B, C, X, Y] fp32, device, read only.
+ *   depth, context : the forward's inputs (read only).
+ *   grad_depth   : [B, N, H, W, D] fp32, device, fully overwritten.
+ *   grad_context : [B, N, H, W, C] fp32, device, fully overwritten.
+ * Both outputs are zeroed on `stream` and then accumulated with fp32 atomics:
+ * grad_depth is deterministic for C <= 64 (one add per element), grad_context
+ * sums one add per (pixel, 4 x 8 cell tile) in run-dependent order.  Pointers
+ * whose buffer has no elements may be NULL.  Other arguments and errors as
+ * for fbev_lss_forward.
+ */
+fbev_status fbev_lss_backward(const float* grad_out, const float* depth, const float* context, fbev_feat_desc fd,
+                              int32_t D, float d_min, float d_step, const float* K, const float* R, const float* t,
+                              fbev_range bev_range, int32_t X, int32_t Y, float* grad_depth, float* grad_context,
+                              void* stream);
 
 /* Static text for a status code. */
 const char* fbev_status_string(fbev_status s);

@@ -149,3 +149,65 @@ def test_binding_refuses_missing_library(tmp_path):
             _lib.load(str(tmp_path / "missing.so"))
         finally:
             _lib._lib = _lib._lib_saved
+
+
+def lss_fwd(lib, depth=FAKE, ctx=FAKE, desc=(1, 6, 64, 8, 22), D=41, d_min=4.0, d_step=1.0, K=FAKE, R=FAKE, t=FAKE,
+            rng=RNG, X=8, Y=8, out=FAKE):
+    return lib.fbev_lss_forward(depth, ctx, _lib.feat_desc(*desc), D, d_min, d_step, K, R, t, _lib.bev_range(rng), X, Y,
+                                out, None)
+
+
+def lss_bwd(lib, grad=FAKE, depth=FAKE, ctx=FAKE, desc=(1, 6, 64, 8, 22), D=41, d_min=4.0, d_step=1.0, rng=RNG,
+            X=8, Y=8, gd=FAKE, gc=FAKE, K=FAKE):
+    return lib.fbev_lss_backward(grad, depth, ctx, _lib.feat_desc(*desc), D, d_min, d_step, K, FAKE, FAKE,
+                                 _lib.bev_range(rng), X, Y, gd, gc, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(desc=(1, 6, -64, 8, 22)), 1, "negative size"),
+    (dict(D=-1), 1, "negative size"),
+    (dict(X=-2), 1, "negative grid size"),
+    (dict(D=70000), 1, "size above"),
+    (dict(desc=(1, 65, 64, 8, 22)), 1, "exceeds FBEV_MAX_CAMERAS"),
+    (dict(rng=(10.0, -10.0, -50.0, 50.0, -5.0, 3.0)), 1, "x and y BEV ranges"),
+    (dict(d_step=0.0), 1, "d_step > 0"),
+    (dict(d_step=-1.0), 1, "d_step > 0"),
+    (dict(d_min=float("nan")), 1, "finite d_min"),
+    (dict(K=None), 1, "K, R and t"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(depth=None), 1, "depth is NULL"),
+    (dict(ctx=None), 1, "context is NULL"),
+    (dict(desc=(1, 64, 4096, 128, 128)), 2, "limit 2^31"),
+])
+def test_lss_forward_validation(lib, kwargs, status, msg):
+    assert lss_fwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+def test_lss_forward_ignores_the_z_range(lib):
+    # the z fields of the range are unused (pillars): an empty z interval is not an error; the call
+    # then fails only at the NULL check that follows
+    assert lss_fwd(lib, rng=(-50.0, 50.0, -50.0, 50.0, 3.0, -5.0), out=None) == 1
+    assert "out is NULL" in lib.fbev_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(D=-3), 1, "negative size"),
+    (dict(d_step=float("inf")), 1, "d_step > 0"),
+    (dict(gd=None), 1, "grad_depth is NULL"),
+    (dict(gc=None), 1, "grad_context is NULL"),
+    (dict(depth=None), 1, "depth and context"),
+    (dict(grad=None), 1, "grad_out is NULL"),
+    (dict(desc=(1, 64, 1024, 256, 256)), 2, "limit 2^31"),
+])
+def test_lss_backward_validation(lib, kwargs, status, msg):
+    assert lss_bwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+def test_lss_empty_problems_return_ok_without_device_work(lib):
+    assert lss_fwd(lib, desc=(0, 6, 64, 8, 22), depth=None, ctx=None, K=None, R=None, t=None, out=None) == 0
+    assert lss_fwd(lib, Y=0, out=None) == 0
+    assert lss_fwd(lib, desc=(1, 6, 0, 8, 22), out=None) == 0
+    assert lss_bwd(lib, desc=(0, 6, 64, 8, 22), grad=None, depth=None, ctx=None, gd=None, gc=None, K=None) == 0
+    assert lss_bwd(lib, desc=(1, 6, 64, 0, 22), grad=None, depth=None, ctx=None, gd=None, gc=None) == 0
