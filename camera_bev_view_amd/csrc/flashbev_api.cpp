@@ -185,6 +185,11 @@ fbev_status check_lss(const fbev_feat_desc& fd, int32_t D, float d_min, float d_
     return fail(FBEV_ERR_INVALID_ARGUMENT, "depth bins need a finite d_min and a finite d_step > 0");
   if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
     return fail(FBEV_ERR_INVALID_ARGUMENT, "K, R and t must be non-NULL when B*N > 0");
+  // the kernels find candidate bins in fp32: bin indices must stay far inside its precision
+  const double span = (std::fabs((double)d_min) + std::fabs((double)d_min + (double)D * d_step)) / d_step;
+  if (span >= (double)(1 << 20))
+    return fail(FBEV_ERR_UNSUPPORTED, "depth bins of %g m at up to %g m: more than 2^20 steps from depth 0",
+                (double)d_step, std::fabs((double)d_min) + (double)D * d_step);
   const int64_t pix = (int64_t)fd.N * fd.H * fd.W;
   const int64_t widest = fd.C > D ? fd.C : D;
   if (pix * widest >= (int64_t)1 << 31 || pix * 4 >= (int64_t)1 << 31)

@@ -23,6 +23,8 @@ struct LssArgs {
   double x_min, y_min, cdx, cdy;   // cell (i, j) covers [x_min + i cdx, +cdx) x [y_min + j cdy, +cdy)
   // set by the launcher
   int tiles_x, tiles_y, c_lo, Cg;
+  double inv_cdx, inv_cdy;
+  float f_dlo, f_dhi, f_dmin, f_inv_dstep, f_slack;   // fp32 constants of the candidate test
 };
 
 hipError_t launch_lss_forward(LssArgs a, hipStream_t stream);
