@@ -70,6 +70,22 @@ def measured_traffic(kernel: str, workload: str):
     return k.get("bytes_per_launch") if k else None
 
 
+def calibration_copy(args, dev):
+    """A plain copy of --calib-copy-mib MiB, three times, for scaling the HBM byte counters."""
+    if not args.calib_copy_mib:
+        return
+    import torch
+    n = args.calib_copy_mib * (1 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    # an elementwise kernel (a plain device-to-device copy_ may go to a DMA engine,
+    # which the shader counters do not see): reads and writes n floats once
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done (x3)")
+
+
 def cpu_baseline_levels(inp, rows):
     """Time the multi-level fp64 oracle (forward + backward) on the first ``rows`` X-rows."""
     import oracle.multilevel as ml
@@ -171,6 +187,7 @@ def main_lss(args):
         fwd_call()
         bwd_call()
     torch.cuda.synchronize()
+    calibration_copy(args, dev)
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -316,16 +333,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.randn(n, device=dev)
-        dst = torch.empty_like(src)
-        # an elementwise kernel (a plain device-to-device copy_ may go to a DMA engine,
-        # which the shader counters do not see): reads and writes n floats once
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done (x3)")
+    calibration_copy(args, dev)
 
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
