@@ -179,3 +179,29 @@ def lss_brute(depth, context, K, R, t, rng6: Sequence[float], X: int, Y: int, d_
                             for c in range(C):
                                 out[b][c][i][j] += a * context[b][n][c][v][u]
     return out
+
+
+def deform_brute(F, K, R, t, anchors, offsets, weights, b: int, q: int) -> List[float]:
+    """Deformable Aggregation output out[b, q, :] by explicit loops (SparseDriveV2
+    notes, "Deformable Aggregation", steps 1-3): keypoint = anchor + offset, each
+    camera's projection, depth > 0 and the closed pixel-centre box, bilinear
+    value times the (query, camera, keypoint) weight, summed.
+
+    F is indexable as F[b][n][c][y][x]; anchors [b][q][3]; offsets [b][q][k][3];
+    weights [b][q][n][k].
+    """
+    N = len(F[b])
+    C = len(F[b][0])
+    H = len(F[b][0][0])
+    W = len(F[b][0][0][0])
+    acc = [0.0] * C
+    for k in range(len(offsets[b][q])):
+        p = [anchors[b][q][r] + offsets[b][q][k][r] for r in range(3)]
+        for n in range(N):
+            d, u, v = _to_pixel(K[b][n], R[b][n], t[b][n], p)
+            if not (d > 0.0 and 0.0 <= u <= W - 1 and 0.0 <= v <= H - 1):
+                continue
+            w = weights[b][q][n][k]
+            for c in range(C):
+                acc[c] += w * _sample(F[b][n][c], H, W, u, v)
+    return acc
