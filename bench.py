@@ -19,7 +19,10 @@ workload (a reported baseline, not a target).
 (single-level), pyramid (the multi-level path, fbev_forward_levels +
 fbev_backward_levels on 32x88 / 16x44 / 8x22 levels of a 6-camera rig), or
 lss / lss_batched (Lift-Splat, the push view transform: fbev_lss_forward +
-fbev_lss_backward with 41 depth bins and 64 context channels per pixel).
+fbev_lss_backward with 41 depth bins and 64 context channels per pixel), or
+deform / deform_bev (Deformable Aggregation: fbev_deform_forward +
+fbev_deform_backward for 900 sparse queries x 13 keypoints, or one query per
+cell of a 200 x 200 grid x 8 keypoints).
 """
 from __future__ import annotations
 
@@ -37,6 +40,7 @@ METRIC = "BEV output elems/s + bilinear samples/s; achieved HBM GB/s vs MI355X p
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "sampling_vt.hip")
 LSS_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "lift_splat.hip")
+DEFORM_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "deform_agg.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -258,6 +262,135 @@ def main_lss(args):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_deform(inp, max_queries, min_seconds=10.0):
+    """Time the fp64 Deformable Aggregation oracle (forward + backward) on the first ``max_queries``
+    queries, repeated until ``min_seconds`` have passed."""
+    import oracle.deform_agg as da
+    Qs = min(max_queries, inp.anchors.shape[1])
+    sl = (slice(None), slice(0, Qs))
+    args = (inp.F, inp.K, inp.R, inp.t, inp.anchors[sl], inp.offsets[sl], inp.weights[sl])
+    reps = 0
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    while True:
+        da.deform_forward(*args)
+        da.deform_backward(inp.grad_out[sl], *args)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds:
+            break
+    cpu = time.process_time() - c0
+    B, C = inp.F.shape[0], inp.F.shape[2]
+    return {
+        "value": reps * B * Qs * C / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy Deformable Aggregation oracle, {reps} forward + backward passes over queries "
+                  f"0..{Qs - 1} of {inp.anchors.shape[1]} (output elements = queries x channels), wall {wall:.2f} s, "
+                  f"process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def main_deform(args):
+    """Deformable Aggregation: one step = fbev_deform_forward + fbev_deform_backward on one batch."""
+    import numpy as np
+    import torch
+    from camera_bev_view_amd import ops
+    from camera_bev_view_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    inp = wl.make_deform_inputs(args.workload, with_grad=True)
+    B, N, C, H, W = inp.F.shape
+    Q, Kp = inp.offsets.shape[1:3]
+    F = to_dev(inp.F.transpose(0, 1, 3, 4, 2))
+    K, R, t = (to_dev(a) for a in (inp.K, inp.R, inp.t))
+    A, D, Wt = to_dev(inp.anchors), to_dev(inp.offsets), to_dev(inp.weights)
+    g = to_dev(inp.grad_out)
+    out = torch.empty((B, Q, C), dtype=torch.float32, device=dev)
+    fwd_call = lambda: ops.deform_forward(F, K, R, t, A, D, Wt, out=out)
+    bwd_call = lambda: ops.deform_backward(g, F, K, R, t, A, D, Wt)
+
+    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
+    for _ in range(args.warmup):
+        fwd_call()
+        bwd_call()
+    torch.cuda.synchronize()
+    calibration_copy(args, dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd_call()
+        ev[k][1].record(stream)
+        bwd_call()
+        ev[k][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
+
+    import oracle.deform_agg as da    # counts in-view samples for the samples/s figure (outside the timed region)
+    sub = slice(0, min(Q, 4000))
+    ref = da.deform_forward(inp.F, inp.K, inp.R, inp.t, inp.anchors[:, sub], inp.offsets[:, sub],
+                            inp.weights[:, sub])
+    in_view = float(ref["valid"].sum()) * Q / ref["valid"].shape[2]
+    out_elems = B * Q * C
+    feat_bytes = B * N * H * W * C * 4
+    q_bytes = B * Q * (3 + 3 * Kp + N * Kp) * 4
+    fwd_bytes = feat_bytes + q_bytes + out_elems * 4 + B * N * 21 * 4
+    bwd_bytes = out_elems * 4 + 2 * feat_bytes + 2 * q_bytes + B * N * 21 * 4
+
+    def rates(ms, nbytes):
+        s_ = ms * 1e-3
+        return {"ms": ms, "out_elems_per_s": out_elems / s_, "bilinear_samples_per_s": in_view * C / s_,
+                "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": nbytes / s_ / 1e9,
+                "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
+
+    fwd = rates(fwd_ms, fwd_bytes)
+    bwd = rates(bwd_ms, bwd_bytes)
+    dom_name, dom, dom_bytes = ("deform_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else ("deform_bwd", bwd, bwd_bytes)
+    achieved = dom["hbm_gbps_algorithmic"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
+                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+    line = {
+        "metric": METRIC,
+        "value": out_elems / (ms_step * 1e-3),
+        "unit": "BEV output elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient, seeded anchors and "
+                "offsets, flat-Dirichlet weights",
+        "config": {"workload": f"{args.workload}: Deformable Aggregation B={B} N={N} C={C} HxW={H}x{W} Q={Q} "
+                               f"queries x Kp={Kp} keypoints (outputs = query features), one step = forward + backward",
+                   "B": B, "N": N, "C": C, "H": H, "W": W, "Q": Q, "Kp": Kp,
+                   "in_view_samples_per_pass": int(round(in_view))},
+        "bilinear_samples_per_s": in_view * C * 2 / (ms_step * 1e-3),
+        "forward": fwd,
+        "backward": bwd,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline_deform(inp, 4000)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +416,8 @@ def main():
 
     if args.workload in wl.LSS_WORKLOADS:
         return main_lss(args)
+    if args.workload in wl.DEFORM_WORKLOADS:
+        return main_deform(args)
     dev = torch.device("cuda:0")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if args.workload in wl.PYRAMIDS:

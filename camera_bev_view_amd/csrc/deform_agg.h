@@ -1,0 +1,32 @@
+// Internal interface between the C-ABI host layer and the Deformable
+// Aggregation kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fbev {
+
+// One problem, validated by the host layer.  Query q of sample b has anchor
+// anchors[b,q,:], keypoint offsets offsets[b,q,k,:] and weights
+// weights[b,q,n,k]; features are channels-last [B,N,H,W,C] fp32.
+struct DeformArgs {
+  const float* feat;
+  const float* K;          // [B,N,3,3]
+  const float* R;          // [B,N,3,3]
+  const float* t;          // [B,N,3]
+  const float* anchors;    // [B,Q,3]
+  const float* offsets;    // [B,Q,Kp,3]
+  const float* weights;    // [B,Q,N,Kp]
+  const float* grad;       // backward: dL/dout [B,Q,C]
+  float* out;              // forward: [B,Q,C]
+  float* gfeat;            // backward: [B,N,H,W,C]
+  float* gweights;         // backward: [B,Q,N,Kp]
+  float* goffsets;         // backward: [B,Q,Kp,3]
+  float* ganchors;         // backward: [B,Q,3] or NULL
+  int B, N, C, H, W, Q, Kp;
+};
+
+hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream);
+hipError_t launch_deform_backward(const DeformArgs& a, hipStream_t stream);
+
+}  // namespace fbev

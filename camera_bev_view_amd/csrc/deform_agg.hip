@@ -1,0 +1,380 @@
+// Deformable Aggregation for gfx950: multi-camera deformable sampling fused
+// into one kernel per direction.
+//
+// The operator is the one the SparseDriveV2 notes describe ("Deformable
+// Aggregation", steps 1-3), which the FlashBEV notes carry over to BEVFormer's
+// spatial cross-attention: query q has a 3D anchor a_q and K keypoint offsets;
+// keypoint p = a_q + offset is projected into every camera
+// ([u, v, 1]^T ~ K_i (R_i p + t_i)); where it is in view (depth > 0, inside
+// the closed box of pixel centres) the camera's feature map is sampled
+// bilinearly and weighted by the query's weight for (camera, keypoint); the
+// query's output is the sum.  Nothing per (query, keypoint, camera) reaches
+// device memory.
+//
+// Forward: a wave owns a query at a time.  Phase A takes one (camera,
+// keypoint) pair per lane: fp64 projection, sign tests for the in-view rule,
+// then the four taps and their weights (bilinear x attention) for the pairs
+// in view, compacted into a per-wave LDS list of tap records.  Phase C
+// gathers with lanes = channels: each record is one coalesced row of the
+// channels-last map, up to 8 in flight, accumulated in fp32; the query's row
+// of [B, Q, C] leaves coalesced.
+//
+// Backward: the same phase A lists the in-view samples with their fractions
+// and depths.  Per sample, lanes = channels load the four taps once and give
+// (i) the feature gradient, one 64-lane atomic per tap, (ii) dL/dw = <sample,
+// g> and (iii) dL/du, dL/dv = w <dsample/du, g>, w <dsample/dv, g>, three wave
+// reductions; the keypoint gradient is then dL/du du/dp + dL/dv dv/dp with
+// du/dp = (P_1 - u P_3) / h_3 (rows of the 3x3 part of P = K [R | t]),
+// summed over cameras per keypoint in LDS.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "deform_agg.h"
+
+namespace fbev {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kBlock = kWave * kWaves;
+constexpr int kQPW = 4;                   // queries per wave
+constexpr int kQPB = kQPW * kWaves;       // queries per workgroup
+constexpr int kUnroll = 8;                // tap rows in flight per lane
+constexpr int kBlockC = 4 * kWave;        // channels a wave accumulates per pass over the samples
+
+struct TapRec {
+  int off;      // element offset of the tap's channel row within the batch sample
+  float w;      // bilinear weight x attention weight
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 1/x in double: hardware estimate and two Newton steps.
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
+}
+
+// P = K [R | t] in fp64 for the N cameras of batch sample b, 12 doubles each
+// (row-major 3 x 4), one camera per thread.
+__device__ void stage_projections(double* sP, const float* K, const float* R, const float* t, int b, int N) {
+  for (int n = threadIdx.x; n < N; n += kBlock) {
+    const size_t bn = (size_t)b * N + n;
+    double k[9], r[9], tt[3];
+    for (int i = 0; i < 9; ++i) {
+      k[i] = (double)K[bn * 9 + i];
+      r[i] = (double)R[bn * 9 + i];
+    }
+    for (int i = 0; i < 3; ++i) tt[i] = (double)t[bn * 3 + i];
+    double* P = sP + n * 12;
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 3; ++j) {
+        double s = 0.0;
+        for (int m = 0; m < 3; ++m) s = fma(k[i * 3 + m], r[m * 3 + j], s);
+        P[i * 4 + j] = s;
+      }
+      double s = 0.0;
+      for (int m = 0; m < 3; ++m) s = fma(k[i * 3 + m], tt[m], s);
+      P[i * 4 + 3] = s;
+    }
+  }
+}
+
+// One (camera, keypoint) pair of a query: h = P [p; 1] and the in-view rule
+// by sign tests (depth h_3 > 0 and 0 <= h_1 <= (W-1) h_3, 0 <= h_2 <= (H-1) h_3).
+struct Proj {
+  double h0, h1, h2;
+  bool valid;
+};
+
+__device__ __forceinline__ Proj project_pair(const double* P, double px, double py, double pz, int H, int W) {
+  Proj r;
+  r.h0 = fma(P[0], px, fma(P[1], py, fma(P[2], pz, P[3])));
+  r.h1 = fma(P[4], px, fma(P[5], py, fma(P[6], pz, P[7])));
+  r.h2 = fma(P[8], px, fma(P[9], py, fma(P[10], pz, P[11])));
+  r.valid = (r.h2 > 0.0) && (r.h0 >= 0.0) && (fma((double)(W - 1), r.h2, -r.h0) >= 0.0) && (r.h1 >= 0.0) &&
+            (fma((double)(H - 1), r.h2, -r.h1) >= 0.0);
+  return r;
+}
+
+// Taps of an in-view sample: x0 = floor(u), x1 = min(x0 + 1, W - 1) (the clamped
+// tap has weight 0), likewise rows; fractions a = u - x0, b = v - y0.
+struct Taps {
+  int p00, dx, dy;   // element offset of tap (y0, x0); steps to x1 and y1 (0 when clamped)
+  float a, b;
+  double u, v;
+};
+
+__device__ __forceinline__ Taps taps_of(const Proj& pr, int n, int H, int W, int C, size_t HWC) {
+  Taps t;
+  const double r = recip(pr.h2);
+  t.u = pr.h0 * r;
+  t.v = pr.h1 * r;
+  const double fu = fmin(fmax(floor(t.u), 0.0), (double)(W - 1));
+  const double fv = fmin(fmax(floor(t.v), 0.0), (double)(H - 1));
+  const int x0 = (int)fu, y0 = (int)fv;
+  t.a = (float)(t.u - fu);
+  t.b = (float)(t.v - fv);
+  t.p00 = (int)((size_t)n * HWC + ((size_t)y0 * W + x0) * C);
+  t.dx = (x0 + 1 < W) ? C : 0;
+  t.dy = (y0 + 1 < H) ? W * C : 0;
+  return t;
+}
+
+__global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  double* sP = reinterpret_cast<double*>(smem);                                   // [N][12]
+  TapRec* sRec = reinterpret_cast<TapRec*>(smem + sizeof(double) * 12 * a.N);     // [kWaves][4 * kWave]
+  const int b = blockIdx.y;
+  stage_projections(sP, a.K, a.R, a.t, b, a.N);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  TapRec* rec = sRec + wid * 4 * kWave;
+  const int NK = a.N * a.Kp;
+  const size_t HWC = (size_t)a.H * a.W * a.C;
+  const float* fb = a.feat + (size_t)b * a.N * HWC;
+
+  for (int i = 0; i < kQPW; ++i) {
+    const int q = blockIdx.x * kQPB + i * kWaves + wid;
+    if (q >= a.Q) break;
+    const size_t bq = (size_t)b * a.Q + q;
+    const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
+    for (int c0 = 0; c0 < a.C; c0 += kBlockC) {
+      float acc[kBlockC / kWave];
+#pragma unroll
+      for (int g = 0; g < kBlockC / kWave; ++g) acc[g] = 0.f;
+      for (int base = 0; base < NK; base += kWave) {
+        // ---- phase A: pair idx = n * Kp + k on this lane
+        const int idx = base + lane;
+        bool valid = false;
+        Taps tp;
+        float wq = 0.f;
+        if (idx < NK) {
+          const int n = idx / a.Kp, k = idx - n * a.Kp;
+          const float* o = a.offsets + (bq * a.Kp + k) * 3;
+          const Proj pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
+          valid = pr.valid;
+          if (valid) {
+            tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
+            wq = a.weights[bq * NK + idx];
+          }
+        }
+        const uint64_t m = __ballot(valid);
+        const int cnt = (int)__builtin_popcountll(m);
+        if (valid) {
+          const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+          const float wa0 = (1.f - tp.a) * wq, wa1 = tp.a * wq;
+          rec[4 * s + 0] = TapRec{tp.p00, wa0 * (1.f - tp.b)};
+          rec[4 * s + 1] = TapRec{tp.p00 + tp.dx, wa1 * (1.f - tp.b)};
+          rec[4 * s + 2] = TapRec{tp.p00 + tp.dy, wa0 * tp.b};
+          rec[4 * s + 3] = TapRec{tp.p00 + tp.dy + tp.dx, wa1 * tp.b};
+        }
+        wave_lds_sync();
+        // ---- phase C: gather the listed taps, lanes = channels
+        const int ntaps = 4 * cnt;
+#pragma unroll
+        for (int g = 0; g < kBlockC / kWave; ++g) {
+          const int c = c0 + g * kWave + lane;
+          if (c0 + g * kWave >= a.C) break;
+          const bool ch = c < a.C;
+          for (int j = 0; j < ntaps; j += kUnroll) {
+            float v[kUnroll], w[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+              const int jj = j + u;
+              const bool in = jj < ntaps;
+              const TapRec rr = rec[in ? jj : 0];
+              w[u] = in ? rr.w : 0.f;
+              v[u] = (in && ch) ? fb[(size_t)rr.off + c] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc[g] = fmaf(w[u], v[u], acc[g]);
+          }
+        }
+        wave_lds_sync();   // the records are read before the next pass overwrites them
+      }
+#pragma unroll
+      for (int g = 0; g < kBlockC / kWave; ++g) {
+        const int c = c0 + g * kWave + lane;
+        if (c < a.C) a.out[bq * a.C + c] = acc[g];
+      }
+    }
+  }
+}
+
+// Per-wave LDS of the backward: the in-view samples of one pass.
+struct SampleRec {
+  int p00, dx, dy, idx;   // taps as in Taps; idx = n * Kp + k
+  float a, b, w, pad;
+  double u, v, h2;
+};
+
+__global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
+  SampleRec* sS = reinterpret_cast<SampleRec*>(smem + sizeof(double) * 12 * a.N);           // [kWaves][kWave]
+  float* sG = reinterpret_cast<float*>(sS + kWaves * kWave);                                // [kWaves][Kp][3]
+  const int b = blockIdx.y;
+  stage_projections(sP, a.K, a.R, a.t, b, a.N);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  SampleRec* smp = sS + wid * kWave;
+  float* gk = sG + wid * a.Kp * 3;
+  const int NK = a.N * a.Kp;
+  const size_t HWC = (size_t)a.H * a.W * a.C;
+  const float* fb = a.feat + (size_t)b * a.N * HWC;
+  float* gfb = a.gfeat + (size_t)b * a.N * HWC;
+
+  for (int i = 0; i < kQPW; ++i) {
+    const int q = blockIdx.x * kQPB + i * kWaves + wid;
+    if (q >= a.Q) break;
+    const size_t bq = (size_t)b * a.Q + q;
+    const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
+    const float* gq = a.grad + bq * a.C;
+    for (int e = lane; e < a.Kp * 3; e += kWave) gk[e] = 0.f;
+    wave_lds_sync();
+    for (int base = 0; base < NK; base += kWave) {
+      // ---- phase A, as in the forward; out-of-view pairs get dL/dw = 0 here
+      const int idx = base + lane;
+      bool valid = false;
+      Proj pr;
+      int n = 0;
+      if (idx < NK) {
+        n = idx / a.Kp;
+        const int k = idx - n * a.Kp;
+        const float* o = a.offsets + (bq * a.Kp + k) * 3;
+        pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
+        valid = pr.valid;
+        if (!valid) a.gweights[bq * NK + idx] = 0.f;
+      }
+      const uint64_t m = __ballot(valid);
+      const int cnt = (int)__builtin_popcountll(m);
+      if (valid) {
+        const Taps tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
+        const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        smp[s] = SampleRec{tp.p00, tp.dx, tp.dy, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
+      }
+      wave_lds_sync();
+      // ---- per in-view sample: feature scatter, dL/dw, dL/du and dL/dv
+      for (int s = 0; s < cnt; ++s) {
+        const SampleRec sr = smp[s];
+        const int p00 = uniform(sr.p00), dx = uniform(sr.dx), dy = uniform(sr.dy);
+        const float fa = sr.a, fbt = sr.b, w = sr.w;
+        const float w00 = (1.f - fa) * (1.f - fbt), w01 = fa * (1.f - fbt), w10 = (1.f - fa) * fbt, w11 = fa * fbt;
+        float ds = 0.f, du = 0.f, dv = 0.f;
+        for (int c = lane; c < a.C; c += kWave) {
+          const float g = gq[c];
+          const float F00 = fb[(size_t)p00 + c], F01 = fb[(size_t)p00 + dx + c];
+          const float F10 = fb[(size_t)p00 + dy + c], F11 = fb[(size_t)p00 + dy + dx + c];
+          const float smpv = w00 * F00 + w01 * F01 + w10 * F10 + w11 * F11;
+          const float su = (1.f - fbt) * (F01 - F00) + fbt * (F11 - F10);
+          const float sv = (1.f - fa) * (F10 - F00) + fa * (F11 - F01);
+          ds = fmaf(g, smpv, ds);
+          du = fmaf(g, su, du);
+          dv = fmaf(g, sv, dv);
+          const float wg = w * g;
+          unsafeAtomicAdd(gfb + (size_t)p00 + c, w00 * wg);
+          unsafeAtomicAdd(gfb + (size_t)p00 + dx + c, w01 * wg);
+          unsafeAtomicAdd(gfb + (size_t)p00 + dy + c, w10 * wg);
+          unsafeAtomicAdd(gfb + (size_t)p00 + dy + dx + c, w11 * wg);
+        }
+        ds = wave_sum(ds);
+        du = wave_sum(du);
+        dv = wave_sum(dv);
+        if (lane == 0) {
+          const int sidx = sr.idx;
+          const int n = sidx / a.Kp, k = sidx - n * a.Kp;
+          a.gweights[bq * NK + sidx] = ds;
+          // keypoint gradient through the projection: du/dp = (P_1 - u P_3) / h_3, dv/dp likewise
+          const double* P = sP + n * 12;
+          const double ih = 1.0 / sr.h2;
+          const double lu = (double)w * du, lv = (double)w * dv;
+          for (int r = 0; r < 3; ++r) {
+            const double ju = (P[r] - sr.u * P[8 + r]) * ih, jv = (P[4 + r] - sr.v * P[8 + r]) * ih;
+            gk[k * 3 + r] += (float)(lu * ju + lv * jv);
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    // the query's keypoint and anchor gradients
+    wave_lds_sync();
+    float sx = 0.f, sy = 0.f, sz = 0.f;
+    for (int k = lane; k < a.Kp; k += kWave) {
+      const float gx = gk[k * 3], gy = gk[k * 3 + 1], gz = gk[k * 3 + 2];
+      float* go = a.goffsets + (bq * a.Kp + k) * 3;
+      go[0] = gx;
+      go[1] = gy;
+      go[2] = gz;
+      sx += gx;
+      sy += gy;
+      sz += gz;
+    }
+    if (a.ganchors != nullptr) {
+      sx = wave_sum(sx);
+      sy = wave_sum(sy);
+      sz = wave_sum(sz);
+      if (lane == 0) {
+        a.ganchors[bq * 3] = sx;
+        a.ganchors[bq * 3 + 1] = sy;
+        a.ganchors[bq * 3 + 2] = sz;
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
+__global__ void deform_fill_zero(float* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream) {
+  if (a.B == 0 || a.Q == 0 || a.C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.Q + kQPB - 1) / kQPB), (unsigned)a.B);
+  const size_t shmem = sizeof(double) * 12 * a.N + sizeof(TapRec) * 4 * kWave * kWaves;
+  hipLaunchKernelGGL(deform_fwd, grid, dim3(kBlock), shmem, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_deform_backward(const DeformArgs& a, hipStream_t stream) {
+  const size_t nF = (size_t)a.B * a.N * a.H * a.W * a.C;
+  if (nF > 0) {
+    const size_t blocks = (nF + 255) / 256;
+    hipLaunchKernelGGL(deform_fill_zero, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream,
+                       a.gfeat, nF);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.B == 0 || a.Q == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.Q + kQPB - 1) / kQPB), (unsigned)a.B);
+  const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves + sizeof(float) * 3 * a.Kp * kWaves;
+  hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fbev

@@ -13,6 +13,7 @@
 #include "../../include/flashbev.h"
 #include "kernels.h"
 #include "lift_splat.h"
+#include "deform_agg.h"
 
 namespace {
 
@@ -259,6 +260,97 @@ fbev_status lss_backward_impl(const float* grad_out, const float* depth, const f
   return device_status(fbev::launch_lss_backward(a, static_cast<hipStream_t>(stream)), "fbev_lss_backward launch");
 }
 
+
+// Deformable Aggregation arguments: features [B,N,H,W,C] fp32, Q queries with
+// anchors [B,Q,3], Kp keypoint offsets [B,Q,Kp,3] and weights [B,Q,N,Kp].
+fbev_status check_deform(const fbev_feat_desc& fd, int32_t Q, int32_t Kp, const float* K, const float* R,
+                         const float* t, fbev::DeformArgs& a) {
+  if (fd.B < 0 || fd.N < 0 || fd.C < 0 || fd.H < 0 || fd.W < 0 || Q < 0 || Kp < 0)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "negative size (B=%d N=%d C=%d H=%d W=%d Q=%d Kp=%d)", fd.B, fd.N, fd.C,
+                fd.H, fd.W, Q, Kp);
+  if (fd.N > FBEV_MAX_CAMERAS)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "N=%d cameras exceeds FBEV_MAX_CAMERAS=%d", fd.N, FBEV_MAX_CAMERAS);
+  if (fd.H > FBEV_MAX_GRID || fd.W > FBEV_MAX_GRID)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "feature map %dx%d above %d", fd.H, fd.W, FBEV_MAX_GRID);
+  if (Kp > FBEV_MAX_KEYPOINTS)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "Kp=%d keypoints exceeds FBEV_MAX_KEYPOINTS=%d", Kp, FBEV_MAX_KEYPOINTS);
+  if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "K, R and t must be non-NULL when B*N > 0");
+  const int64_t per_sample = (int64_t)fd.N * fd.H * fd.W * fd.C;
+  if (per_sample >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld elements (limit 2^31 - 1)",
+                (long long)per_sample);
+  if ((int64_t)Q * fd.C >= (int64_t)1 << 40 || (int64_t)Q >= (int64_t)1 << 30)
+    return fail(FBEV_ERR_UNSUPPORTED, "Q=%d queries too many", Q);
+  a.K = K;
+  a.R = R;
+  a.t = t;
+  a.B = fd.B;
+  a.N = fd.N;
+  a.C = fd.C;
+  a.H = fd.H;
+  a.W = fd.W;
+  a.Q = Q;
+  a.Kp = Kp;
+  return FBEV_OK;
+}
+
+fbev_status deform_forward_impl(const float* features, fbev_feat_desc fd, const float* K, const float* R,
+                                const float* t, const float* anchors, const float* offsets, const float* weights,
+                                int32_t Q, int32_t Kp, float* out, void* stream) {
+  fbev::DeformArgs a{};
+  fbev_status s = check_deform(fd, Q, Kp, K, R, t, a);
+  if (s != FBEV_OK) return s;
+  const int64_t n_out = (int64_t)fd.B * Q * fd.C;
+  if (n_out == 0) return FBEV_OK;
+  if (out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (anchors == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "anchors is NULL");
+  const bool pairs = (int64_t)fd.N * Kp > 0;
+  if (pairs && (offsets == nullptr || weights == nullptr))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "offsets and weights must be non-NULL when N*Kp > 0");
+  if (pairs && (int64_t)fd.H * fd.W > 0 && features == nullptr)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "features is NULL");
+  a.feat = features;
+  a.anchors = anchors;
+  a.offsets = offsets;
+  a.weights = weights;
+  a.out = out;
+  return device_status(fbev::launch_deform_forward(a, static_cast<hipStream_t>(stream)), "fbev_deform_forward launch");
+}
+
+fbev_status deform_backward_impl(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                 const float* R, const float* t, const float* anchors, const float* offsets,
+                                 const float* weights, int32_t Q, int32_t Kp, float* grad_features,
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream) {
+  fbev::DeformArgs a{};
+  fbev_status s = check_deform(fd, Q, Kp, K, R, t, a);
+  if (s != FBEV_OK) return s;
+  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  const int64_t n_q = (int64_t)fd.B * Q;
+  const bool pairs = (int64_t)fd.N * Kp > 0;
+  if (n_feat > 0 && grad_features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_features is NULL");
+  if (n_q > 0 && pairs && grad_weights == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_weights is NULL");
+  if (n_q > 0 && Kp > 0 && grad_offsets == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_offsets is NULL");
+  if (n_q > 0) {
+    if (anchors == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "anchors is NULL");
+    if (Kp > 0 && offsets == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "offsets is NULL");
+    if (pairs && weights == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "weights is NULL");
+    if (pairs && fd.C > 0 && (int64_t)fd.H * fd.W > 0 && (features == nullptr || grad_out == nullptr))
+      return fail(FBEV_ERR_INVALID_ARGUMENT, "features and grad_out must be non-NULL");
+  }
+  a.grad = grad_out;
+  a.feat = features;
+  a.anchors = anchors;
+  a.offsets = offsets;
+  a.weights = weights;
+  a.gfeat = grad_features;
+  a.gweights = grad_weights;
+  a.goffsets = grad_offsets;
+  a.ganchors = grad_anchors;
+  return device_status(fbev::launch_deform_backward(a, static_cast<hipStream_t>(stream)),
+                       "fbev_deform_backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +392,20 @@ fbev_status fbev_lss_backward(const float* grad_out, const float* depth, const f
                               void* stream) {
   return lss_backward_impl(grad_out, depth, context, fd, D, d_min, d_step, K, R, t, bev_range, X, Y, grad_depth,
                            grad_context, stream);
+}
+
+fbev_status fbev_deform_forward(const float* features, fbev_feat_desc fd, const float* K, const float* R,
+                                const float* t, const float* anchors, const float* offsets, const float* weights,
+                                int32_t Q, int32_t Kp, float* out, void* stream) {
+  return deform_forward_impl(features, fd, K, R, t, anchors, offsets, weights, Q, Kp, out, stream);
+}
+
+fbev_status fbev_deform_backward(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                 const float* R, const float* t, const float* anchors, const float* offsets,
+                                 const float* weights, int32_t Q, int32_t Kp, float* grad_features,
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream) {
+  return deform_backward_impl(grad_out, features, fd, K, R, t, anchors, offsets, weights, Q, Kp, grad_features,
+                              grad_weights, grad_offsets, grad_anchors, stream);
 }
 
 const char* fbev_status_string(fbev_status s) {

@@ -242,3 +242,59 @@ def lss_backward(grad_out: torch.Tensor, depth: torch.Tensor, context: torch.Ten
                                      _lib.bev_range(bev_range), X, Y, _ptr(grad_depth), _ptr(grad_context),
                                      _stream(dev)))
     return grad_depth, grad_context
+
+
+# ---- Deformable Aggregation (multi-camera deformable sampling)
+
+def _check_deform(features, K, R, t, anchors, offsets, weights):
+    if features.dim() != 5 or features.dtype != torch.float32 or not features.is_cuda or not features.is_contiguous():
+        raise ValueError("features must be a contiguous float32 [B,N,H,W,C] device tensor")
+    B, N, H, W, C = features.shape
+    dev = features.device
+    _check_cams(K, R, t, B, N, dev)
+    if anchors.dim() != 3 or anchors.shape[0] != B or anchors.shape[2] != 3:
+        raise ValueError(f"anchors must be [B,Q,3], got {tuple(anchors.shape)}")
+    Q = anchors.shape[1]
+    if offsets.dim() != 4 or tuple(offsets.shape[:2]) != (B, Q) or offsets.shape[3] != 3:
+        raise ValueError(f"offsets must be [B,Q,Kp,3], got {tuple(offsets.shape)}")
+    Kp = offsets.shape[2]
+    if tuple(weights.shape) != (B, Q, N, Kp):
+        raise ValueError(f"weights must be [{B},{Q},{N},{Kp}], got {tuple(weights.shape)}")
+    for name, x in (("anchors", anchors), ("offsets", offsets), ("weights", weights)):
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.device != dev:
+            raise ValueError(f"{name} must be a contiguous float32 tensor on {dev}")
+    return B, N, H, W, C, Q, Kp, dev
+
+
+def deform_forward(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor, anchors: torch.Tensor,
+                   offsets: torch.Tensor, weights: torch.Tensor, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fbev_deform_forward: features [B,N,H,W,C] fp32, anchors [B,Q,3], offsets [B,Q,Kp,3],
+    weights [B,Q,N,Kp]; returns [B,Q,C] fp32."""
+    B, N, H, W, C, Q, Kp, dev = _check_deform(features, K, R, t, anchors, offsets, weights)
+    if out is None:
+        out = torch.empty((B, Q, C), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (B, Q, C) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,Q,C] tensor")
+    lib = _lib.load()
+    _lib.check(lib.fbev_deform_forward(_ptr(features), _lib.feat_desc(B, N, C, H, W), _ptr(K), _ptr(R), _ptr(t),
+                                       _ptr(anchors), _ptr(offsets), _ptr(weights), Q, Kp, _ptr(out), _stream(dev)))
+    return out
+
+
+def deform_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Tensor, R: torch.Tensor,
+                    t: torch.Tensor, anchors: torch.Tensor, offsets: torch.Tensor, weights: torch.Tensor, *,
+                    with_anchors: bool = True):
+    """fbev_deform_backward: (dL/dfeatures, dL/dweights, dL/doffsets, dL/danchors or None)."""
+    B, N, H, W, C, Q, Kp, dev = _check_deform(features, K, R, t, anchors, offsets, weights)
+    if tuple(grad_out.shape) != (B, Q, C) or grad_out.dtype != torch.float32 or not grad_out.is_contiguous() \
+            or grad_out.device != dev:
+        raise ValueError(f"grad_out must be a contiguous float32 [{B},{Q},{C}] tensor on {dev}")
+    gF = torch.empty_like(features)
+    gW = torch.empty_like(weights)
+    gO = torch.empty_like(offsets)
+    gA = torch.empty_like(anchors) if with_anchors else None
+    lib = _lib.load()
+    _lib.check(lib.fbev_deform_backward(_ptr(grad_out), _ptr(features), _lib.feat_desc(B, N, C, H, W), _ptr(K),
+                                        _ptr(R), _ptr(t), _ptr(anchors), _ptr(offsets), _ptr(weights), Q, Kp,
+                                        _ptr(gF), _ptr(gW), _ptr(gO), _ptr(gA), _stream(dev)))
+    return gF, gW, gO, gA

@@ -330,3 +330,81 @@ def random_lss_case(seed: int, B: int, N: int, C: int, H: int, W: int, D: int, X
     g = make_grad_out(3000 + seed, B, C, X, Y)
     return LssInputs(depth, ctx, K, R, t, tuple(float(np.float32(r)) for r in rng6), X, Y,
                      float(np.float32(d_min)), float(np.float32(d_step)), g)
+
+
+# ---- Deformable Aggregation inputs
+#
+# The SparseDriveV2 notes give the operator's scale: queries ~10^2 with tens
+# of keypoints each over up to six cameras (about 1.5 of them seeing a
+# keypoint).  "deform" stands in for a sparse detection head: 900 queries,
+# 13 keypoints, C = 256 on 16 x 44 maps (a 256 x 704 image at stride 16);
+# anchors uniform over +-50 m at heights in [-1, 2] m, offsets N(0, 1 m) per
+# axis.  "deform_bev" is the dense BEV form (spatial cross-attention over a
+# 200 x 200 grid): one query per cell centre at z = 0, 8 keypoints at the
+# height-bin centres of [-5, 3) m plus N(0, 0.1 m) jitter, C = 64.  Weights
+# per query are a flat-Dirichlet draw over its (camera, keypoint) pairs (a
+# point on the simplex, standing in for the network's softmax).
+
+DEFORM_WORKLOADS: Dict[str, dict] = {
+    "deform": dict(cid=8, B=1, N=6, C=256, H=16, W=44, Q=900, Kp=13, kind="sparse"),
+    "deform_bev": dict(cid=9, B=1, N=6, C=64, H=16, W=44, X=200, Y=200, Kp=8, rng6=_R50, kind="bev"),
+}
+
+
+@dataclasses.dataclass
+class DeformInputs:
+    F: np.ndarray            # logical [B,N,C,H,W] fp32
+    K: np.ndarray
+    R: np.ndarray
+    t: np.ndarray
+    anchors: np.ndarray      # [B,Q,3] fp32
+    offsets: np.ndarray      # [B,Q,Kp,3] fp32
+    weights: np.ndarray      # [B,Q,N,Kp] fp32
+    grad_out: Optional[np.ndarray] = None   # [B,Q,C] fp32
+
+
+def _dirichlet_weights(g, B: int, Q: int, N: int, Kp: int) -> np.ndarray:
+    if N * Kp == 0:
+        return np.zeros((B, Q, N, Kp), np.float32)
+    return g.dirichlet(np.ones(N * Kp), size=(B, Q)).reshape(B, Q, N, Kp).astype(np.float32)
+
+
+def make_deform_inputs(name: str = "deform", with_grad: bool = False) -> DeformInputs:
+    w = DEFORM_WORKLOADS[name]
+    B, N, C, H, W, Kp, cid = w["B"], w["N"], w["C"], w["H"], w["W"], w["Kp"], w["cid"]
+    K, R, t = make_rig(cid, B, N, H, W, False)
+    F = make_features(cid, B, N, C, H, W)
+    g = np.random.default_rng([cid, 4])
+    if w["kind"] == "sparse":
+        Q = w["Q"]
+        anchors = np.stack([g.uniform(-50, 50, (B, Q)), g.uniform(-50, 50, (B, Q)), g.uniform(-1, 2, (B, Q))], -1)
+        offsets = g.normal(0.0, 1.0, (B, Q, Kp, 3))
+    else:
+        X, Y = w["X"], w["Y"]
+        xmin, xmax, ymin, ymax, zmin, zmax = w["rng6"]
+        xs = xmin + (np.arange(X) + 0.5) * (xmax - xmin) / X
+        ys = ymin + (np.arange(Y) + 0.5) * (ymax - ymin) / Y
+        zs = zmin + (np.arange(Kp) + 0.5) * (zmax - zmin) / Kp
+        Q = X * Y
+        anchors = np.zeros((B, Q, 3))
+        anchors[..., 0] = np.repeat(xs, Y)[None]
+        anchors[..., 1] = np.tile(ys, X)[None]
+        offsets = g.normal(0.0, 0.1, (B, Q, Kp, 3))
+        offsets[..., 2] += zs[None, None, :]
+    weights = _dirichlet_weights(g, B, Q, N, Kp)
+    gout = np.random.default_rng([cid, 2]).standard_normal((B, Q, C), dtype=np.float32) if with_grad else None
+    return DeformInputs(F, K, R, t, anchors.astype(np.float32), offsets.astype(np.float32), weights, gout)
+
+
+def random_deform_case(seed: int, B: int, N: int, C: int, H: int, W: int, Q: int, Kp: int, spread: float = 30.0,
+                       offset_sigma: float = 1.5, pitch_deg: float = 0.0) -> DeformInputs:
+    """An arbitrary-size seeded Deformable Aggregation case (ragged / edge-case parity runs)."""
+    K, R, t = make_rig(4000 + seed, B, N, H, W, True, pitch_deg=pitch_deg)
+    F = make_features(4000 + seed, B, N, C, H, W)
+    g = np.random.default_rng([4000 + seed, 4])
+    anchors = np.stack([g.uniform(-spread, spread, (B, Q)), g.uniform(-spread, spread, (B, Q)),
+                        g.uniform(-1, 2, (B, Q))], -1)
+    offsets = g.normal(0.0, offset_sigma, (B, Q, Kp, 3))
+    weights = _dirichlet_weights(g, B, Q, N, Kp)
+    gout = np.random.default_rng([4000 + seed, 2]).standard_normal((B, Q, C), dtype=np.float32)
+    return DeformInputs(F, K, R, t, anchors.astype(np.float32), offsets.astype(np.float32), weights, gout)

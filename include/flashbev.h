@@ -45,10 +45,11 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 3
+#define FBEV_ABI_VERSION 4
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
+#define FBEV_MAX_KEYPOINTS 256
 
 typedef enum {
   FBEV_OK = 0,
@@ -209,6 +210,50 @@ fbev_status fbev_lss_backward(const float* grad_out, const float* depth, const f
                               int32_t D, float d_min, float d_step, const float* K, const float* R, const float* t,
                               fbev_range bev_range, int32_t X, int32_t Y, float* grad_depth, float* grad_context,
                               void* stream);
+
+/*
+ * Deformable Aggregation: multi-camera deformable sampling (SparseDriveV2
+ * notes, "Deformable Aggregation", steps 1-3), the operator the FlashBEV
+ * notes fuse for BEVFormer's spatial cross-attention.  For query q of batch
+ * sample b with anchor a_q and keypoint offsets o_{q,k} (k < Kp):
+ *
+ *   p_{q,k} = a_q + o_{q,k}                                   (ego frame, metres)
+ *   out[b, q, c] = sum_n sum_k  weights[b,q,n,k] * bilinear(F[b,n,:,:,c], u, v)   over (n, k) in view
+ *
+ * with [u, v, 1]^T ~ K_n (R_n p + t_n) and the in-view rule, pixel-centre
+ * convention and bilinear taps of fbev_forward (depth > 0, closed box
+ * [0, W-1] x [0, H-1]).  The weights are used as given (no renormalisation
+ * over the pairs in view).  Projection and the in-view test in double
+ * precision, interpolation and sums in fp32.
+ *
+ *   features : [B, N, H, W, C] fp32 channels-last, device, read only.
+ *   K, R, t  : as for fbev_forward.
+ *   anchors  : [B, Q, 3] fp32; offsets : [B, Q, Kp, 3] fp32; weights : [B, Q, N, Kp] fp32; device.
+ *   Q, Kp    : queries per sample and keypoints per query (Kp <= FBEV_MAX_KEYPOINTS).
+ *   out      : [B, Q, C] fp32, device, fully overwritten.  Deterministic.
+ * Errors as for fbev_forward.
+ */
+fbev_status fbev_deform_forward(const float* features, fbev_feat_desc fd, const float* K, const float* R,
+                                const float* t, const float* anchors, const float* offsets, const float* weights,
+                                int32_t Q, int32_t Kp, float* out, void* stream);
+
+/*
+ * Gradients of fbev_deform_forward with the in-view mask held fixed (the page
+ * asks for a sampling chain that gradients pass through):
+ *   grad_features : [B,N,H,W,C] fp32 — each in-view sample adds w * tap weight * g
+ *                   to its four taps (zeroed on `stream`, then fp32 atomics).
+ *   grad_weights  : [B,Q,N,Kp] fp32 — <sample, g> for pairs in view, 0 otherwise.
+ *   grad_offsets  : [B,Q,Kp,3] fp32 — sum over cameras of w (<ds/du, g> du/dp + <ds/dv, g> dv/dp),
+ *                   the bilinear sample's derivative inside its pixel square times the
+ *                   projection's Jacobian du/dp = (P_1 - u P_3) / h_3 (P = K [R | t]).
+ *   grad_anchors  : [B,Q,3] fp32 — the sum of grad_offsets over k; may be NULL.
+ * All outputs are fully overwritten; grad_out is [B,Q,C]; other arguments as
+ * for fbev_deform_forward.
+ */
+fbev_status fbev_deform_backward(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                 const float* R, const float* t, const float* anchors, const float* offsets,
+                                 const float* weights, int32_t Q, int32_t Kp, float* grad_features,
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream);
 
 /* Static text for a status code. */
 const char* fbev_status_string(fbev_status s);

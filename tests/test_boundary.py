@@ -211,3 +211,56 @@ def test_lss_empty_problems_return_ok_without_device_work(lib):
     assert lss_fwd(lib, desc=(1, 6, 0, 8, 22), out=None) == 0
     assert lss_bwd(lib, desc=(0, 6, 64, 8, 22), grad=None, depth=None, ctx=None, gd=None, gc=None, K=None) == 0
     assert lss_bwd(lib, desc=(1, 6, 64, 0, 22), grad=None, depth=None, ctx=None, gd=None, gc=None) == 0
+
+
+def dfwd(lib, feat=FAKE, desc=(1, 6, 64, 16, 44), K=FAKE, A=FAKE, D=FAKE, Wt=FAKE, Q=10, Kp=4, out=FAKE):
+    return lib.fbev_deform_forward(feat, _lib.feat_desc(*desc), K, FAKE, FAKE, A, D, Wt, Q, Kp, out, None)
+
+
+def dbwd(lib, grad=FAKE, feat=FAKE, desc=(1, 6, 64, 16, 44), A=FAKE, D=FAKE, Wt=FAKE, Q=10, Kp=4, gF=FAKE, gW=FAKE,
+         gO=FAKE, gA=None):
+    return lib.fbev_deform_backward(grad, feat, _lib.feat_desc(*desc), FAKE, FAKE, FAKE, A, D, Wt, Q, Kp, gF, gW, gO,
+                                    gA, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(desc=(1, 6, -1, 16, 44)), 1, "negative size"),
+    (dict(Q=-1), 1, "negative size"),
+    (dict(Kp=-2), 1, "negative size"),
+    (dict(Kp=257), 1, "FBEV_MAX_KEYPOINTS"),
+    (dict(desc=(1, 65, 64, 16, 44)), 1, "exceeds FBEV_MAX_CAMERAS"),
+    (dict(K=None), 1, "K, R and t"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(A=None), 1, "anchors is NULL"),
+    (dict(D=None), 1, "offsets and weights"),
+    (dict(Wt=None), 1, "offsets and weights"),
+    (dict(feat=None), 1, "features is NULL"),
+    (dict(desc=(1, 64, 4096, 128, 128)), 2, "limit 2^31"),
+])
+def test_deform_forward_validation(lib, kwargs, status, msg):
+    assert dfwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(Q=-3), 1, "negative size"),
+    (dict(gF=None), 1, "grad_features is NULL"),
+    (dict(gW=None), 1, "grad_weights is NULL"),
+    (dict(gO=None), 1, "grad_offsets is NULL"),
+    (dict(A=None), 1, "anchors is NULL"),
+    (dict(D=None), 1, "offsets is NULL"),
+    (dict(Wt=None), 1, "weights is NULL"),
+    (dict(grad=None), 1, "features and grad_out"),
+    (dict(feat=None), 1, "features and grad_out"),
+])
+def test_deform_backward_validation(lib, kwargs, status, msg):
+    assert dbwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+def test_deform_empty_problems_return_ok_without_device_work(lib):
+    assert dfwd(lib, desc=(0, 6, 64, 16, 44), feat=None, K=None, A=None, D=None, Wt=None, out=None) == 0
+    assert dfwd(lib, Q=0, A=None, D=None, Wt=None, out=None) == 0
+    assert dfwd(lib, desc=(1, 6, 0, 16, 44), out=None) == 0
+    assert dbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, feat=None, A=None, D=None, Wt=None, gF=None, gW=None,
+                gO=None) == 0
