@@ -24,9 +24,10 @@ struct DeformArgs {
   float* goffsets;         // backward: [B,Q,Kp,3]
   float* ganchors;         // backward: [B,Q,3] or NULL
   int B, N, C, H, W, Q, Kp;
+  int q_stride;            // set by the backward's launcher
 };
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream);
-hipError_t launch_deform_backward(const DeformArgs& a, hipStream_t stream);
+hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream);
 
 }  // namespace fbev

@@ -38,10 +38,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kBlock = kWave * kWaves;
-constexpr int kQPW = 4;                   // queries per wave
-constexpr int kQPB = kQPW * kWaves;       // queries per workgroup
 constexpr int kUnroll = 8;                // tap rows in flight per lane
-constexpr int kBlockC = 4 * kWave;        // channels a wave accumulates per pass over the samples
 
 struct TapRec {
   int off;      // element offset of the tap's channel row within the batch sample
@@ -154,72 +151,62 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
   const size_t HWC = (size_t)a.H * a.W * a.C;
   const float* fb = a.feat + (size_t)b * a.N * HWC;
 
-  for (int i = 0; i < kQPW; ++i) {
-    const int q = blockIdx.x * kQPB + i * kWaves + wid;
-    if (q >= a.Q) break;
-    const size_t bq = (size_t)b * a.Q + q;
-    const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
-    for (int c0 = 0; c0 < a.C; c0 += kBlockC) {
-      float acc[kBlockC / kWave];
-#pragma unroll
-      for (int g = 0; g < kBlockC / kWave; ++g) acc[g] = 0.f;
-      for (int base = 0; base < NK; base += kWave) {
-        // ---- phase A: pair idx = n * Kp + k on this lane
-        const int idx = base + lane;
-        bool valid = false;
-        Taps tp;
-        float wq = 0.f;
-        if (idx < NK) {
-          const int n = idx / a.Kp, k = idx - n * a.Kp;
-          const float* o = a.offsets + (bq * a.Kp + k) * 3;
-          const Proj pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
-          valid = pr.valid;
-          if (valid) {
-            tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
-            wq = a.weights[bq * NK + idx];
-          }
-        }
-        const uint64_t m = __ballot(valid);
-        const int cnt = (int)__builtin_popcountll(m);
-        if (valid) {
-          const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-          const float wa0 = (1.f - tp.a) * wq, wa1 = tp.a * wq;
-          rec[4 * s + 0] = TapRec{tp.p00, wa0 * (1.f - tp.b)};
-          rec[4 * s + 1] = TapRec{tp.p00 + tp.dx, wa1 * (1.f - tp.b)};
-          rec[4 * s + 2] = TapRec{tp.p00 + tp.dy, wa0 * tp.b};
-          rec[4 * s + 3] = TapRec{tp.p00 + tp.dy + tp.dx, wa1 * tp.b};
-        }
-        wave_lds_sync();
-        // ---- phase C: gather the listed taps, lanes = channels
-        const int ntaps = 4 * cnt;
-#pragma unroll
-        for (int g = 0; g < kBlockC / kWave; ++g) {
-          const int c = c0 + g * kWave + lane;
-          if (c0 + g * kWave >= a.C) break;
-          const bool ch = c < a.C;
-          for (int j = 0; j < ntaps; j += kUnroll) {
-            float v[kUnroll], w[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-              const int jj = j + u;
-              const bool in = jj < ntaps;
-              const TapRec rr = rec[in ? jj : 0];
-              w[u] = in ? rr.w : 0.f;
-              v[u] = (in && ch) ? fb[(size_t)rr.off + c] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[g] = fmaf(w[u], v[u], acc[g]);
-          }
-        }
-        wave_lds_sync();   // the records are read before the next pass overwrites them
-      }
-#pragma unroll
-      for (int g = 0; g < kBlockC / kWave; ++g) {
-        const int c = c0 + g * kWave + lane;
-        if (c < a.C) a.out[bq * a.C + c] = acc[g];
+  // this wave's unit: query q, channels [c0, c0 + 64)
+  const int groups = (a.C + kWave - 1) / kWave;
+  const int unit = blockIdx.x * kWaves + wid;
+  if (unit >= a.Q * groups) return;                   // no barrier follows
+  const int q = unit / groups;
+  const int c0 = (unit - q * groups) * kWave;
+  const size_t bq = (size_t)b * a.Q + q;
+  const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
+  const int c = c0 + lane;
+  const bool ch = c < a.C;
+  float acc = 0.f;
+  for (int base = 0; base < NK; base += kWave) {
+    // ---- phase A: pair idx = n * Kp + k on this lane
+    const int idx = base + lane;
+    bool valid = false;
+    Taps tp;
+    float wq = 0.f;
+    if (idx < NK) {
+      const int n = idx / a.Kp, k = idx - n * a.Kp;
+      const float* o = a.offsets + (bq * a.Kp + k) * 3;
+      const Proj pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
+      valid = pr.valid;
+      if (valid) {
+        tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
+        wq = a.weights[bq * NK + idx];
       }
     }
+    const uint64_t m = __ballot(valid);
+    const int cnt = (int)__builtin_popcountll(m);
+    if (valid) {
+      const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      const float wa0 = (1.f - tp.a) * wq, wa1 = tp.a * wq;
+      rec[4 * s + 0] = TapRec{tp.p00, wa0 * (1.f - tp.b)};
+      rec[4 * s + 1] = TapRec{tp.p00 + tp.dx, wa1 * (1.f - tp.b)};
+      rec[4 * s + 2] = TapRec{tp.p00 + tp.dy, wa0 * tp.b};
+      rec[4 * s + 3] = TapRec{tp.p00 + tp.dy + tp.dx, wa1 * tp.b};
+    }
+    wave_lds_sync();
+    // ---- phase C: gather the listed taps, lanes = channels
+    const int ntaps = 4 * cnt;
+    for (int j = 0; j < ntaps; j += kUnroll) {
+      float v[kUnroll], w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int jj = j + u;
+        const bool in = jj < ntaps;
+        const TapRec rr = rec[in ? jj : 0];
+        w[u] = in ? rr.w : 0.f;
+        v[u] = (in && ch) ? fb[(size_t)rr.off + c] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc = fmaf(w[u], v[u], acc);
+    }
+    wave_lds_sync();   // the records are read before the next pass overwrites them
   }
+  if (ch) a.out[bq * a.C + c] = acc;
 }
 
 // Per-wave LDS of the backward: the in-view samples of one pass.
@@ -247,9 +234,12 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   const float* fb = a.feat + (size_t)b * a.N * HWC;
   float* gfb = a.gfeat + (size_t)b * a.N * HWC;
 
-  for (int i = 0; i < kQPW; ++i) {
-    const int q = blockIdx.x * kQPB + i * kWaves + wid;
-    if (q >= a.Q) break;
+  {
+    // one query per wave, visited in the order q = unit * stride mod Q (stride coprime to Q), which
+    // spreads the waves that run at the same time over the image and so over the atomics' addresses
+    const int unit = blockIdx.x * kWaves + wid;
+    if (unit >= a.Q) return;                          // no barrier follows
+    const int q = (int)(((long long)unit * a.q_stride) % a.Q);
     const size_t bq = (size_t)b * a.Q + q;
     const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
     const float* gq = a.grad + bq * a.C;
@@ -355,13 +345,24 @@ __global__ void deform_fill_zero(float* __restrict__ dst, size_t n) {
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream) {
   if (a.B == 0 || a.Q == 0 || a.C == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.Q + kQPB - 1) / kQPB), (unsigned)a.B);
+  const long long units = (long long)a.Q * ((a.C + kWave - 1) / kWave);
+  const dim3 grid((unsigned)((units + kWaves - 1) / kWaves), (unsigned)a.B);
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(TapRec) * 4 * kWave * kWaves;
   hipLaunchKernelGGL(deform_fwd, grid, dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_deform_backward(const DeformArgs& a, hipStream_t stream) {
+// A stride coprime to Q near Q times the golden ratio (1 when Q is small).
+int query_stride(int Q) {
+  if (Q < 64) return 1;
+  auto gcd = [](long long x, long long y) { while (y) { const long long r = x % y; x = y; y = r; } return x; };
+  long long s = (long long)(0.6180339887 * Q) | 1;
+  while (gcd(s, Q) != 1) s += 2;
+  return (int)(s % Q);
+}
+
+hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream) {
+  a.q_stride = query_stride(a.Q);
   const size_t nF = (size_t)a.B * a.N * a.H * a.W * a.C;
   if (nF > 0) {
     const size_t blocks = (nF + 255) / 256;
@@ -371,7 +372,7 @@ hipError_t launch_deform_backward(const DeformArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.B == 0 || a.Q == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.Q + kQPB - 1) / kQPB), (unsigned)a.B);
+  const dim3 grid((unsigned)((a.Q + kWaves - 1) / kWaves), (unsigned)a.B);
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves + sizeof(float) * 3 * a.Kp * kWaves;
   hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
