@@ -22,7 +22,9 @@ lss / lss_batched (Lift-Splat, the push view transform: fbev_lss_forward +
 fbev_lss_backward with 41 depth bins and 64 context channels per pixel), or
 deform / deform_bev (Deformable Aggregation: fbev_deform_forward +
 fbev_deform_backward for 900 sparse queries x 13 keypoints, or one query per
-cell of a 200 x 200 grid x 8 keypoints).
+cell of a 200 x 200 grid x 8 keypoints), or cameras (the gradients of the
+Sampling-VT output with respect to K, R and t, fbev_backward_cameras, on the
+nuScenes-shaped workload).
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "sampling_vt.hip")
 LSS_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "lift_splat.hip")
 DEFORM_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "deform_agg.hip")
+CAMERA_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "camera_grad.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -53,10 +56,14 @@ def kernel_source_hash(path: str = KERNEL_SRC) -> str:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel, workload: str):
     """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
     they were taken on a different kernel source or workload (or never).  Each
-    workload's record names the source file its counters were taken on."""
+    workload's record names the source file its counters were taken on.
+    ``kernel`` may be a list: the bytes of one pass of those kernels."""
+    if isinstance(kernel, (list, tuple)):
+        parts = [measured_traffic(k, workload) for k in kernel]
+        return None if any(v is None for v in parts) else sum(parts)
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -72,6 +79,18 @@ def measured_traffic(kernel: str, workload: str):
         return None
     k = w.get("kernels", {}).get(kernel)
     return k.get("bytes_per_launch") if k else None
+
+
+def pass_roofline(kernels, rate, nbytes, workload, exact_traffic=True):
+    """The ``roofline`` object of one timed pass: algorithmic bytes over the pass's HIP-event time.
+    ``kernels`` lists the pass's launches in order (their rocprofv3 durations add up to the pass);
+    ``traffic`` sums their counter bytes (None when a launch of a different size repeats a name, or
+    when the counters are missing or stale)."""
+    achieved = rate["hbm_gbps_algorithmic"]
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(kernels, workload) if exact_traffic else None,
+            "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
 
 
 def calibration_copy(args, dev):
@@ -227,12 +246,10 @@ def main_lss(args):
 
     fwd = rates(fwd_ms, fwd_bytes)
     bwd = rates(bwd_ms, bwd_bytes)
-    dom_name, dom, dom_bytes = ("lift_splat_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        ("lift_splat_bwd", bwd, bwd_bytes)
-    achieved = dom["hbm_gbps_algorithmic"]
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
-                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+    # the timed passes: the forward kernel alone; the backward's two zero-fills and its kernel
+    dom_k, dom, dom_bytes = (["lift_splat_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        (["lss_fill_zero", "lss_fill_zero", "lift_splat_bwd"], bwd, bwd_bytes)
+    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
     line = {
         "metric": METRIC,
         "value": out_elems / (ms_step * 1e-3),
@@ -354,11 +371,9 @@ def main_deform(args):
 
     fwd = rates(fwd_ms, fwd_bytes)
     bwd = rates(bwd_ms, bwd_bytes)
-    dom_name, dom, dom_bytes = ("deform_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else ("deform_bwd", bwd, bwd_bytes)
-    achieved = dom["hbm_gbps_algorithmic"]
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
-                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+    dom_k, dom, dom_bytes = (["deform_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        (["deform_fill_zero", "deform_bwd"], bwd, bwd_bytes)
+    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
     line = {
         "metric": METRIC,
         "value": out_elems / (ms_step * 1e-3),
@@ -383,6 +398,100 @@ def main_deform(args):
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline_deform(inp, 4000)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_cameras(inp, min_seconds=10.0):
+    """Time the fp64 camera-gradient oracle over the whole grid, repeated until ``min_seconds`` have passed."""
+    import oracle.camera_grad as cg
+    reps = 0
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    while True:
+        cg.oracle_camera_backward(inp.grad_out, inp.F, inp.K, inp.R, inp.t, inp.rng6, inp.X, inp.Y, inp.Z)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds:
+            break
+    cpu = time.process_time() - c0
+    B, C = inp.F.shape[0], inp.F.shape[2]
+    return {
+        "value": reps * B * C * inp.X * inp.Y / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy camera-gradient oracle, {reps} whole passes over the {inp.X}x{inp.Y}x{inp.Z} grid, "
+                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def main_cameras(args):
+    """Camera gradients: one step = fbev_backward_cameras (gather pass + fixed-order finish) on one batch."""
+    import numpy as np
+    import torch
+    from camera_bev_view_amd import ops
+    from camera_bev_view_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    inp = wl.make_inputs("nuscenes", with_grad=True)
+    B, N, C, H, W = inp.F.shape
+    X, Y, Z = inp.X, inp.Y, inp.Z
+    F = to_dev(inp.F.transpose(0, 1, 3, 4, 2))
+    K, R, t = (to_dev(a) for a in (inp.K, inp.R, inp.t))
+    g = to_dev(inp.grad_out)
+    ws = torch.empty((1 << 24,), dtype=torch.uint8, device=dev)
+    call = lambda: ops.camera_backward(g, F, K, R, t, inp.rng6, X, Y, Z, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup} steps on cameras")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    calibration_copy(args, dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        call()
+        ev[k][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    pass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (pass {pass_ms * 1e3:.2f} us)")
+
+    out_elems = B * C * X * Y
+    nbytes = B * N * H * W * C * 4 + out_elems * 4 + B * N * 21 * 4 * 2   # features, grad_out, cameras in, gradients out
+    achieved = nbytes / (pass_ms * 1e-3) / 1e9
+    roofline = pass_roofline(["camera_grad_main", "camera_grad_finish"], {"ms": pass_ms, "hbm_gbps_algorithmic": achieved},
+                             nbytes, "cameras")
+    line = {
+        "metric": METRIC,
+        "value": out_elems / (ms_step * 1e-3),
+        "unit": "BEV output elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
+        "config": {"workload": f"cameras: dL/dK, dL/dR, dL/dt of the Sampling-VT, B={B} N={N} C={C} HxW={H}x{W} "
+                               f"grid {X}x{Y}x{Z} (outputs = the BEV elements whose gradient is pulled back)",
+                   "B": B, "N": N, "C": C, "H": H, "W": W, "X": X, "Y": Y, "Z": Z},
+        "pass": {"ms": pass_ms, "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": achieved},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline_cameras(inp)
     print(json.dumps(line), flush=True)
 
 
@@ -413,6 +522,8 @@ def main():
         return main_lss(args)
     if args.workload in wl.DEFORM_WORKLOADS:
         return main_deform(args)
+    if args.workload == "cameras":
+        return main_cameras(args)
     dev = torch.device("cuda:0")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if args.workload in wl.PYRAMIDS:
@@ -501,12 +612,11 @@ def main():
 
     fwd = rates(fwd_ms, fwd_bytes)
     bwd = rates(bwd_ms, bwd_bytes)
-    dom_name, dom, dom_bytes = ("sampling_vt_fwd", fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        ("sampling_vt_bwd", bwd, bwd_bytes)
-    achieved = dom["hbm_gbps_algorithmic"]
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom_name, args.workload),
-                "kernel": dom_name, "launch_ms": dom["ms"], "algorithmic_bytes": dom_bytes}
+    # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch
+    # per feature level)
+    dom_k, dom, dom_bytes = (["sampling_vt_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        (["fill_zero_f32"] + ["sampling_vt_bwd"] * nlev, bwd, bwd_bytes)
+    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload, exact_traffic=(nlev == 1))
 
     line = {
         "metric": METRIC,

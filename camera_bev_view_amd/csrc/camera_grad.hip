@@ -1,0 +1,366 @@
+// Gradients of the dense Sampling-VT output with respect to the cameras
+// (dL/dK, dL/dR, dL/dt) for gfx950.
+//
+// The sampling chain of the FlashBEV notes ("Method" items 1-4: projection,
+// validity, bilinear sample, valid-camera mean, height sum) is differentiable
+// in the cameras wherever the in-view mask and the counts do not change
+// (SparseDriveV2 notes, "Deformable Aggregation" pitfalls: the projection and
+// the sampling must let gradients through).  For an in-view sample of camera
+// n at voxel centre p with h = P [p; 1], P = K [R | t], u = h_1 / h_3 and
+// v = h_2 / h_3:
+//
+//   dL/du = <g_cell, d(sample)/du> / count,  dL/dv likewise,
+//   d(sample)/du = (1 - b)(F01 - F00) + b (F11 - F10),
+//   d(sample)/dv = (1 - a)(F10 - F00) + a (F11 - F01),
+//   dL/dP_n += [dL/du; dL/dv; -(u dL/du + v dL/dv)] [p; 1]^T / h_3,
+//
+// and finally dL/dK = dL/dP [R | t]^T, dL/d[R | t] = K^T dL/dP.
+//
+// camera_grad_main: a workgroup walks units of 16 cells of one x-row and one
+// 64-channel group (the tile's upstream gradient staged in LDS).  Per cell and
+// pass, lane n * zpc + zl tests bin zc + zl against camera n (the layout of the
+// forward's validity pass, so a lane's camera is the same in every pass and
+// every cell); the in-view samples are compacted into a per-wave list, and for
+// each of them the wave computes the four tap dot products <g_cell, F_tap> with
+// lanes = (tap, 4-channel chunk) and a 16-lane DPP sum.  The owning lane turns
+// them into dL/du, dL/dv and adds its 12 entries of dL/dP in registers.  At the
+// end the lanes of one camera and the four waves are summed in a fixed order
+// into the workgroup's slice of the workspace.  camera_grad_finish (a
+// workgroup per camera, a wave per entry) sums the slices in a fixed order
+// (fp64) and applies the chain through P: the result is deterministic.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace fbev {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kBlock = kWave * kWaves;
+constexpr int kTileY = 16;               // cells per unit (one x-row)
+constexpr int kCg = 64;                  // channels per unit
+constexpr int kGLd = kCg + 4;            // padded LDS row of one cell's upstream gradient
+constexpr int kRedLd = 13;               // padded LDS row of one lane's 12 partial sums
+constexpr int kUnroll = 4;               // samples in flight per gather step
+constexpr int kMaxGroups = 1792;         // workgroups of the main kernel per batch sample, at most
+constexpr int kFinishPer = 28;           // workgroup slices each finishing lane adds
+static_assert(kMaxGroups <= kFinishPer * kWave, "the finish reads every slice in one step");
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row (DPP: swap
+// neighbours, swap pairs, mirror within 8, mirror within 16).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+struct CamGradArgs {
+  Problem p;
+  const float* grad;       // [B, C, X, Y]
+  double* work;            // [B, N, 12, gx] partial dL/dP per workgroup
+  float* gK;               // [B, N, 3, 3]
+  float* gR;               // [B, N, 3, 3]
+  float* gt;               // [B, N, 3]
+  int gx;                  // workgroups per batch sample
+  int tiles_y, groups, units;
+};
+
+// V = 4: lane chunk j holds channels 4j..4j+3 of the group (one 16-byte load
+// per tap); V = 1: channels j, j+16, j+32, j+48 (four 4-byte loads).
+template <int V>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void camera_grad_main(CamGradArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Problem& p = a.p;
+  double* sP = reinterpret_cast<double*>(smem);                                   // [N][12]
+  float* sG = reinterpret_cast<float*>(sP + 12 * p.N);                            // [kTileY][kGLd]
+  float* sW = sG + kTileY * kGLd;                                                 // [kWaves][kWave * kRedLd]
+  const int b = blockIdx.y;
+  for (int e = threadIdx.x; e < p.N * 12; e += kBlock) {
+    const int n = e / 12, r = (e % 12) >> 2, c = e & 3;
+    const size_t bn = (size_t)b * p.N + n;
+    double s = 0.0;
+    for (int k = 0; k < 3; ++k)
+      s = fma((double)p.K[bn * 9 + r * 3 + k], (double)(c < 3 ? p.R[bn * 9 + k * 3 + c] : p.t[bn * 3 + k]), s);
+    sP[e] = s;
+  }
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  float* wbuf = sW + wid * kWave * kRedLd;
+  int4* rec = reinterpret_cast<int4*>(wbuf);                                      // [64] taps of listed samples
+  float* dots = wbuf + 4 * kWave;                                                 // [64][4] tap dot products
+  const int tap = lane >> 4, j = lane & 15;
+
+  // phase-A lane role: camera ln, bin zl of each pass
+  const int zpc = kWave / p.N;
+  const int ln = lane / zpc, zl = lane - ln * zpc;
+  const bool lane_ok = lane < zpc * p.N;
+  uint64_t bin_lanes = 0;
+  for (int n = 0; n < p.N; ++n) bin_lanes |= 1ull << (n * zpc);
+  bin_lanes <<= zl;
+  const double* P = sP + (lane_ok ? ln : 0) * 12;
+  const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
+  const int HWC = p.H * p.W * p.C;
+  const float* fb = static_cast<const float*>(p.feat) + (size_t)b * p.N * HWC;
+  float acc[12];
+#pragma unroll
+  for (int k = 0; k < 12; ++k) acc[k] = 0.f;
+
+  // units dealt round-robin: neighbouring units run on different XCDs (keeping them on one XCD
+  // halves the HBM traffic but concentrates each XCD's workgroups on the same image rows, which
+  // measured slower)
+  for (int u = blockIdx.x; u < a.units; u += a.gx) {
+    const int grp = u % a.groups;
+    const int rest = u / a.groups;
+    const int ty = rest % a.tiles_y, x = rest / a.tiles_y;
+    const int c0 = grp * kCg;
+    const int Cg = min(kCg, p.C - c0);
+    // the tile's upstream gradient, all loads issued before the first is used (element 0 stands in
+    // for the ones outside the grid, whose values are then dropped)
+    float gv[kTileY * kCg / kBlock];
+#pragma unroll
+    for (int i = 0; i < kTileY * kCg / kBlock; ++i) {
+      const int e = threadIdx.x + i * kBlock;
+      const int c = e / kTileY, cell = e - c * kTileY;
+      const int y = ty * kTileY + cell;
+      const bool ok = c < Cg && y < p.Y;
+      gv[i] = a.grad[ok ? (((size_t)b * p.C + c0 + c) * p.X + x) * p.Y + y : 0];
+    }
+    __syncthreads();   // the camera table is staged; the previous unit's readers are done with sG
+#pragma unroll
+    for (int i = 0; i < kTileY * kCg / kBlock; ++i) {
+      const int e = threadIdx.x + i * kBlock;
+      const int c = e / kTileY, cell = e - c * kTileY;
+      sG[cell * kGLd + c] = (c < Cg && ty * kTileY + cell < p.Y) ? gv[i] : 0.f;
+    }
+    __syncthreads();
+    const double px = p.ox + ((double)x + 0.5) * p.dx;
+    const double hA0 = fma(P[0], px, P[3]), hA1 = fma(P[4], px, P[7]), hA2 = fma(P[8], px, P[11]);
+    for (int cell = wid; cell < kTileY; cell += kWaves) {
+      const int y = ty * kTileY + cell;
+      if (y >= p.Y) break;
+      const double py = p.oy + ((double)y + 0.5) * p.dy;
+      float g[4];
+      if (V == 4) {
+        const float4 gv = *reinterpret_cast<const float4*>(sG + cell * kGLd + 4 * j);
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[i] = sG[cell * kGLd + j + 16 * i];
+      }
+      for (int zc = 0; zc < p.Z; zc += zpc) {
+        // ---- validity of (bin zc + zl, camera ln) by sign tests on h
+        const int z = zc + zl;
+        const bool in_range = lane_ok && z < p.Z;
+        bool valid = false;
+        double pz = 0.0, h0 = 0.0, h1 = 0.0, h2 = 1.0;
+        if (in_range) {
+          pz = p.oz + ((double)z + 0.5) * p.dz;
+          h0 = fma(P[2], pz, fma(P[1], py, hA0));
+          h1 = fma(P[6], pz, fma(P[5], py, hA1));
+          h2 = fma(P[10], pz, fma(P[9], py, hA2));
+          valid = (h2 > 0.0) && (h0 >= 0.0) && (fma(Wm1, h2, -h0) >= 0.0) && (h1 >= 0.0) && (fma(Hm1, h2, -h1) >= 0.0);
+        }
+        const uint64_t m = __ballot(valid);
+        if (m == 0) continue;
+        const int ns = (int)__builtin_popcountll(m);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        float fa = 0.f, fbt = 0.f, rc = 0.f, ih = 0.f, uf = 0.f, vf = 0.f;
+        if (valid) {
+          const double r = recip(h2);
+          const double uu = h0 * r, vv = h1 * r;
+          const double fu = fmin(fmax(floor(uu), 0.0), Wm1);
+          const double fv = fmin(fmax(floor(vv), 0.0), Hm1);
+          const int x0 = (int)fu, y0 = (int)fv;
+          fa = (float)(uu - fu);
+          fbt = (float)(vv - fv);
+          rc = __builtin_amdgcn_rcpf((float)__builtin_popcountll(m & bin_lanes));
+          ih = (float)r;
+          uf = (float)uu;
+          vf = (float)vv;
+          rec[rank] = make_int4(ln * HWC + (y0 * p.W + x0) * p.C, (x0 + 1 < p.W) ? p.C : 0,
+                                (y0 + 1 < p.H) ? p.W * p.C : 0, 0);
+        }
+        wave_lds_sync();
+        // ---- tap dot products <g_cell, F_tap>, lanes = (tap, channel chunk)
+        // All loads of a step are issued before any is used: past the list's end the last sample
+        // is read again and channels past the group read channel c0, and both are dropped.
+        for (int s0 = 0; s0 < ns; s0 += kUnroll) {
+          float f[kUnroll][4];
+#pragma unroll
+          for (int i = 0; i < kUnroll; ++i) {
+            const int4 rr = rec[min(s0 + i, ns - 1)];
+            const int off = rr.x + ((tap & 1) ? rr.y : 0) + ((tap & 2) ? rr.z : 0) + c0;
+            if (V == 4) {
+              const float4 v = *reinterpret_cast<const float4*>(fb + off + ((4 * j < Cg) ? 4 * j : 0));
+              f[i][0] = v.x;
+              f[i][1] = v.y;
+              f[i][2] = v.z;
+              f[i][3] = v.w;
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const int c = j + 16 * k;
+                f[i][k] = fb[off + ((c < Cg) ? c : 0)];
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < kUnroll; ++i) {
+            float dot = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dot = fmaf(f[i][k], g[k], dot);   // g is 0 past the group's channels
+            const float sum = row_sum16(s0 + i < ns ? dot : 0.f);
+            if (j == 0 && s0 + i < ns) dots[(s0 + i) * 4 + tap] = sum;
+          }
+        }
+        wave_lds_sync();
+        // ---- dL/du, dL/dv of the lane's sample and its 12 entries of dL/dP
+        if (valid) {
+          const float4 dd = *reinterpret_cast<const float4*>(dots + rank * 4);
+          const float du = rc * ((1.f - fbt) * (dd.y - dd.x) + fbt * (dd.w - dd.z));
+          const float dv = rc * ((1.f - fa) * (dd.z - dd.x) + fa * (dd.w - dd.y));
+          const float al = du * ih, be = dv * ih, ga = -(du * uf + dv * vf) * ih;
+          const float pt[4] = {(float)px, (float)py, (float)pz, 1.f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[k] = fmaf(al, pt[k], acc[k]);
+            acc[4 + k] = fmaf(be, pt[k], acc[4 + k]);
+            acc[8 + k] = fmaf(ga, pt[k], acc[8 + k]);
+          }
+        }
+        wave_lds_sync();   // rec and dots are rewritten by the next pass
+      }
+    }
+  }
+  // ---- fixed-order sums: the lanes of each camera, then the four waves
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 12; ++k) wbuf[lane * kRedLd + k] = acc[k];
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.N * 12; e += kBlock) {
+    const int n = e / 12, k = e - n * 12;
+    double s = 0.0;
+    for (int w = 0; w < kWaves; ++w)
+      for (int i = 0; i < zpc; ++i) s += (double)sW[w * kWave * kRedLd + (n * zpc + i) * kRedLd + k];
+    a.work[((size_t)b * p.N * 12 + e) * a.gx + blockIdx.x] = s;
+  }
+}
+
+// One workgroup per (camera, batch sample), one wave per entry of dL/dP: the
+// entry is the sum of the workgroup slices (each lane a fixed strided subset,
+// all loads in flight at once, then a fixed tree); then dL/dK = dL/dP [R | t]^T
+// and dL/d[R | t] = K^T dL/dP.
+__global__ __launch_bounds__(12 * kWave) void camera_grad_finish(CamGradArgs a) {
+  __shared__ double sGP[12];
+  const Problem& p = a.p;
+  const int n = blockIdx.x, b = blockIdx.y;
+  const size_t bn = (size_t)b * p.N + n;
+  const int lane = threadIdx.x & (kWave - 1), e = threadIdx.x / kWave;
+  const double* src = a.work + (bn * 12 + e) * a.gx;
+  double v[kFinishPer];
+#pragma unroll
+  for (int k = 0; k < kFinishPer; ++k) {
+    const int i = lane + k * kWave;
+    v[k] = (i < a.gx) ? src[i] : 0.0;
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kFinishPer; ++k) s += v[k];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) sGP[e] = s;
+  __syncthreads();
+  if (threadIdx.x >= 21) return;
+  const int r = threadIdx.x;
+  const double* G = sGP;                          // dL/dP, row-major 3 x 4
+  const float* K = p.K + bn * 9;
+  const float* R = p.R + bn * 9;
+  const float* t = p.t + bn * 3;
+  if (r < 9) {                                    // dL/dK_ik = sum_j dL/dP_ij M_kj, M = [R | t]
+    const int ii = r / 3, k = r % 3;
+    double w = G[ii * 4 + 3] * (double)t[k];
+    for (int jj = 0; jj < 3; ++jj) w = fma(G[ii * 4 + jj], (double)R[k * 3 + jj], w);
+    a.gK[bn * 9 + r] = (float)w;
+  } else {                                        // dL/dM_ij = sum_k K_ki dL/dP_kj
+    const int q = r - 9;
+    const int ii = (q < 9) ? q / 3 : q - 9, jj = (q < 9) ? q % 3 : 3;
+    double w = 0.0;
+    for (int k = 0; k < 3; ++k) w = fma((double)K[k * 3 + ii], G[k * 4 + jj], w);
+    if (q < 9) a.gR[bn * 9 + q] = (float)w;
+    else a.gt[bn * 3 + (q - 9)] = (float)w;
+  }
+}
+
+// Workgroups per batch sample: about one resident round of the chip in total
+// (six or seven per CU), at least one so that the main kernel always writes
+// the slices the finish reads.
+int workgroups_per_sample(const Problem& p, int units) {
+  const int cap = (p.B > 0 && kMaxGroups / p.B > 64) ? kMaxGroups / p.B : 64;
+  return units < 1 ? 1 : (units < cap ? units : cap);
+}
+
+size_t work_bytes(const Problem& p, int gx) { return sizeof(double) * (size_t)p.B * p.N * 12 * (size_t)gx; }
+
+void unit_counts(const Problem& p, int& tiles_y, int& groups, int& units) {
+  tiles_y = (p.Y + kTileY - 1) / kTileY;
+  groups = (p.C + kCg - 1) / kCg;
+  const long long u = (p.Z > 0 && p.N > 0) ? (long long)p.X * tiles_y * groups : 0;
+  units = (int)u;
+}
+
+}  // namespace
+
+size_t camera_grad_workspace_bytes(const Problem& p) {
+  if (p.B == 0 || p.N == 0) return 0;
+  int tiles_y, groups, units;
+  unit_counts(p, tiles_y, groups, units);
+  return work_bytes(p, workgroups_per_sample(p, units));
+}
+
+hipError_t launch_camera_backward(const Problem& p, const float* grad_out, float* gK, float* gR, float* gt,
+                                  void* work, hipStream_t stream) {
+  if (p.B == 0 || p.N == 0) return hipSuccess;
+  CamGradArgs a;
+  a.p = p;
+  a.grad = grad_out;
+  a.gK = gK;
+  a.gR = gR;
+  a.gt = gt;
+  unit_counts(p, a.tiles_y, a.groups, a.units);
+  a.gx = workgroups_per_sample(p, a.units);
+  a.work = static_cast<double*>(work);
+  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kTileY * kGLd +
+                       sizeof(float) * kWaves * kWave * kRedLd;
+  const dim3 grid((unsigned)a.gx, (unsigned)p.B);
+  if (p.C % 4 == 0 && (reinterpret_cast<uintptr_t>(p.feat) & 15) == 0)
+    hipLaunchKernelGGL(camera_grad_main<4>, grid, dim3(kBlock), shmem, stream, a);
+  else
+    hipLaunchKernelGGL(camera_grad_main<1>, grid, dim3(kBlock), shmem, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(camera_grad_finish, dim3((unsigned)p.N, (unsigned)p.B), dim3(12 * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fbev

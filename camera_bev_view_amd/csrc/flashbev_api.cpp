@@ -164,6 +164,67 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
                        "fbev_backward launch");
 }
 
+// Camera gradients: geometry checks of the single-level forward, fp32 features.
+fbev_status check_cameras(const fbev_feat_desc& fd, int32_t X, int32_t Y, int32_t Z, fbev::Problem& p) {
+  const fbev_range unit{0.f, 1.f, 0.f, 1.f, 0.f, 1.f};
+  static const float dummy = 0.f;
+  fbev_status s = check_common(fd, &dummy, &dummy, &dummy, unit, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  s = check_levels(fd, 1, nullptr, p);
+  if (s != FBEV_OK) return s;
+  const int64_t batch_elems = (int64_t)fd.N * fd.H * fd.W * fd.C;
+  if (batch_elems >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld elements (limit 2^31 - 1)",
+                (long long)batch_elems);
+  const int64_t units = (int64_t)X * ((Y + 15) / 16) * ((fd.C + 63) / 64);
+  if (units >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "%lld work units (x-rows x 16-cell tiles x 64-channel groups), limit 2^31 - 1",
+                (long long)units);
+  p.elem_bytes = 4;
+  p.vec_bytes = 4;
+  return FBEV_OK;
+}
+
+fbev_status cameras_workspace_impl(fbev_feat_desc fd, int32_t X, int32_t Y, int32_t Z, size_t* bytes) {
+  if (bytes == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  fbev::Problem p{};
+  const fbev_status s = check_cameras(fd, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  *bytes = fbev::camera_grad_workspace_bytes(p);
+  return FBEV_OK;
+}
+
+fbev_status backward_cameras_impl(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                  const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                                  int32_t Z, float* grad_K, float* grad_R, float* grad_t, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  fbev::Problem p{};
+  fbev_status s = check_cameras(fd, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
+  if (s != FBEV_OK) return s;
+  const int64_t n_cam = (int64_t)fd.B * fd.N;
+  if (n_cam == 0) return FBEV_OK;
+  if (grad_K == nullptr || grad_R == nullptr || grad_t == nullptr)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_K, grad_R and grad_t must be non-NULL when B*N > 0");
+  const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
+  const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  if (n_feat > 0 && features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "features is NULL");
+  if (n_out > 0 && grad_out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(features);
+  if (n_feat > 0 && (addr & 3) != 0) return fail(FBEV_ERR_UNSUPPORTED, "features must be 4-byte aligned");
+  const size_t need = fbev::camera_grad_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "workspace must be 8-byte aligned");
+  p.feat = features;
+  return device_status(fbev::launch_camera_backward(p, grad_out, grad_K, grad_R, grad_t, workspace,
+                                                    static_cast<hipStream_t>(stream)),
+                       "fbev_backward_cameras launch");
+}
+
 
 // Lift-Splat arguments: depth [B,N,H,W,D] and context [B,N,H,W,C], the depth
 // bins, the rig and the x-y extent of the BEV grid (its z fields are unused:
@@ -372,6 +433,18 @@ fbev_status fbev_forward_levels(const void* features, fbev_dtype dtype, fbev_fea
                                 fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* out, uint8_t* counts,
                                 void* stream) {
   return forward_impl(features, dtype, fd, L, ratios, K, R, t, bev_range, X, Y, Z, out, counts, stream);
+}
+
+fbev_status fbev_backward_cameras_workspace(fbev_feat_desc fd, int32_t X, int32_t Y, int32_t Z, size_t* bytes) {
+  return cameras_workspace_impl(fd, X, Y, Z, bytes);
+}
+
+fbev_status fbev_backward_cameras(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                  const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                                  int32_t Z, float* grad_K, float* grad_R, float* grad_t, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return backward_cameras_impl(grad_out, features, fd, K, R, t, bev_range, X, Y, Z, grad_K, grad_R, grad_t, workspace,
+                               workspace_bytes, stream);
 }
 
 fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios,

@@ -29,4 +29,10 @@ struct Problem {
 hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream);
 hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream);
 
+// Camera gradients (single level, fp32 features): dL/dK, dL/dR [B,N,3,3] and
+// dL/dt [B,N,3], fully overwritten; `work` holds camera_grad_workspace_bytes(p).
+size_t camera_grad_workspace_bytes(const Problem& p);
+hipError_t launch_camera_backward(const Problem& p, const float* grad_out, float* gK, float* gR, float* gt, void* work,
+                                  hipStream_t stream);
+
 }  // namespace fbev

@@ -7,6 +7,7 @@ on an H x W map; a BEV grid of X x Y cells and Z height bins.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence, Tuple
 
 import torch
@@ -76,22 +77,57 @@ def backward(grad_out: torch.Tensor, feat_shape: Sequence[int], K: torch.Tensor,
     return gF
 
 
+def camera_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Tensor, R: torch.Tensor,
+                    t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, Z: int,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """fbev_backward_cameras: (dL/dK [B,N,3,3], dL/dR [B,N,3,3], dL/dt [B,N,3]) of L = <grad_out, out>
+    for fp32 channels-last features [B,N,H,W,C].  ``workspace`` (a uint8 device tensor) is allocated when
+    not given or too small."""
+    if features.dim() != 5 or features.dtype != torch.float32 or not features.is_cuda or not features.is_contiguous():
+        raise ValueError("features must be a contiguous float32 device tensor [B,N,H,W,C]")
+    B, N, H, W, C = features.shape
+    dev = features.device
+    if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32 [B,C,X,Y]")
+    grad_out = grad_out.contiguous()
+    _check_cams(K, R, t, B, N, dev)
+    lib = _lib.load()
+    fd = _lib.feat_desc(B, N, C, H, W)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.fbev_backward_cameras_workspace(fd, X, Y, Z, ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=dev)
+    gK = torch.empty((B, N, 3, 3), dtype=torch.float32, device=dev)
+    gR = torch.empty((B, N, 3, 3), dtype=torch.float32, device=dev)
+    gt = torch.empty((B, N, 3), dtype=torch.float32, device=dev)
+    _lib.check(lib.fbev_backward_cameras(_ptr(grad_out), _ptr(features), fd, _ptr(K), _ptr(R), _ptr(t),
+                                         _lib.bev_range(bev_range), X, Y, Z, _ptr(gK), _ptr(gR), _ptr(gt),
+                                         _ptr(workspace), workspace.numel(), _stream(dev)))
+    return gK, gR, gt
+
+
 class SamplingVT(torch.autograd.Function):
-    """Autograd wrapper: gradient with respect to the features only."""
+    """Autograd wrapper: gradients with respect to the features and, for fp32 features, the cameras."""
 
     @staticmethod
     def forward(ctx, features, K, R, t, bev_range, X, Y, Z):
         out, _ = forward(features, K, R, t, bev_range, X, Y, Z)
-        ctx.save_for_backward(K, R, t)
+        ctx.save_for_backward(features, K, R, t)
         ctx.meta = (tuple(features.shape), features.dtype, tuple(bev_range), X, Y, Z)
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
-        K, R, t = ctx.saved_tensors
+        features, K, R, t = ctx.saved_tensors
         shape, dtype, rng, X, Y, Z = ctx.meta
-        gF = backward(grad_out.float(), shape, K, R, t, rng, X, Y, Z)
-        return gF.to(dtype), None, None, None, None, None, None, None
+        g = grad_out.float().contiguous()
+        gF = backward(g, shape, K, R, t, rng, X, Y, Z).to(dtype) if ctx.needs_input_grad[0] else None
+        gK = gR = gt = None
+        if any(ctx.needs_input_grad[1:4]):
+            if dtype != torch.float32:
+                raise NotImplementedError("camera gradients need float32 features")
+            gK, gR, gt = camera_backward(g, features, K, R, t, rng, X, Y, Z)
+        return gF, gK, gR, gt, None, None, None, None
 
 
 def bev_sample(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor,

@@ -39,13 +39,14 @@
 #ifndef FLASHBEV_H
 #define FLASHBEV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 4
+#define FBEV_ABI_VERSION 5
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
@@ -111,6 +112,43 @@ fbev_status fbev_forward(const void* features, fbev_dtype dtype, fbev_feat_desc 
 fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,
                           const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z,
                           float* grad_features, void* stream);
+
+/*
+ * Gradients of fbev_forward's output with respect to the cameras.  The
+ * SparseDriveV2 notes ("Deformable Aggregation", pitfalls) ask for a
+ * projection-and-sampling chain that gradients flow through; for
+ * L = <grad_out, out> this returns dL/dK, dL/dR and dL/dt with the validity
+ * mask and the camera counts held fixed (they are piecewise constant in the
+ * cameras).  Per in-view sample of camera n at voxel centre p, with
+ * h = K (R p + t), u = h_1 / h_3 and v = h_2 / h_3:
+ *
+ *   dL/du = <grad_out[b,:,cell], d sample / du> / count   (likewise v; inside
+ *           the pixel square floor() picks, the sample is bilinear in u, v),
+ *   dL/dP += [dL/du; dL/dv; -(u dL/du + v dL/dv)] [p; 1]^T / h_3,  P = K [R | t],
+ *   dL/dK = dL/dP [R | t]^T,   [dL/dR | dL/dt] = K^T dL/dP.
+ *
+ * Every entry of K, R and t gets its partial derivative (R is not constrained
+ * to a rotation).
+ *
+ *   grad_out   : [B,C,X,Y] fp32, device, read only.
+ *   features   : [B,N,H,W,C] fp32, device, read only (4-byte aligned;
+ *                16-byte alignment with C a multiple of 4 takes the wide path).
+ *   grad_K, grad_R : [B,N,3,3] fp32, device; fully overwritten.
+ *   grad_t     : [B,N,3] fp32, device; fully overwritten.
+ *   workspace  : device scratch of at least the size that
+ *                fbev_backward_cameras_workspace() reports for these sizes
+ *                (may be NULL when that is 0); its contents are not needed
+ *                before or after the call.  Calls that share a workspace must
+ *                not overlap.
+ * Other arguments as for fbev_forward; features are fp32 only.  A workspace
+ * smaller than required gives FBEV_ERR_INVALID_ARGUMENT.  The result is deterministic: partial sums per workgroup are added in a
+ * fixed order in fp64.  Zero sizes give zero (or empty) gradients.
+ */
+fbev_status fbev_backward_cameras_workspace(fbev_feat_desc fd, int32_t X, int32_t Y, int32_t Z, size_t* bytes);
+fbev_status fbev_backward_cameras(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
+                                  const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                                  int32_t Z, float* grad_K, float* grad_R, float* grad_t, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Multi-level (feature-pyramid) variants.  The pages name a multi-scale fused

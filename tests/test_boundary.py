@@ -264,3 +264,54 @@ def test_deform_empty_problems_return_ok_without_device_work(lib):
     assert dfwd(lib, desc=(1, 6, 0, 16, 44), out=None) == 0
     assert dbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, feat=None, A=None, D=None, Wt=None, gF=None, gW=None,
                 gO=None) == 0
+
+
+def cbwd(lib, grad=FAKE, feat=FAKE, desc=(1, 6, 64, 16, 44), K=FAKE, rng=RNG, X=200, Y=200, Z=8, gK=FAKE, gR=FAKE,
+         gt=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.fbev_backward_cameras(grad, feat, _lib.feat_desc(*desc), K, FAKE, FAKE, _lib.bev_range(rng), X, Y, Z,
+                                     gK, gR, gt, ws, ws_bytes, None)
+
+
+def cam_workspace(lib, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8):
+    n = ctypes.c_size_t(12345)
+    st = lib.fbev_backward_cameras_workspace(_lib.feat_desc(*desc), X, Y, Z, ctypes.byref(n))
+    return st, n.value
+
+
+def test_camera_workspace_size(lib):
+    st, n = cam_workspace(lib)
+    # fp64 dL/dP slices, 12 per camera and workgroup
+    assert st == 0 and n > 0 and n % (8 * 6 * 12) == 0
+    st0, n0 = cam_workspace(lib, Z=0)
+    assert st0 == 0 and 0 < n0 < n
+    assert cam_workspace(lib, desc=(1, 6, 0, 16, 44)) == (0, n0)
+    assert cam_workspace(lib, desc=(0, 6, 64, 16, 44)) == (0, 0)
+    assert cam_workspace(lib, desc=(1, 0, 64, 16, 44)) == (0, 0)
+    assert cam_workspace(lib, X=-1)[0] == 1
+    assert lib.fbev_backward_cameras_workspace(_lib.feat_desc(1, 6, 64, 16, 44), 200, 200, 8, None) == 1
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(desc=(1, 6, -1, 16, 44)), 1, "negative feature size"),
+    (dict(Z=-1), 1, "negative grid size"),
+    (dict(desc=(1, 65, 64, 16, 44)), 1, "exceeds FBEV_MAX_CAMERAS"),
+    (dict(rng=(1.0, 1.0, -50.0, 50.0, -5.0, 3.0)), 1, "finite min < max"),
+    (dict(K=None), 1, "K, R and t"),
+    (dict(gK=None), 1, "grad_K, grad_R and grad_t"),
+    (dict(gt=None), 1, "grad_K, grad_R and grad_t"),
+    (dict(feat=None), 1, "features is NULL"),
+    (dict(grad=None), 1, "grad_out is NULL"),
+    (dict(feat=FAKE + 2), 2, "4-byte aligned"),
+    (dict(ws=None), 1, "workspace"),
+    (dict(ws_bytes=100), 1, "workspace"),
+    (dict(ws=FAKE + 4), 1, "8-byte aligned"),
+    (dict(desc=(1, 64, 4096, 128, 128)), 2, "limit 2^31"),
+])
+def test_camera_backward_validation(lib, kwargs, status, msg):
+    assert cbwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+def test_camera_empty_problems_return_ok_without_device_work(lib):
+    assert cbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, feat=None, K=None, gK=None, gR=None, gt=None, ws=None) == 0
+    assert cbwd(lib, desc=(1, 0, 64, 16, 44), K=None, gK=None, gR=None, gt=None, ws=None) == 0

@@ -1,0 +1,154 @@
+"""GPU: camera gradients of the Sampling-VT (fbev_backward_cameras) against the
+fp64 oracle (oracle.camera_grad).
+
+Parity rule: dL/dK, dL/dR and dL/dt each within 1e-3 relative L2 of the
+oracle, on an upstream gradient that is zero on every cell with a sample
+within 1e-4 px of an image edge (a rounding flip of the in-view test there
+changes which samples count; both sides get the same masked gradient).
+Every case prints its label before the GPU work starts.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.camera_grad as cg
+from camera_bev_view_amd import ops
+from camera_bev_view_amd import workloads as wl
+from gpu_helpers import BWD_REL_L2, rel_l2, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def camera_parity(inp, label, rows=None):
+    B, N, C, H, W = inp.F.shape
+    X, Y, Z = inp.X, inp.Y, inp.Z
+    say(f"[case] cameras {label}: B,N,C={B},{N},{C} HxW={H}x{W} grid {X}x{Y}x{Z}"
+        + (f" rows {len(rows)}" if rows is not None else ""))
+    G = np.array(inp.grad_out, np.float32, copy=True)
+    if rows is not None:
+        keep = np.zeros(X, bool)
+        keep[rows] = True
+        G[:, :, ~keep] = 0.0
+    probe = cg.oracle_camera_backward(np.zeros_like(G), inp.F[:, :, :0], inp.K, inp.R, inp.t, inp.rng6, X, Y, Z,
+                                      rows=rows)
+    G[np.broadcast_to(probe["near_edge"][:, None], G.shape)] = 0.0
+    ref = cg.oracle_camera_backward(G, inp.F, inp.K, inp.R, inp.t, inp.rng6, X, Y, Z, rows=rows)
+    F, K, R, t = to_device(inp)
+    gK, gR, gt = ops.camera_backward(torch.from_numpy(G).cuda(), F, K, R, t, inp.rng6, X, Y, Z)
+    torch.cuda.synchronize()
+    got = {"K": gK.cpu().numpy(), "R": gR.cpu().numpy(), "t": gt.cpu().numpy()}
+    errs = {n: rel_l2(got[n], ref[n]) for n in ("K", "R", "t")}
+    say(f"[parity] cameras {label}: rel L2 K {errs['K']:.3e} R {errs['R']:.3e} t {errs['t']:.3e}, "
+        f"excluded cells {int(probe['near_edge'].sum())}")
+    for n in ("K", "R", "t"):
+        if np.linalg.norm(ref[n]) > 0:
+            assert errs[n] <= BWD_REL_L2, f"{label}: dL/d{n} rel L2 {errs[n]:.3e}"
+        else:
+            assert not got[n].any(), f"{label}: dL/d{n} should be zero"
+    return got, ref
+
+
+def test_tiny_full():
+    camera_parity(wl.make_inputs("tiny", with_grad=True), "tiny")
+
+
+def test_nuscenes_full():
+    camera_parity(wl.make_inputs("nuscenes", with_grad=True), "nuScenes-shaped")
+
+
+def test_batched_sampled_rows():
+    inp = wl.make_inputs("batched", dtype="f32", with_grad=True)
+    camera_parity(inp, "batched fp32", rows=np.arange(3, 200, 17))
+
+
+CAMERA_CASES = [
+    # label, B, N, C, H, W, X, Y, Z
+    ("ragged channels, scalar lanes, two groups", 2, 6, 70, 8, 22, 23, 37, 5),
+    ("five channel groups", 1, 6, 300, 6, 14, 11, 19, 3),
+    ("three passes of bins", 1, 6, 12, 8, 22, 20, 21, 24),
+    ("one camera", 2, 1, 8, 8, 22, 30, 17, 6),
+    ("64 cameras, one bin per pass", 1, 64, 16, 4, 8, 9, 33, 3),
+    ("one channel", 1, 6, 1, 16, 44, 25, 25, 4),
+]
+
+
+@pytest.mark.parametrize("case", CAMERA_CASES, ids=[c[0] for c in CAMERA_CASES])
+def test_camera_cases(case):
+    label, B, N, C, H, W, X, Y, Z = case
+    inp = wl.random_case(len(label) + 50, B, N, C, H, W, X, Y, Z, rng6=(-30.0, 30.0, -30.0, 30.0, -4.0, 3.0))
+    camera_parity(inp, label)
+
+
+def test_pitched_rig():
+    inp = wl.random_case(77, 1, 6, 32, 16, 44, 40, 40, 8)
+    inp.K, inp.R, inp.t = wl.make_rig(1077, 1, 6, 16, 44, True, pitch_deg=-7.0)
+    camera_parity(inp, "pitched rig")
+
+
+def test_deterministic_and_workspace_reuse():
+    inp = wl.make_inputs("tiny", with_grad=True)
+    say("[case] cameras determinism")
+    F, K, R, t = to_device(inp)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    ws = torch.full((1 << 20,), 255, dtype=torch.uint8, device="cuda")
+    a = ops.camera_backward(g, F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, workspace=ws)
+    b = ops.camera_backward(g, F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z, workspace=ws)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_constant_features_give_zero():
+    inp = wl.make_inputs("tiny", with_grad=True)
+    say("[case] cameras constant features")
+    inp.F[:] = 3.0
+    F, K, R, t = to_device(inp)
+    gK, gR, gt = ops.camera_backward(torch.from_numpy(inp.grad_out).cuda(), F, K, R, t, inp.rng6, inp.X, inp.Y,
+                                     inp.Z)
+    torch.cuda.synchronize()
+    for x in (gK, gR, gt):
+        assert not x.any()
+
+
+def test_autograd_matches():
+    inp = wl.make_inputs("tiny", with_grad=True)
+    say("[case] cameras autograd")
+    F, K, R, t = to_device(inp)
+    K.requires_grad_(True)
+    R.requires_grad_(True)
+    t.requires_grad_(True)
+    F.requires_grad_(True)
+    out = ops.bev_sample(F, K, R, t, inp.rng6, inp.X, inp.Y, inp.Z)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    gF, gK, gR, gt = torch.autograd.grad(out, (F, K, R, t), g)
+    eK, eR, et = ops.camera_backward(g, F.detach(), K.detach(), R.detach(), t.detach(), inp.rng6, inp.X, inp.Y,
+                                     inp.Z)
+    torch.cuda.synchronize()
+    assert torch.equal(gK, eK) and torch.equal(gR, eR) and torch.equal(gt, et)
+    assert gF.shape == F.shape
+
+
+def test_degenerate_sizes():
+    say("[case] cameras degenerate sizes")
+    inp = wl.random_case(9, 1, 6, 8, 8, 22, 10, 10, 3)
+    F, K, R, t = to_device(inp)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    # Z = 0 and C = 0: zero gradients, fully written
+    gK, gR, gt = ops.camera_backward(g, F, K, R, t, inp.rng6, 10, 10, 0)
+    Fc = torch.empty((1, 6, 8, 22, 0), device="cuda")
+    cK, cR, ct = ops.camera_backward(torch.empty((1, 0, 10, 10), device="cuda"), Fc, K, R, t, inp.rng6, 10, 10, 3)
+    # N = 0: empty gradients
+    F0 = torch.empty((1, 0, 8, 22, 8), device="cuda")
+    e = torch.empty((1, 0, 3, 3), device="cuda")
+    nK, nR, nt = ops.camera_backward(g, F0, e, e.clone(), torch.empty((1, 0, 3), device="cuda"), inp.rng6, 10, 10, 3)
+    torch.cuda.synchronize()
+    for x in (gK, gR, gt, cK, cR, ct):
+        assert not x.any()
+    assert nK.numel() == 0 and nR.numel() == 0 and nt.numel() == 0
