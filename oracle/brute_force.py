@@ -205,3 +205,22 @@ def deform_brute(F, K, R, t, anchors, offsets, weights, b: int, q: int) -> List[
             for c in range(C):
                 acc[c] += w * _sample(F[b][n][c], H, W, u, v)
     return acc
+
+
+def align_brute(prev_b, A_b, rng6: Sequence[float], X: int, Y: int, c: int, i: int, j: int) -> float:
+    """One element of the aligned previous BEV map: current cell (i, j) mapped into the previous
+    ego frame by the planar affine A_b (2 x 3), then bilinear on the previous grid's cell centres,
+    0 outside the closed box of centres.  ``prev_b`` is indexed [c][i][j]."""
+    x = _centre(rng6[0], rng6[1], X, i)
+    y = _centre(rng6[2], rng6[3], Y, j)
+    xp = A_b[0][0] * x + A_b[0][1] * y + A_b[0][2]
+    yp = A_b[1][0] * x + A_b[1][1] * y + A_b[1][2]
+    si = (xp - rng6[0]) / ((rng6[1] - rng6[0]) / X) - 0.5
+    sj = (yp - rng6[2]) / ((rng6[3] - rng6[2]) / Y) - 0.5
+    if not (0.0 <= si <= X - 1 and 0.0 <= sj <= Y - 1):
+        return 0.0
+    i0, j0 = int(math.floor(si)), int(math.floor(sj))
+    a, bb = si - i0, sj - j0
+    i1, j1 = min(i0 + 1, X - 1), min(j0 + 1, Y - 1)
+    p = prev_b[c]
+    return ((1 - a) * (1 - bb) * p[i0][j0] + (1 - a) * bb * p[i0][j1] + a * (1 - bb) * p[i1][j0] + a * bb * p[i1][j1])
