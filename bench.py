@@ -24,7 +24,9 @@ deform / deform_bev (Deformable Aggregation: fbev_deform_forward +
 fbev_deform_backward for 900 sparse queries x 13 keypoints, or one query per
 cell of a 200 x 200 grid x 8 keypoints), or cameras (the gradients of the
 Sampling-VT output with respect to K, R and t, fbev_backward_cameras, on the
-nuScenes-shaped workload).
+nuScenes-shaped workload), or temporal (fbev_forward_temporal +
+fbev_backward_temporal: the nuScenes-shaped transform stacked with a 64-channel
+previous BEV map resampled under a seeded ego motion).
 """
 from __future__ import annotations
 
@@ -495,6 +497,125 @@ def main_cameras(args):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_temporal(ti, min_seconds=10.0):
+    """Time the fp64 temporal oracle (forward + backward) over the whole grid until ``min_seconds`` have passed."""
+    import oracle.temporal as tp
+    cur = ti.cur
+    B, N, C, H, W = cur.F.shape
+    reps = 0
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    while True:
+        tp.temporal_forward(cur.F, cur.K, cur.R, cur.t, cur.rng6, cur.X, cur.Y, cur.Z, ti.prev, ti.ego)
+        tp.temporal_backward(ti.grad_out, cur.K, cur.R, cur.t, cur.rng6, cur.X, cur.Y, cur.Z, H, W, C, ti.ego)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds:
+            break
+    cpu = time.process_time() - c0
+    Cp = ti.prev.shape[1]
+    return {
+        "value": reps * B * (C + Cp) * cur.X * cur.Y / wall,
+        "unit": "BEV output elems/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy temporal oracle (Sampling-VT + resampled previous map), {reps} forward + backward "
+                  f"passes over the whole {cur.X}x{cur.Y} grid, wall {wall:.2f} s, process CPU {cpu:.2f} s, "
+                  f"{len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def main_temporal(args):
+    """Temporal fused transform: one step = fbev_forward_temporal + fbev_backward_temporal on one batch."""
+    import numpy as np
+    import torch
+    from camera_bev_view_amd import ops
+    from camera_bev_view_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ti = wl.make_temporal_inputs(args.workload)
+    cur = ti.cur
+    B, N, C, H, W = cur.F.shape
+    X, Y, Z = cur.X, cur.Y, cur.Z
+    Cp = ti.prev.shape[1]
+    F = to_dev(cur.F.transpose(0, 1, 3, 4, 2))
+    K, R, t = (to_dev(a) for a in (cur.K, cur.R, cur.t))
+    prev, ego, g = to_dev(ti.prev), to_dev(ti.ego), to_dev(ti.grad_out)
+    out = torch.empty((B, C + Cp, X, Y), dtype=torch.float32, device=dev)
+    fwd_call = lambda: ops.forward_temporal(F, K, R, t, cur.rng6, X, Y, Z, prev, ego, out=out)
+    bwd_call = lambda: ops.backward_temporal(g, (B, N, H, W, C), K, R, t, cur.rng6, X, Y, Z, Cp, ego)
+
+    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
+    for _ in range(args.warmup):
+        fwd_call()
+        bwd_call()
+    torch.cuda.synchronize()
+    calibration_copy(args, dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd_call()
+        ev[k][1].record(stream)
+        bwd_call()
+        ev[k][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
+
+    out_elems = B * (C + Cp) * X * Y
+    cams = B * N * 21 * 4 + B * 6 * 4
+    feat_bytes = B * N * H * W * C * 4
+    fwd_bytes = feat_bytes + B * Cp * X * Y * 4 + out_elems * 4 + cams       # features, previous map, output
+    bwd_bytes = out_elems * 4 + feat_bytes + B * Cp * X * Y * 4 + cams       # upstream gradient, dL/dF, dL/dprev
+
+    def rates(ms, nbytes):
+        s_ = ms * 1e-3
+        return {"ms": ms, "out_elems_per_s": out_elems / s_, "algorithmic_bytes": nbytes,
+                "hbm_gbps_algorithmic": nbytes / s_ / 1e9, "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
+
+    fwd = rates(fwd_ms, fwd_bytes)
+    bwd = rates(bwd_ms, bwd_bytes)
+    dom_k, dom, dom_bytes = (["sampling_vt_fwd", "bev_align_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        (["fill_zero_f32", "sampling_vt_bwd", "bev_align_bwd"], bwd, bwd_bytes)
+    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
+    line = {
+        "metric": METRIC,
+        "value": out_elems / (ms_step * 1e-3),
+        "unit": "BEV output elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
+                "seeded planar ego motion",
+        "config": {"workload": f"{args.workload}: Sampling-VT B={B} N={N} C={C} HxW={H}x{W} grid {X}x{Y}x{Z} "
+                               f"stacked with a Cp={Cp} previous BEV map resampled under the ego motion, one step = "
+                               f"forward + backward", "B": B, "N": N, "C": C, "Cp": Cp, "H": H, "W": W, "X": X, "Y": Y,
+                   "Z": Z},
+        "forward": fwd,
+        "backward": bwd,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline_temporal(ti)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -524,6 +645,8 @@ def main():
         return main_deform(args)
     if args.workload == "cameras":
         return main_cameras(args)
+    if args.workload in wl.TEMPORAL_WORKLOADS:
+        return main_temporal(args)
     dev = torch.device("cuda:0")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if args.workload in wl.PYRAMIDS:

@@ -19,12 +19,13 @@ FBEV_DTYPE_F32 = 0
 FBEV_DTYPE_BF16 = 1
 FBEV_MAX_CAMERAS = 64
 FBEV_MAX_LEVELS = 4
-ABI_VERSION = 5
+ABI_VERSION = 6
 FBEV_MAX_KEYPOINTS = 256
 
 EXPORTED = ("fbev_forward", "fbev_backward", "fbev_forward_levels", "fbev_backward_levels", "fbev_lss_forward",
             "fbev_lss_backward", "fbev_deform_forward", "fbev_deform_backward", "fbev_backward_cameras_workspace",
-            "fbev_backward_cameras", "fbev_status_string", "fbev_last_error", "fbev_abi_version")
+            "fbev_backward_cameras", "fbev_forward_temporal", "fbev_backward_temporal", "fbev_status_string",
+            "fbev_last_error", "fbev_abi_version")
 
 
 class FeatDesc(ctypes.Structure):
@@ -87,6 +88,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fbev_backward_cameras.argtypes = [f32p, f32p, FeatDesc, f32p, f32p, f32p, BevRange, i32, i32, i32, f32p,
                                               f32p, f32p, vp, ctypes.c_size_t, vp]
         lib.fbev_backward_cameras.restype = ctypes.c_int
+        lib.fbev_forward_temporal.argtypes = [vp, ctypes.c_int, FeatDesc, f32p, f32p, f32p, BevRange, i32, i32, i32,
+                                              f32p, i32, f32p, f32p, vp, vp]
+        lib.fbev_forward_temporal.restype = ctypes.c_int
+        lib.fbev_backward_temporal.argtypes = [f32p, FeatDesc, f32p, f32p, f32p, BevRange, i32, i32, i32, i32, f32p,
+                                               f32p, f32p, vp]
+        lib.fbev_backward_temporal.restype = ctypes.c_int
         lib.fbev_status_string.argtypes = [ctypes.c_int]
         lib.fbev_status_string.restype = ctypes.c_char_p
         lib.fbev_last_error.argtypes = []

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflashbev.so")
 SOURCES = [os.path.join(CSRC, "flashbev_api.cpp"), os.path.join(CSRC, "sampling_vt.hip"),
            os.path.join(CSRC, "lift_splat.hip"), os.path.join(CSRC, "deform_agg.hip"),
-           os.path.join(CSRC, "camera_grad.hip")]
+           os.path.join(CSRC, "camera_grad.hip"), os.path.join(CSRC, "temporal.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code.

@@ -68,6 +68,7 @@ fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* 
   p.dy = ((double)r.y_max - (double)r.y_min) / (Y > 0 ? Y : 1);
   p.oz = (double)r.z_min;
   p.dz = ((double)r.z_max - (double)r.z_min) / (Z > 0 ? Z : 1);
+  p.out_ch = fd.C;
   return FBEV_OK;
 }
 
@@ -108,22 +109,41 @@ fbev_status device_status(hipError_t e, const char* what) {
   return fail(FBEV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Temporal fusion arguments: Cp channels of the previous BEV map and the planar
+// ego motion [B, 2, 3]; both pointers may be NULL when nothing would read them.
+fbev_status check_temporal(const fbev_feat_desc& fd, int32_t X, int32_t Y, int32_t Cp, const void* prev,
+                           const float* ego, const char* prev_name) {
+  if (Cp < 0) return fail(FBEV_ERR_INVALID_ARGUMENT, "negative Cp=%d previous-map channels", Cp);
+  const int64_t n_prev = (int64_t)fd.B * Cp * X * Y;
+  if (n_prev > 0 && prev == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "%s is NULL", prev_name);
+  if (n_prev > 0 && ego == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "ego is NULL");
+  if ((int64_t)X * Y >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "X*Y = %lld cells (limit 2^31 - 1)", (long long)X * Y);
+  if ((int64_t)fd.C + Cp > INT32_MAX) return fail(FBEV_ERR_UNSUPPORTED, "C + Cp channels above 2^31 - 1");
+  return FBEV_OK;
+}
+
 fbev_status forward_impl(const void* features, fbev_dtype dtype, fbev_feat_desc fd, int32_t L, const int32_t* ratios,
                          const float* K, const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
-                         int32_t Z, float* out, uint8_t* counts, void* stream) {
+                         int32_t Z, float* out, uint8_t* counts, void* stream, const float* prev = nullptr,
+                         int32_t Cp = 0, const float* ego = nullptr) {
   fbev::Problem p{};
   fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
   if (s != FBEV_OK) return s;
   s = check_levels(fd, L, ratios, p);
   if (s != FBEV_OK) return s;
+  s = check_temporal(fd, X, Y, Cp, prev, ego, "prev_bev");
+  if (s != FBEV_OK) return s;
+  p.out_ch = fd.C + Cp;
   if (dtype != FBEV_DTYPE_F32 && dtype != FBEV_DTYPE_BF16)
     return fail(FBEV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   const int es = (dtype == FBEV_DTYPE_F32) ? 4 : 2;
   const int64_t n_feat = (int64_t)fd.B * fd.N * p.P * fd.C;
   const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  const int64_t n_prev = (int64_t)fd.B * Cp * X * Y;
   const int64_t n_cnt = (int64_t)fd.B * X * Y * Z;
   if (n_feat > 0 && features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "features is NULL");
-  if (n_out > 0 && out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
+  if ((n_out > 0 || n_prev > 0) && out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "out is NULL");
   if ((fd.C * es) % 4 != 0) return fail(FBEV_ERR_UNSUPPORTED, "bf16 features need an even C (got %d)", fd.C);
   const int64_t batch_bytes = (int64_t)fd.N * p.P * fd.C * es;
   if (batch_bytes >= (int64_t)1 << 31)
@@ -134,24 +154,35 @@ fbev_status forward_impl(const void* features, fbev_dtype dtype, fbev_feat_desc 
   p.feat = features;
   p.elem_bytes = es;
   p.vec_bytes = ((fd.C * es) % 16 == 0 && (addr & 15) == 0) ? 16 : 4;
-  if (n_out == 0 && (counts == nullptr || n_cnt == 0)) return FBEV_OK;
-  return device_status(fbev::launch_forward(p, n_out > 0 ? out : nullptr, n_cnt > 0 ? counts : nullptr,
-                                            static_cast<hipStream_t>(stream)),
-                       "fbev_forward launch");
+  if (n_out > 0 || (counts != nullptr && n_cnt > 0)) {
+    s = device_status(fbev::launch_forward(p, n_out > 0 ? out : nullptr, n_cnt > 0 ? counts : nullptr,
+                                           static_cast<hipStream_t>(stream)),
+                      "fbev_forward launch");
+    if (s != FBEV_OK) return s;
+  }
+  if (n_prev == 0) return FBEV_OK;
+  return device_status(fbev::launch_align_forward(p, prev, Cp, ego, out, fd.C, static_cast<hipStream_t>(stream)),
+                       "fbev_forward_temporal launch");
 }
 
 fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios, const float* K,
                           const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z,
-                          float* grad_features, void* stream) {
+                          float* grad_features, void* stream, int32_t Cp = 0, const float* ego = nullptr,
+                          float* grad_prev = nullptr) {
   fbev::Problem p{};
   fbev_status s = check_common(fd, K, R, t, bev_range, X, Y, Z, p);
   if (s != FBEV_OK) return s;
   s = check_levels(fd, L, ratios, p);
   if (s != FBEV_OK) return s;
+  s = check_temporal(fd, X, Y, Cp, grad_prev, ego, "grad_prev");
+  if (s != FBEV_OK) return s;
+  p.out_ch = fd.C + Cp;
   const int64_t n_feat = (int64_t)fd.B * fd.N * p.P * fd.C;
   const int64_t n_out = (int64_t)fd.B * fd.C * X * Y;
+  const int64_t n_prev = (int64_t)fd.B * Cp * X * Y;
   if (n_feat > 0 && grad_features == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_features is NULL");
-  if (n_out > 0 && n_feat > 0 && grad_out == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (((n_out > 0 && n_feat > 0) || n_prev > 0) && grad_out == nullptr)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "grad_out is NULL");
   const int64_t batch_elems = (int64_t)fd.N * p.P * fd.C;
   if (batch_elems >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's gradient spans %lld elements (limit 2^31 - 1)",
@@ -159,9 +190,15 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
   p.feat = nullptr;
   p.elem_bytes = 4;
   p.vec_bytes = 4;
-  if (n_feat == 0) return FBEV_OK;
-  return device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
-                       "fbev_backward launch");
+  if (n_feat > 0) {
+    s = device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
+                      "fbev_backward launch");
+    if (s != FBEV_OK) return s;
+  }
+  if (n_prev == 0) return FBEV_OK;
+  return device_status(fbev::launch_align_backward(p, grad_out, Cp, ego, grad_prev, fd.C,
+                                                   static_cast<hipStream_t>(stream)),
+                       "fbev_backward_temporal launch");
 }
 
 // Camera gradients: geometry checks of the single-level forward, fp32 features.
@@ -426,6 +463,21 @@ fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float*
                           fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, float* grad_features,
                           void* stream) {
   return backward_impl(grad_out, fd, 1, nullptr, K, R, t, bev_range, X, Y, Z, grad_features, stream);
+}
+
+fbev_status fbev_forward_temporal(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K,
+                                  const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                                  int32_t Z, const float* prev_bev, int32_t Cp, const float* ego, float* out,
+                                  uint8_t* counts, void* stream) {
+  return forward_impl(features, dtype, fd, 1, nullptr, K, R, t, bev_range, X, Y, Z, out, counts, stream, prev_bev, Cp,
+                      ego);
+}
+
+fbev_status fbev_backward_temporal(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,
+                                   const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, int32_t Cp,
+                                   const float* ego, float* grad_features, float* grad_prev, void* stream) {
+  return backward_impl(grad_out, fd, 1, nullptr, K, R, t, bev_range, X, Y, Z, grad_features, stream, Cp, ego,
+                       grad_prev);
 }
 
 fbev_status fbev_forward_levels(const void* features, fbev_dtype dtype, fbev_feat_desc fd, int32_t L,

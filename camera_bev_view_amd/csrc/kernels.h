@@ -16,6 +16,8 @@ struct Problem {
   const float* t;         // [B,N,3]
   int B, N, C, H, W;      // H, W: the level-0 map (the in-view test)
   int X, Y, Z;
+  int out_ch;             // channels per batch sample of the output (forward) / upstream gradient (backward)
+                          // tensor [B, out_ch, X, Y]; the transform's C channels come first
   double ox, dx, oy, dy, oz, dz;   // voxel centre i -> o + (i + 1/2) d
   int elem_bytes;         // 4 (fp32) or 2 (bf16)
   int vec_bytes;          // bytes one lane moves per tap: 16 or 4
@@ -34,5 +36,15 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
 size_t camera_grad_workspace_bytes(const Problem& p);
 hipError_t launch_camera_backward(const Problem& p, const float* grad_out, float* gK, float* gR, float* gt, void* work,
                                   hipStream_t stream);
+
+// Temporal fusion: the previous BEV map prev [B, Cp, X, Y] resampled at the
+// current cells mapped by the planar motion ego [B, 2, 3] (current ego x, y ->
+// previous ego x, y) into channels [c0, c0 + Cp) of out [B, out_ch, X, Y]; and
+// the adjoint, dL/dprev [B, Cp, X, Y] (fully overwritten) from channels
+// [c0, c0 + Cp) of grad [B, out_ch, X, Y].  p supplies B, X, Y and the grid.
+hipError_t launch_align_forward(const Problem& p, const float* prev, int Cp, const float* ego, float* out, int c0,
+                                hipStream_t stream);
+hipError_t launch_align_backward(const Problem& p, const float* grad, int Cp, const float* ego, float* gprev, int c0,
+                                 hipStream_t stream);
 
 }  // namespace fbev

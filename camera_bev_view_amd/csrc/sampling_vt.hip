@@ -597,7 +597,7 @@ void sampling_vt_fwd(FwdArgs a) {
   // Coalesced write-out of the tile: rows of n_cells consecutive y per channel.
   {
     const size_t c_stride = (size_t)p.X * p.Y;
-    float* ob = a.out + (((size_t)b * p.C + a.c_lo) * p.X + x) * p.Y + y_base;
+    float* ob = a.out + (((size_t)b * p.out_ch + a.c_lo) * p.X + x) * p.Y + y_base;
     const int yl = threadIdx.x & (kTileY - 1);
     if (yl < n_cells) {
       for (int c = threadIdx.x / kTileY; c < a.Cg; c += kBlock / kTileY)
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   float gpre[kGPer];
   {
     const size_t c_stride = (size_t)p.X * p.Y;
-    const float* gb = a.grad + (((size_t)b * p.C + c_lo) * p.X + x_base) * p.Y + y_base;
+    const float* gb = a.grad + (((size_t)b * p.out_ch + c_lo) * p.X + x_base) * p.Y + y_base;
 #pragma unroll
     for (int i = 0; i < kGPer; ++i) {
       const int e = threadIdx.x + i * kBlock;
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   // found no table slot; such taps can be listed before the LDS tile is written)
   auto grad_at = [&](int k, int c) -> float {
     const int dx = k / ncy, dy = k - dx * ncy;
-    return a.grad[(((size_t)b * p.C + c_lo + c) * p.X + x_base + dx) * p.Y + y_base + dy];
+    return a.grad[(((size_t)b * p.out_ch + c_lo + c) * p.X + x_base + dx) * p.Y + y_base + dy];
   };
 
   int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin

@@ -139,6 +139,82 @@ def bev_sample(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torc
     return SamplingVT.apply(features, K, R, t, tuple(bev_range), X, Y, Z)
 
 
+# ---- temporal fusion (fbev_forward_temporal / fbev_backward_temporal)
+
+def _check_temporal(prev_bev: torch.Tensor, ego: torch.Tensor, B: int, X: int, Y: int, device) -> int:
+    if prev_bev.dim() != 4 or prev_bev.shape[0] != B or tuple(prev_bev.shape[2:]) != (X, Y):
+        raise ValueError(f"prev_bev must be [B={B}, Cp, X={X}, Y={Y}], got {tuple(prev_bev.shape)}")
+    if prev_bev.dtype != torch.float32 or not prev_bev.is_contiguous() or prev_bev.device != device:
+        raise ValueError(f"prev_bev must be a contiguous float32 tensor on {device}")
+    if tuple(ego.shape) != (B, 2, 3) or ego.dtype != torch.float32 or not ego.is_contiguous() or ego.device != device:
+        raise ValueError(f"ego must be a contiguous float32 [B, 2, 3] tensor on {device}")
+    return int(prev_bev.shape[1])
+
+
+def forward_temporal(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.Tensor,
+                     bev_range: Sequence[float], X: int, Y: int, Z: int, prev_bev: torch.Tensor, ego: torch.Tensor,
+                     *, with_counts: bool = False, out: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fbev_forward_temporal: out [B, C + Cp, X, Y] = the current frame's Sampling-VT channels, then the previous
+    BEV map prev_bev [B, Cp, X, Y] resampled at the current cells moved by ego [B, 2, 3] (current -> previous
+    ego x, y).  Returns (out, counts or None)."""
+    if features.dim() != 5 or features.dtype not in _DTYPES or not features.is_cuda or not features.is_contiguous():
+        raise ValueError("features must be a contiguous fp32 or bf16 device tensor [B,N,H,W,C]")
+    B, N, H, W, C = features.shape
+    dev = features.device
+    _check_cams(K, R, t, B, N, dev)
+    Cp = _check_temporal(prev_bev, ego, B, X, Y, dev)
+    if out is None:
+        out = torch.empty((B, C + Cp, X, Y), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (B, C + Cp, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, C + Cp, X, Y] tensor")
+    counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
+    lib = _lib.load()
+    _lib.check(lib.fbev_forward_temporal(_ptr(features), _DTYPES[features.dtype], _lib.feat_desc(B, N, C, H, W),
+                                         _ptr(K), _ptr(R), _ptr(t), _lib.bev_range(bev_range), X, Y, Z,
+                                         _ptr(prev_bev), Cp, _ptr(ego), _ptr(out), _ptr(counts), _stream(dev)))
+    return out, counts
+
+
+def backward_temporal(grad_out: torch.Tensor, feat_shape: Sequence[int], K: torch.Tensor, R: torch.Tensor,
+                      t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, Z: int, Cp: int,
+                      ego: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fbev_backward_temporal: (dL/dF [B,N,H,W,C] fp32, dL/dprev_bev [B,Cp,X,Y]) from grad_out [B, C + Cp, X, Y]."""
+    B, N, H, W, C = (int(v) for v in feat_shape)
+    if tuple(grad_out.shape) != (B, C + Cp, X, Y) or grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32 [B, C + Cp, X, Y]")
+    grad_out = grad_out.contiguous()
+    dev = grad_out.device
+    _check_cams(K, R, t, B, N, dev)
+    if tuple(ego.shape) != (B, 2, 3) or ego.dtype != torch.float32 or not ego.is_contiguous() or ego.device != dev:
+        raise ValueError(f"ego must be a contiguous float32 [B, 2, 3] tensor on {dev}")
+    gF = torch.empty((B, N, H, W, C), dtype=torch.float32, device=dev)
+    gP = torch.empty((B, Cp, X, Y), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.fbev_backward_temporal(_ptr(grad_out), _lib.feat_desc(B, N, C, H, W), _ptr(K), _ptr(R), _ptr(t),
+                                          _lib.bev_range(bev_range), X, Y, Z, Cp, _ptr(ego), _ptr(gF), _ptr(gP),
+                                          _stream(dev)))
+    return gF, gP
+
+
+class TemporalVT(torch.autograd.Function):
+    """Autograd wrapper of the temporal fused transform: gradients for the features and the previous map."""
+
+    @staticmethod
+    def forward(ctx, features, prev_bev, K, R, t, ego, bev_range, X, Y, Z):
+        out, _ = forward_temporal(features, K, R, t, bev_range, X, Y, Z, prev_bev, ego)
+        ctx.save_for_backward(K, R, t, ego)
+        ctx.meta = (tuple(features.shape), features.dtype, int(prev_bev.shape[1]), tuple(bev_range), X, Y, Z)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        K, R, t, ego = ctx.saved_tensors
+        shape, dtype, Cp, rng, X, Y, Z = ctx.meta
+        gF, gP = backward_temporal(grad_out.float(), shape, K, R, t, rng, X, Y, Z, Cp, ego)
+        return gF.to(dtype), gP, None, None, None, None, None, None, None, None
+
+
 # ---- feature pyramids (fbev_forward_levels / fbev_backward_levels)
 
 def level_ratios(H: int, W: int, shapes: Sequence[Sequence[int]]) -> Tuple[int, ...]:

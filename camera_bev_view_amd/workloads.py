@@ -408,3 +408,54 @@ def random_deform_case(seed: int, B: int, N: int, C: int, H: int, W: int, Q: int
     weights = _dirichlet_weights(g, B, Q, N, Kp)
     gout = np.random.default_rng([4000 + seed, 2]).standard_normal((B, Q, C), dtype=np.float32)
     return DeformInputs(F, K, R, t, anchors.astype(np.float32), offsets.astype(np.float32), weights, gout)
+
+
+# ---- temporal fusion inputs
+#
+# The previous frame's BEV map stands in for the output of the previous step:
+# N(0, 1) values on the current grid.  The ego motion maps current-ego (x, y)
+# to previous-ego (x, y): a yaw of U(-5, 5) degrees and a move of U(2, 8) m
+# forward and U(-0.5, 0.5) m sideways per sample, the motion of a car between
+# frames half a second apart, from ``default_rng([id, 5])``.
+
+TEMPORAL_WORKLOADS: Dict[str, dict] = {
+    "temporal": dict(base="nuscenes", cid=10, Cp=64),
+}
+
+
+def make_ego_motion(cid: int, B: int, yaw_deg: Optional[float] = None, shift=None) -> np.ndarray:
+    """[B, 2, 3] fp32 planar motions current-ego (x, y) -> previous-ego (x, y)."""
+    g = np.random.default_rng([cid, 5])
+    A = np.empty((B, 2, 3), np.float64)
+    for b in range(B):
+        psi = math.radians(g.uniform(-5.0, 5.0) if yaw_deg is None else yaw_deg)
+        tx, ty = (g.uniform(2.0, 8.0), g.uniform(-0.5, 0.5)) if shift is None else shift
+        A[b] = [[math.cos(psi), -math.sin(psi), tx], [math.sin(psi), math.cos(psi), ty]]
+    return A.astype(np.float32)
+
+
+@dataclasses.dataclass
+class TemporalInputs:
+    cur: Inputs
+    prev: np.ndarray          # [B, Cp, X, Y] fp32
+    ego: np.ndarray           # [B, 2, 3] fp32
+    grad_out: np.ndarray      # [B, C + Cp, X, Y] fp32
+
+
+def make_temporal_inputs(name: str = "temporal") -> TemporalInputs:
+    w = TEMPORAL_WORKLOADS[name]
+    cur = make_inputs(w["base"], with_grad=False)
+    B, C = cur.F.shape[0], cur.F.shape[2]
+    prev = np.random.default_rng([w["cid"], 1]).standard_normal((B, w["Cp"], cur.X, cur.Y), dtype=np.float32)
+    g = np.random.default_rng([w["cid"], 2]).standard_normal((B, C + w["Cp"], cur.X, cur.Y), dtype=np.float32)
+    return TemporalInputs(cur, prev, make_ego_motion(w["cid"], B), g)
+
+
+def random_temporal_case(seed: int, B: int, N: int, C: int, H: int, W: int, X: int, Y: int, Z: int, Cp: int,
+                         rng6=(-30.0, 30.0, -30.0, 30.0, -4.0, 3.0), yaw_deg: Optional[float] = None,
+                         shift=None) -> TemporalInputs:
+    """An arbitrary-size seeded temporal case; ``yaw_deg`` / ``shift`` fix the motion."""
+    cur = random_case(5000 + seed, B, N, C, H, W, X, Y, Z, rng6=rng6, with_grad=False)
+    prev = np.random.default_rng([5000 + seed, 1]).standard_normal((B, Cp, X, Y), dtype=np.float32)
+    g = np.random.default_rng([5000 + seed, 2]).standard_normal((B, C + Cp, X, Y), dtype=np.float32)
+    return TemporalInputs(cur, prev, make_ego_motion(5000 + seed, B, yaw_deg, shift), g)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 5
+#define FBEV_ABI_VERSION 6
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
@@ -144,6 +144,52 @@ fbev_status fbev_backward(const float* grad_out, fbev_feat_desc fd, const float*
  * smaller than required gives FBEV_ERR_INVALID_ARGUMENT.  The result is deterministic: partial sums per workgroup are added in a
  * fixed order in fp64.  Zero sizes give zero (or empty) gradients.
  */
+/*
+ * Temporal fused view transform.  The FlashBEV notes name a temporal fused
+ * transform as future work ("Takeaway" item 4); the SparseDriveV2 notes ask
+ * that history be moved into the current ego frame before use (ego-motion
+ * compensation), and the Lift-Splat-Shoot tutorial stacks two BEV maps of one
+ * scene in the same BEV space (the BEVFusion paragraph).  This call writes
+ *
+ *   out[b, 0:C]      = fbev_forward(features, ...)[b]           (current frame)
+ *   out[b, C:C+Cp]   = prev_bev[b] resampled at the current cells
+ *
+ * where current cell (i, j), centre (x, y), maps to (x', y') = A_b [x; y; 1]
+ * in the previous ego frame, i.e. to the continuous cell index
+ * i' = (x' - x_min)/dx - 1/2, j' = (y' - y_min)/dy - 1/2 of the previous map,
+ * which lies on the same grid (bev_range, X, Y).  Inside the closed box
+ * [0, X-1] x [0, Y-1] of cell centres the previous map is sampled bilinearly
+ * (the clamped tap at i' = X-1 has weight 0); outside it the value is 0.
+ *
+ *   prev_bev : [B,Cp,X,Y] fp32, device, read only (NULL allowed when B*Cp*X*Y == 0).
+ *   ego      : [B,2,3] fp32, device: A_b, current-ego (x, y) -> previous-ego
+ *              (x, y) in metres (a rigid planar motion in practice).
+ *   out      : [B,C+Cp,X,Y] fp32, device, fully overwritten.
+ *   counts   : as for fbev_forward.
+ * Other arguments as for fbev_forward.  Deterministic.  Cp < 0 or NULL
+ * pointers for non-empty buffers -> FBEV_ERR_INVALID_ARGUMENT; X*Y >= 2^31 ->
+ * FBEV_ERR_UNSUPPORTED.
+ */
+fbev_status fbev_forward_temporal(const void* features, fbev_dtype dtype, fbev_feat_desc fd, const float* K,
+                                  const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
+                                  int32_t Z, const float* prev_bev, int32_t Cp, const float* ego, float* out,
+                                  uint8_t* counts, void* stream);
+
+/*
+ * Gradients of fbev_forward_temporal: dL/dF from grad_out[:, 0:C] exactly as
+ * fbev_backward, and dL/dprev_bev [B,Cp,X,Y] (fp32, device, fully overwritten,
+ * deterministic) = the adjoint of the resampling: every current cell passes
+ * grad_out[b, C + c, i, j] times its bilinear weights to its four taps.  The
+ * adjoint is computed as a gather over the current cells whose sample can
+ * reach a previous cell; motions whose inverse stretches the grid by more than
+ * 16 cells per cell (far from rigid) are not supported and leave those cells'
+ * gradient at 0.  No gradient with respect to the ego motion.
+ *   grad_out : [B,C+Cp,X,Y] fp32, device, read only.
+ */
+fbev_status fbev_backward_temporal(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,
+                                   const float* t, fbev_range bev_range, int32_t X, int32_t Y, int32_t Z, int32_t Cp,
+                                   const float* ego, float* grad_features, float* grad_prev, void* stream);
+
 fbev_status fbev_backward_cameras_workspace(fbev_feat_desc fd, int32_t X, int32_t Y, int32_t Z, size_t* bytes);
 fbev_status fbev_backward_cameras(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
                                   const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,

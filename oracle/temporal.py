@@ -116,5 +116,8 @@ def temporal_forward(F, K, R, t, rng6, X: int, Y: int, Z: int, prev, A) -> Dict[
 def temporal_backward(grad_out, K, R, t, rng6, X: int, Y: int, Z: int, H: int, W: int, C: int, A):
     """(dL/dF [B, N, C, H, W], dL/dprev_bev [B, Cp, X, Y]) of ``temporal_forward`` (T5)."""
     g = np.asarray(grad_out, np.float64)
-    gF = oracle_backward(g[:, :C], K, R, t, rng6, X, Y, Z, H, W)
+    if C == 0:                                  # no current channels: an empty feature gradient
+        gF = np.zeros((g.shape[0], np.asarray(K).shape[1], 0, H, W), np.float64)
+    else:
+        gF = oracle_backward(g[:, :C], K, R, t, rng6, X, Y, Z, H, W)
     return gF, align_adjoint(g[:, C:], A, rng6)

@@ -315,3 +315,44 @@ def test_camera_backward_validation(lib, kwargs, status, msg):
 def test_camera_empty_problems_return_ok_without_device_work(lib):
     assert cbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, feat=None, K=None, gK=None, gR=None, gt=None, ws=None) == 0
     assert cbwd(lib, desc=(1, 0, 64, 16, 44), K=None, gK=None, gR=None, gt=None, ws=None) == 0
+
+
+def tfwd(lib, feat=FAKE, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8, prev=FAKE, Cp=64, ego=FAKE, out=FAKE):
+    return lib.fbev_forward_temporal(feat, _lib.FBEV_DTYPE_F32, _lib.feat_desc(*desc), FAKE, FAKE, FAKE,
+                                     _lib.bev_range(RNG), X, Y, Z, prev, Cp, ego, out, None, None)
+
+
+def tbwd(lib, grad=FAKE, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8, Cp=64, ego=FAKE, gF=FAKE, gP=FAKE):
+    return lib.fbev_backward_temporal(grad, _lib.feat_desc(*desc), FAKE, FAKE, FAKE, _lib.bev_range(RNG), X, Y, Z, Cp,
+                                      ego, gF, gP, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(Cp=-1), 1, "negative Cp"),
+    (dict(prev=None), 1, "prev_bev is NULL"),
+    (dict(ego=None), 1, "ego is NULL"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(X=65536, Y=65536, Z=1), 2, "X*Y"),
+    (dict(desc=(1, 6, 64, -16, 44)), 1, "negative feature size"),
+])
+def test_temporal_forward_validation(lib, kwargs, status, msg):
+    assert tfwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(Cp=-2), 1, "negative Cp"),
+    (dict(gP=None), 1, "grad_prev is NULL"),
+    (dict(ego=None), 1, "ego is NULL"),
+    (dict(grad=None), 1, "grad_out is NULL"),
+    (dict(gF=None), 1, "grad_features is NULL"),
+])
+def test_temporal_backward_validation(lib, kwargs, status, msg):
+    assert tbwd(lib, **kwargs) == status
+    assert msg in lib.fbev_last_error().decode()
+
+
+def test_temporal_empty_problems_return_ok_without_device_work(lib):
+    assert tfwd(lib, desc=(0, 6, 64, 16, 44), feat=None, prev=None, ego=None, out=None) == 0
+    assert tfwd(lib, X=0, prev=None, ego=None, out=None) == 0
+    assert tbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, ego=None, gF=None, gP=None) == 0
