@@ -61,7 +61,7 @@ def kernel_source_hash(path: str = KERNEL_SRC) -> str:
 def measured_traffic(kernel, workload: str):
     """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
     they were taken on a different kernel source or workload (or never).  Each
-    workload's record names the source file its counters were taken on.
+    workload's record names the source file(s) its counters were taken on.
     ``kernel`` may be a list: the bytes of one pass of those kernels."""
     if isinstance(kernel, (list, tuple)):
         parts = [measured_traffic(k, workload) for k in kernel]
@@ -72,10 +72,10 @@ def measured_traffic(kernel, workload: str):
     except (OSError, ValueError):
         return None
     w = rec.get("workloads", {}).get(workload, {})
-    src = os.path.join(ROOT, w.get("source", os.path.relpath(KERNEL_SRC, ROOT)))
-    sha = w.get("source_sha256", rec.get("source_sha256"))
+    sources = w.get("sources") or {w.get("source", os.path.relpath(KERNEL_SRC, ROOT)):
+                                   w.get("source_sha256", rec.get("source_sha256"))}
     try:
-        if sha != kernel_source_hash(src):
+        if any(sha != kernel_source_hash(os.path.join(ROOT, src)) for src, sha in sources.items()):
             return None
     except OSError:
         return None

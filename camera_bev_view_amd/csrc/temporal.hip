@@ -15,8 +15,10 @@
 // there is no history and the value is 0.
 //
 // bev_align_fwd: a thread per (cell, 8 channels): the source position in fp64
-// once, then four taps per channel.  bev_align_bwd: the adjoint as a gather, a
-// thread per (previous cell q, 8 channels): the current cells whose sample can
+// once, then four taps per channel; workgroups are numbered so that each XCD
+// takes a contiguous run of (cell block, channel chunk) units.
+// bev_align_bwd: the adjoint as a gather, a thread per (previous cell q,
+// 8 channels): the current cells whose sample can
 // touch q lie in a small box around A^{-1}(q) (the inverse image of the open
 // 2 x 2 square of q's taps); each is re-evaluated with the forward's own
 // arithmetic and adds weight x upstream gradient when q is one of its taps.
@@ -34,11 +36,21 @@ constexpr int kBlock = 256;
 constexpr int kChunk = 8;                // channels per thread
 constexpr int kMaxWin = 33;              // candidate cells per axis in the backward, at most
 
+// Workgroups are dealt round-robin to the eight XCDs; renumbering them so that
+// each XCD takes a contiguous run of units keeps neighbouring cell blocks, which
+// read the same rows of the source map, in one L2.
+__device__ __forceinline__ int xcd_unit(int bid, int nblk) {
+  const int xcd = bid & 7, k = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+}
+
 struct AlignArgs {
   const float* src;        // forward: prev [B, Cp, X, Y]; backward: grad [B, out_ch, X, Y]
   const float* ego;        // [B, 2, 3]
   float* dst;              // forward: out [B, out_ch, X, Y]; backward: dprev [B, Cp, X, Y]
   int B, X, Y, Cp, out_ch, c0;
+  int nblk, nchunk;        // cell blocks per channel chunk, channel chunks
   double ox, dx, oy, dy;
 };
 
@@ -90,14 +102,16 @@ __device__ __forceinline__ Src source_of(const AlignArgs& a, const IndexMap& im,
 }
 
 __global__ __launch_bounds__(kBlock) void bev_align_fwd(AlignArgs a) {
-  const int b = blockIdx.z;
+  const int u = xcd_unit(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
+  const int blk = u % a.nblk, rest = u / a.nblk;
+  const int chunk = rest % a.nchunk, b = rest / a.nchunk;
   const int XY = a.X * a.Y;
-  const int q = blockIdx.x * kBlock + threadIdx.x;
+  const int q = blk * kBlock + threadIdx.x;
   if (q >= XY) return;
   const int i = q / a.Y, j = q - i * a.Y;
   const IndexMap im = index_map(a, b);
   const Src s = source_of(a, im, i, j);
-  const int c_begin = blockIdx.y * kChunk;
+  const int c_begin = chunk * kChunk;
   const int c_end = min(c_begin + kChunk, a.Cp);
   const int t00 = s.i0 * a.Y + s.j0;
   const int t01 = t00 + s.dj, t10 = t00 + s.di * a.Y, t11 = t10 + s.dj;
@@ -116,9 +130,11 @@ __global__ __launch_bounds__(kBlock) void bev_align_fwd(AlignArgs a) {
 }
 
 __global__ __launch_bounds__(kBlock) void bev_align_bwd(AlignArgs a) {
-  const int b = blockIdx.z;
+  const int u = xcd_unit(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
+  const int blk = u % a.nblk, rest = u / a.nblk;
+  const int chunk = rest % a.nchunk, b = rest / a.nchunk;
   const int XY = a.X * a.Y;
-  const int q = blockIdx.x * kBlock + threadIdx.x;
+  const int q = blk * kBlock + threadIdx.x;
   if (q >= XY) return;
   const int qi = q / a.Y, qj = q - qi * a.Y;
   const IndexMap im = index_map(a, b);
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void bev_align_bwd(AlignArgs a) {
   const bool ok = isfinite(ci) && isfinite(cj) && ri < 0.5 * (kMaxWin - 1) && rj < 0.5 * (kMaxWin - 1);
   const int i_lo = ok ? max(0, (int)ceil(ci - ri)) : 1, i_hi = ok ? min(a.X - 1, (int)floor(ci + ri)) : 0;
   const int j_lo = ok ? max(0, (int)ceil(cj - rj)) : 1, j_hi = ok ? min(a.Y - 1, (int)floor(cj + rj)) : 0;
-  const int c_begin = blockIdx.y * kChunk;
+  const int c_begin = chunk * kChunk;
   const int c_end = min(c_begin + kChunk, a.Cp);
   float acc[kChunk];
 #pragma unroll
@@ -178,9 +194,11 @@ AlignArgs align_args(const Problem& p, int Cp, const float* ego, int c0) {
   return a;
 }
 
-dim3 align_grid(const Problem& p, int Cp) {
-  const long long XY = (long long)p.X * p.Y;
-  return dim3((unsigned)((XY + kBlock - 1) / kBlock), (unsigned)((Cp + kChunk - 1) / kChunk), (unsigned)p.B);
+dim3 align_grid(AlignArgs& a) {
+  const long long XY = (long long)a.X * a.Y;
+  a.nblk = (int)((XY + kBlock - 1) / kBlock);
+  a.nchunk = (a.Cp + kChunk - 1) / kChunk;
+  return dim3((unsigned)((long long)a.nblk * a.nchunk * a.B));
 }
 
 }  // namespace
@@ -191,7 +209,8 @@ hipError_t launch_align_forward(const Problem& p, const float* prev, int Cp, con
   AlignArgs a = align_args(p, Cp, ego, c0);
   a.src = prev;
   a.dst = out;
-  hipLaunchKernelGGL(bev_align_fwd, align_grid(p, Cp), dim3(kBlock), 0, stream, a);
+  const dim3 grid = align_grid(a);
+  hipLaunchKernelGGL(bev_align_fwd, grid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -201,7 +220,8 @@ hipError_t launch_align_backward(const Problem& p, const float* grad, int Cp, co
   AlignArgs a = align_args(p, Cp, ego, c0);
   a.src = grad;
   a.dst = gprev;
-  hipLaunchKernelGGL(bev_align_bwd, align_grid(p, Cp), dim3(kBlock), 0, stream, a);
+  const dim3 grid = align_grid(a);
+  hipLaunchKernelGGL(bev_align_bwd, grid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 
