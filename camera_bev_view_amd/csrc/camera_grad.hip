@@ -44,10 +44,12 @@ constexpr int kTileY = 16;               // cells per unit (one x-row)
 constexpr int kCg = 64;                  // channels per unit
 constexpr int kGLd = kCg + 4;            // padded LDS row of one cell's upstream gradient
 constexpr int kRedLd = 13;               // padded LDS row of one lane's 12 partial sums
-constexpr int kUnroll = 4;               // samples in flight per gather step
+constexpr int kUnroll = 4;               // samples per gather step (the four-way row sum)
 constexpr int kMaxGroups = 1792;         // workgroups of the main kernel per batch sample, at most
 constexpr int kFinishPer = 28;           // workgroup slices each finishing lane adds
 static_assert(kMaxGroups <= kFinishPer * kWave, "the finish reads every slice in one step");
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -64,14 +66,29 @@ __device__ __forceinline__ double recip(double x) {
   return r;
 }
 
-// Sum over each row of 16 lanes, left in every lane of the row (DPP: swap
-// neighbours, swap pairs, mirror within 8, mirror within 16).
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-  return x;
+// x of another lane of the same row of 16 (DPP): kQuadSwap1 / kQuadSwap2 swap
+// neighbours / pairs within a quad, kHalfMirror mirrors within 8 lanes,
+// kRowMirror within 16.
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
+
+// Four row sums at once: d[q] holds lane j's part of value q (j = lane % 16);
+// afterwards every lane of quad q of the row (j / 4 == q) holds the row's sum
+// of value q.  Mirroring across the row and then across each half pairs every
+// lane with three others so that the four lanes of a quad together cover the
+// row; each step keeps half of the values (5 DPP adds instead of 16).
+__device__ __forceinline__ float row_sum16_x4(const float (&d)[4], int j) {
+  const bool lower = j < 8;
+  const float a0 = (lower ? d[0] : d[2]) + dpp<kRowMirror>(lower ? d[2] : d[0]);
+  const float a1 = (lower ? d[1] : d[3]) + dpp<kRowMirror>(lower ? d[3] : d[1]);
+  const bool lo4 = (j & 7) < 4;
+  float b = (lo4 ? a0 : a1) + dpp<kHalfMirror>(lo4 ? a1 : a0);
+  b += dpp<kQuadSwap1>(b);
+  b += dpp<kQuadSwap2>(b);
+  return b;
 }
 
 struct CamGradArgs {
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = uniform(threadIdx.x / kWave);
   float* wbuf = sW + wid * kWave * kRedLd;
-  int4* rec = reinterpret_cast<int4*>(wbuf);                                      // [64] taps of listed samples
+  int* rec = reinterpret_cast<int*>(wbuf);                                        // [64][4] tap offsets of listed samples
   float* dots = wbuf + 4 * kWave;                                                 // [64][4] tap dot products
   const int tap = lane >> 4, j = lane & 15;
 
@@ -122,6 +139,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   const int HWC = p.H * p.W * p.C;
   const float* fb = static_cast<const float*>(p.feat) + (size_t)b * p.N * HWC;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(fb), 0,
+                                                                      (int)(sizeof(float) * p.N * HWC), 0x00020000);
   float acc[12];
 #pragma unroll
   for (int k = 0; k < 12; ++k) acc[k] = 0.f;
@@ -156,6 +175,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     __syncthreads();
     const double px = p.ox + ((double)x + 0.5) * p.dx;
     const double hA0 = fma(P[0], px, P[3]), hA1 = fma(P[4], px, P[7]), hA2 = fma(P[8], px, P[11]);
+    const int jo = (4 * j < Cg) ? 4 * j : 0;             // this lane's channels; past the group it rereads c0
     for (int cell = wid; cell < kTileY; cell += kWaves) {
       const int y = ty * kTileY + cell;
       if (y >= p.Y) break;
@@ -198,8 +218,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
           ih = (float)r;
           uf = (float)uu;
           vf = (float)vv;
-          rec[rank] = make_int4(ln * HWC + (y0 * p.W + x0) * p.C, (x0 + 1 < p.W) ? p.C : 0,
-                                (y0 + 1 < p.H) ? p.W * p.C : 0, 0);
+          const int o00 = ln * HWC + (y0 * p.W + x0) * p.C + c0;
+          const int ox = (x0 + 1 < p.W) ? p.C : 0, oy = (y0 + 1 < p.H) ? p.W * p.C : 0;
+          *reinterpret_cast<int4*>(rec + 4 * rank) = make_int4(o00, o00 + ox, o00 + oy, o00 + ox + oy);
         }
         wave_lds_sync();
         // ---- tap dot products <g_cell, F_tap>, lanes = (tap, channel chunk)
@@ -207,16 +228,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         // is read again and channels past the group read channel c0, and both are dropped.
         for (int s0 = 0; s0 < ns; s0 += kUnroll) {
           float f[kUnroll][4];
+          int offs[kUnroll];
+#pragma unroll
+          for (int i = 0; i < kUnroll; ++i) offs[i] = rec[4 * min(s0 + i, ns - 1) + tap];   // this lane's taps
 #pragma unroll
           for (int i = 0; i < kUnroll; ++i) {
-            const int4 rr = rec[min(s0 + i, ns - 1)];
-            const int off = rr.x + ((tap & 1) ? rr.y : 0) + ((tap & 2) ? rr.z : 0) + c0;
+            const int off = offs[i];
             if (V == 4) {
-              const float4 v = *reinterpret_cast<const float4*>(fb + off + ((4 * j < Cg) ? 4 * j : 0));
-              f[i][0] = v.x;
-              f[i][1] = v.y;
-              f[i][2] = v.z;
-              f[i][3] = v.w;
+              const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (off + jo), 0, 0);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) f[i][k] = __uint_as_float(v[k]);
             } else {
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
@@ -225,14 +246,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
               }
             }
           }
+          float d[kUnroll];
 #pragma unroll
           for (int i = 0; i < kUnroll; ++i) {
-            float dot = 0.f;
+            d[i] = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dot = fmaf(f[i][k], g[k], dot);   // g is 0 past the group's channels
-            const float sum = row_sum16(s0 + i < ns ? dot : 0.f);
-            if (j == 0 && s0 + i < ns) dots[(s0 + i) * 4 + tap] = sum;
+            for (int k = 0; k < 4; ++k) d[i] = fmaf(f[i][k], g[k], d[i]);   // g is 0 past the group's channels
           }
+          const float sum = row_sum16_x4(d, j);                // sample s0 + j / 4 of this lane's tap row
+          const int q = j >> 2;
+          if ((j & 3) == 0 && s0 + q < ns) dots[(s0 + q) * 4 + tap] = sum;
         }
         wave_lds_sync();
         // ---- dL/du, dL/dv of the lane's sample and its 12 entries of dL/dP
