@@ -95,6 +95,57 @@ def pass_roofline(kernels, rate, nbytes, workload, exact_traffic=True):
             "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
 
 
+def time_passes(args, dev, passes, label):
+    """W untimed warm-up steps, then K timed steps of ``passes`` (callables, run in order on the
+    current stream) bracketed by synchronizations; HIP events around every pass.  Returns
+    (ms per step over the whole timed region, [mean ms of each pass])."""
+    import numpy as np
+    import torch
+    log(f"[bench] warmup {args.warmup} steps on {label}")
+    for _ in range(args.warmup):
+        for f in passes:
+            f()
+    torch.cuda.synchronize()
+    calibration_copy(args, dev)
+    stream = torch.cuda.current_stream(dev)
+    n = len(passes)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        for i, f in enumerate(passes):
+            ev[k][i].record(stream)
+            f()
+        ev[k][n].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    pass_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(n)]
+    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (passes " + ", ".join(f"{m * 1e3:.2f}" for m in pass_ms) + " us)")
+    return ms_step, pass_ms
+
+
+def pass_rates(ms, nbytes, **counts):
+    """Per-pass figures: ``counts`` (items per pass) become items/s; algorithmic HBM GB/s and fraction."""
+    s_ = ms * 1e-3
+    d = {"ms": ms}
+    for k, v in counts.items():
+        d[k] = v / s_
+    d.update({"algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": nbytes / s_ / 1e9,
+              "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS})
+    return d
+
+
+def bench_line(args, value, ms_step, dtype, data, config):
+    """The JSON line's fixed fields, in order."""
+    return {"metric": METRIC, "value": value, "unit": "BEV output elems/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": data, "config": config}
+
+
 def calibration_copy(args, dev):
     """A plain copy of --calib-copy-mib MiB, three times, for scaling the HBM byte counters."""
     if not args.calib_copy_mib:
@@ -207,74 +258,27 @@ def main_lss(args):
     fwd_call = lambda: ops.lss_forward(dep, ctx, K, R, t, *geo, out=out)
     bwd_call = lambda: ops.lss_backward(g, dep, ctx, K, R, t, *geo, grad_depth=gd, grad_context=gc)
 
-    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
-    for _ in range(args.warmup):
-        fwd_call()
-        bwd_call()
-    torch.cuda.synchronize()
-    calibration_copy(args, dev)
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        fwd_call()
-        ev[k][1].record(stream)
-        bwd_call()
-        ev[k][2].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
-
+    ms_step, (fwd_ms, bwd_ms) = time_passes(args, dev, [fwd_call, bwd_call], args.workload)
     out_elems = B * C * X * Y
     pix = B * N * H * W
     points = pix * D
     cam_bytes = B * N * 21 * 4
     fwd_bytes = pix * (D + C) * 4 + out_elems * 4 + cam_bytes            # alpha and c once, output once
     bwd_bytes = out_elems * 4 + 2 * pix * (D + C) * 4 + cam_bytes         # grad_out, alpha and c once; both grads once
-
-    def rates(ms, nbytes):
-        s_ = ms * 1e-3
-        return {"ms": ms, "out_elems_per_s": out_elems / s_, "lifted_points_per_s": points / s_,
-                "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": nbytes / s_ / 1e9,
-                "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
-
-    fwd = rates(fwd_ms, fwd_bytes)
-    bwd = rates(bwd_ms, bwd_bytes)
+    fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems, lifted_points_per_s=points)
+    bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems, lifted_points_per_s=points)
     # the timed passes: the forward kernel alone; the backward's two zero-fills and its kernel
     dom_k, dom, dom_bytes = (["lift_splat_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
         (["lss_fill_zero", "lss_fill_zero", "lift_splat_bwd"], bwd, bwd_bytes)
-    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
-    line = {
-        "metric": METRIC,
-        "value": out_elems / (ms_step * 1e-3),
-        "unit": "BEV output elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic: seeded 6-camera ring rig, flat-Dirichlet depth distributions, N(0,1) context and "
-                "upstream gradient",
-        "config": {"workload": f"{args.workload}: Lift-Splat B={B} N={N} HxW={H}x{W} D={D} bins "
-                               f"{inp.d_min}+k*{inp.d_step} m, C={C} -> X*Y={X}x{Y} pillars, "
-                               f"one step = forward + backward",
-                   "B": B, "N": N, "C": C, "H": H, "W": W, "D": D, "X": X, "Y": Y},
-        "lifted_points_per_s": points * 2 / (ms_step * 1e-3),
-        "forward": fwd,
-        "backward": bwd,
-        "roofline": roofline,
-    }
+    line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
+                      "synthetic: seeded 6-camera ring rig, flat-Dirichlet depth distributions, N(0,1) context and "
+                      "upstream gradient",
+                      {"workload": f"{args.workload}: Lift-Splat B={B} N={N} HxW={H}x{W} D={D} bins "
+                                   f"{inp.d_min}+k*{inp.d_step} m, C={C} -> X*Y={X}x{Y} pillars, "
+                                   f"one step = forward + backward",
+                       "B": B, "N": N, "C": C, "H": H, "W": W, "D": D, "X": X, "Y": Y})
+    line.update({"lifted_points_per_s": points * 2 / (ms_step * 1e-3), "forward": fwd, "backward": bwd,
+                 "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload)})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline_lss(inp)
@@ -334,69 +338,23 @@ def main_deform(args):
     fwd_call = lambda: ops.deform_forward(F, K, R, t, A, D, Wt, out=out)
     bwd_call = lambda: ops.deform_backward(g, F, K, R, t, A, D, Wt)
 
-    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
-    for _ in range(args.warmup):
-        fwd_call()
-        bwd_call()
-    torch.cuda.synchronize()
-    calibration_copy(args, dev)
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        fwd_call()
-        ev[k][1].record(stream)
-        bwd_call()
-        ev[k][2].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
-
+    ms_step, (fwd_ms, bwd_ms) = time_passes(args, dev, [fwd_call, bwd_call], args.workload)
     out_elems = B * Q * C
     feat_bytes = B * N * H * W * C * 4
     q_bytes = B * Q * (3 + 3 * Kp + N * Kp) * 4
     fwd_bytes = feat_bytes + q_bytes + out_elems * 4 + B * N * 21 * 4
     bwd_bytes = out_elems * 4 + 2 * feat_bytes + 2 * q_bytes + B * N * 21 * 4
-
-    def rates(ms, nbytes):
-        s_ = ms * 1e-3
-        return {"ms": ms, "out_elems_per_s": out_elems / s_, "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": nbytes / s_ / 1e9,
-                "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
-
-    fwd = rates(fwd_ms, fwd_bytes)
-    bwd = rates(bwd_ms, bwd_bytes)
+    fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems)
+    bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems)
     dom_k, dom, dom_bytes = (["deform_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
         (["deform_fill_zero", "deform_bwd"], bwd, bwd_bytes)
-    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
-    line = {
-        "metric": METRIC,
-        "value": out_elems / (ms_step * 1e-3),
-        "unit": "BEV output elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient, seeded anchors and "
-                "offsets, flat-Dirichlet weights",
-        "config": {"workload": f"{args.workload}: Deformable Aggregation B={B} N={N} C={C} HxW={H}x{W} Q={Q} "
-                               f"queries x Kp={Kp} keypoints (outputs = query features), one step = forward + backward",
-                   "B": B, "N": N, "C": C, "H": H, "W": W, "Q": Q, "Kp": Kp},
-        "forward": fwd,
-        "backward": bwd,
-        "roofline": roofline,
-    }
+    line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
+                      "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient, seeded anchors and "
+                      "offsets, flat-Dirichlet weights",
+                      {"workload": f"{args.workload}: Deformable Aggregation B={B} N={N} C={C} HxW={H}x{W} Q={Q} "
+                                   f"queries x Kp={Kp} keypoints (outputs = query features), one step = forward + "
+                                   f"backward", "B": B, "N": N, "C": C, "H": H, "W": W, "Q": Q, "Kp": Kp})
+    line.update({"forward": fwd, "backward": bwd, "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload)})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline_deform(inp, 4000)
@@ -445,52 +403,17 @@ def main_cameras(args):
     ws = torch.empty((1 << 24,), dtype=torch.uint8, device=dev)
     call = lambda: ops.camera_backward(g, F, K, R, t, inp.rng6, X, Y, Z, workspace=ws)
 
-    log(f"[bench] warmup {args.warmup} steps on cameras")
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    calibration_copy(args, dev)
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        call()
-        ev[k][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    pass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (pass {pass_ms * 1e3:.2f} us)")
-
+    ms_step, (pass_ms,) = time_passes(args, dev, [call], "cameras")
     out_elems = B * C * X * Y
     nbytes = B * N * H * W * C * 4 + out_elems * 4 + B * N * 21 * 4 * 2   # features, grad_out, cameras in, gradients out
-    achieved = nbytes / (pass_ms * 1e-3) / 1e9
-    roofline = pass_roofline(["camera_grad_main", "camera_grad_finish"], {"ms": pass_ms, "hbm_gbps_algorithmic": achieved},
-                             nbytes, "cameras")
-    line = {
-        "metric": METRIC,
-        "value": out_elems / (ms_step * 1e-3),
-        "unit": "BEV output elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
-        "config": {"workload": f"cameras: dL/dK, dL/dR, dL/dt of the Sampling-VT, B={B} N={N} C={C} HxW={H}x{W} "
-                               f"grid {X}x{Y}x{Z} (outputs = the BEV elements whose gradient is pulled back)",
-                   "B": B, "N": N, "C": C, "H": H, "W": W, "X": X, "Y": Y, "Z": Z},
-        "pass": {"ms": pass_ms, "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": achieved},
-        "roofline": roofline,
-    }
+    rate = pass_rates(pass_ms, nbytes)
+    line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
+                      "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
+                      {"workload": f"cameras: dL/dK, dL/dR, dL/dt of the Sampling-VT, B={B} N={N} C={C} "
+                                   f"HxW={H}x{W} grid {X}x{Y}x{Z} (outputs = the BEV elements whose gradient is "
+                                   f"pulled back)", "B": B, "N": N, "C": C, "H": H, "W": W, "X": X, "Y": Y, "Z": Z})
+    line.update({"pass": {"ms": pass_ms, "algorithmic_bytes": nbytes, "hbm_gbps_algorithmic": rate["hbm_gbps_algorithmic"]},
+                 "roofline": pass_roofline(["camera_grad_main", "camera_grad_finish"], rate, nbytes, "cameras")})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline_cameras(inp)
@@ -546,70 +469,24 @@ def main_temporal(args):
     fwd_call = lambda: ops.forward_temporal(F, K, R, t, cur.rng6, X, Y, Z, prev, ego, out=out)
     bwd_call = lambda: ops.backward_temporal(g, (B, N, H, W, C), K, R, t, cur.rng6, X, Y, Z, Cp, ego)
 
-    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
-    for _ in range(args.warmup):
-        fwd_call()
-        bwd_call()
-    torch.cuda.synchronize()
-    calibration_copy(args, dev)
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        fwd_call()
-        ev[k][1].record(stream)
-        bwd_call()
-        ev[k][2].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
-
+    ms_step, (fwd_ms, bwd_ms) = time_passes(args, dev, [fwd_call, bwd_call], args.workload)
     out_elems = B * (C + Cp) * X * Y
     cams = B * N * 21 * 4 + B * 6 * 4
     feat_bytes = B * N * H * W * C * 4
     fwd_bytes = feat_bytes + B * Cp * X * Y * 4 + out_elems * 4 + cams       # features, previous map, output
     bwd_bytes = out_elems * 4 + feat_bytes + B * Cp * X * Y * 4 + cams       # upstream gradient, dL/dF, dL/dprev
-
-    def rates(ms, nbytes):
-        s_ = ms * 1e-3
-        return {"ms": ms, "out_elems_per_s": out_elems / s_, "algorithmic_bytes": nbytes,
-                "hbm_gbps_algorithmic": nbytes / s_ / 1e9, "hbm_frac_algorithmic": nbytes / s_ / 1e9 / HBM_PEAK_GBPS}
-
-    fwd = rates(fwd_ms, fwd_bytes)
-    bwd = rates(bwd_ms, bwd_bytes)
+    fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems)
+    bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems)
     dom_k, dom, dom_bytes = (["sampling_vt_fwd", "bev_align_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
         (["fill_zero_f32", "sampling_vt_bwd", "bev_align_bwd"], bwd, bwd_bytes)
-    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload)
-    line = {
-        "metric": METRIC,
-        "value": out_elems / (ms_step * 1e-3),
-        "unit": "BEV output elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
-                "seeded planar ego motion",
-        "config": {"workload": f"{args.workload}: Sampling-VT B={B} N={N} C={C} HxW={H}x{W} grid {X}x{Y}x{Z} "
-                               f"stacked with a Cp={Cp} previous BEV map resampled under the ego motion, one step = "
-                               f"forward + backward", "B": B, "N": N, "C": C, "Cp": Cp, "H": H, "W": W, "X": X, "Y": Y,
-                   "Z": Z},
-        "forward": fwd,
-        "backward": bwd,
-        "roofline": roofline,
-    }
+    line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
+                      "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
+                      "seeded planar ego motion",
+                      {"workload": f"{args.workload}: Sampling-VT B={B} N={N} C={C} HxW={H}x{W} grid {X}x{Y}x{Z} "
+                                   f"stacked with a Cp={Cp} previous BEV map resampled under the ego motion, one step "
+                                   f"= forward + backward", "B": B, "N": N, "C": C, "Cp": Cp, "H": H, "W": W, "X": X,
+                       "Y": Y, "Z": Z})
+    line.update({"forward": fwd, "backward": bwd, "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload)})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline_temporal(ti)
@@ -688,37 +565,7 @@ def main():
     valid_tuples = int(cnt.to(torch.int64).sum().item())
     del cnt
 
-    def step():
-        fwd_call(out=out)
-        return bwd_call()
-
-    log(f"[bench] warmup {args.warmup} steps on {args.workload}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    calibration_copy(args, dev)
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        fwd_call(out=out)
-        ev[k][1].record(stream)
-        bwd_call()
-        ev[k][2].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    log(f"[bench] done: {ms_step * 1e3:.2f} us/step (fwd {fwd_ms * 1e3:.2f} us, bwd {bwd_ms * 1e3:.2f} us)")
-
+    ms_step, (fwd_ms, bwd_ms) = time_passes(args, dev, [lambda: fwd_call(out=out), bwd_call], args.workload)
     out_elems = B * C * X * Y
     cam_bytes = B * N * 21 * 4
     feat_bytes = B * N * P * C * es
@@ -726,43 +573,23 @@ def main():
     bwd_bytes = out_elems * 4 + B * N * P * C * 4 + cam_bytes      # grad_out once, dL/dF once
     samples = valid_tuples * C * nlev                              # one bilinear sample per level
     logical = B * N * C * X * Y * Z * nlev
-
-    def rates(ms, nbytes):
-        s = ms * 1e-3
-        return {"ms": ms, "out_elems_per_s": out_elems / s, "bilinear_samples_per_s": samples / s,
-                "logical_samples_per_s": logical / s, "algorithmic_bytes": nbytes,
-                "hbm_gbps_algorithmic": nbytes / s / 1e9, "hbm_frac_algorithmic": nbytes / s / 1e9 / HBM_PEAK_GBPS}
-
-    fwd = rates(fwd_ms, fwd_bytes)
-    bwd = rates(bwd_ms, bwd_bytes)
+    fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems, bilinear_samples_per_s=samples,
+                     logical_samples_per_s=logical)
+    bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems, bilinear_samples_per_s=samples,
+                     logical_samples_per_s=logical)
     # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch
     # per feature level)
     dom_k, dom, dom_bytes = (["sampling_vt_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
         (["fill_zero_f32"] + ["sampling_vt_bwd"] * nlev, bwd, bwd_bytes)
-    roofline = pass_roofline(dom_k, dom, dom_bytes, args.workload, exact_traffic=(nlev == 1))
-
-    line = {
-        "metric": METRIC,
-        "value": out_elems / (ms_step * 1e-3),
-        "unit": "BEV output elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
-        "data": "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
-        "config": {"workload": f"{args.workload}: B={B} N={N} C={C} {desc} {inp.dtype} -> "
-                               f"X*Y*Z={X}x{Y}x{Z}, one step = forward + backward",
-                   "B": B, "N": N, "C": C, "H": H, "W": W, "levels": nlev, "X": X, "Y": Y, "Z": Z,
-                   "valid_samples_per_pass": valid_tuples},
-        "bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3),
-        "forward": fwd,
-        "backward": bwd,
-        "roofline": roofline,
-    }
+    line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step,
+                      "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
+                      "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
+                      {"workload": f"{args.workload}: B={B} N={N} C={C} {desc} {inp.dtype} -> "
+                                   f"X*Y*Z={X}x{Y}x{Z}, one step = forward + backward",
+                       "B": B, "N": N, "C": C, "H": H, "W": W, "levels": nlev, "X": X, "Y": Y, "Z": Z,
+                       "valid_samples_per_pass": valid_tuples})
+    line.update({"bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3), "forward": fwd, "backward": bwd,
+                 "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload, exact_traffic=(nlev == 1))})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = baseline(inp, args.cpu_rows or X)

@@ -33,9 +33,8 @@ fbev_status fail(fbev_status s, const char* fmt, ...) {
 
 bool finite_range(float lo, float hi) { return std::isfinite(lo) && std::isfinite(hi) && hi > lo; }
 
-// Shared validation of the geometry arguments; fills `p` on success.
-fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* R, const float* t,
-                         const fbev_range& r, int32_t X, int32_t Y, int32_t Z, fbev::Problem& p) {
+// Validation of the sizes of a Sampling-VT problem (features and grid).
+fbev_status check_sizes(const fbev_feat_desc& fd, int32_t X, int32_t Y, int32_t Z) {
   if (fd.B < 0 || fd.N < 0 || fd.C < 0 || fd.H < 0 || fd.W < 0)
     return fail(FBEV_ERR_INVALID_ARGUMENT, "negative feature size (B=%d N=%d C=%d H=%d W=%d)", fd.B, fd.N, fd.C,
                 fd.H, fd.W);
@@ -46,6 +45,14 @@ fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* 
     return fail(FBEV_ERR_INVALID_ARGUMENT, "N=%d cameras exceeds FBEV_MAX_CAMERAS=%d", fd.N, FBEV_MAX_CAMERAS);
   if (fd.H > FBEV_MAX_GRID || fd.W > FBEV_MAX_GRID)
     return fail(FBEV_ERR_INVALID_ARGUMENT, "feature map %dx%d above %d", fd.H, fd.W, FBEV_MAX_GRID);
+  return FBEV_OK;
+}
+
+// Shared validation of the geometry arguments; fills `p` on success.
+fbev_status check_common(const fbev_feat_desc& fd, const float* K, const float* R, const float* t,
+                         const fbev_range& r, int32_t X, int32_t Y, int32_t Z, fbev::Problem& p) {
+  const fbev_status st = check_sizes(fd, X, Y, Z);
+  if (st != FBEV_OK) return st;
   if (!finite_range(r.x_min, r.x_max) || !finite_range(r.y_min, r.y_max) || !finite_range(r.z_min, r.z_max))
     return fail(FBEV_ERR_INVALID_ARGUMENT, "each BEV range axis needs finite min < max");
   if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
@@ -201,14 +208,21 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
                        "fbev_backward_temporal launch");
 }
 
-// Camera gradients: geometry checks of the single-level forward, fp32 features.
+// Camera gradients: the sizes of a single-level problem with fp32 features;
+// fills the size fields of `p` (all the workspace size depends on).
 fbev_status check_cameras(const fbev_feat_desc& fd, int32_t X, int32_t Y, int32_t Z, fbev::Problem& p) {
-  const fbev_range unit{0.f, 1.f, 0.f, 1.f, 0.f, 1.f};
-  static const float dummy = 0.f;
-  fbev_status s = check_common(fd, &dummy, &dummy, &dummy, unit, X, Y, Z, p);
+  fbev_status s = check_sizes(fd, X, Y, Z);
   if (s != FBEV_OK) return s;
   s = check_levels(fd, 1, nullptr, p);
   if (s != FBEV_OK) return s;
+  p.B = fd.B;
+  p.N = fd.N;
+  p.C = fd.C;
+  p.H = fd.H;
+  p.W = fd.W;
+  p.X = X;
+  p.Y = Y;
+  p.Z = Z;
   const int64_t batch_elems = (int64_t)fd.N * fd.H * fd.W * fd.C;
   if (batch_elems >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld elements (limit 2^31 - 1)",
