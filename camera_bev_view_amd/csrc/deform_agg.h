@@ -25,6 +25,7 @@ struct DeformArgs {
   float* ganchors;         // backward: [B,Q,3] or NULL
   int B, N, C, H, W, Q, Kp;
   int q_stride;            // set by the backward's launcher
+  int wq_n;                // waves per query in the backward (set by its launcher)
 };
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream);

@@ -11,8 +11,8 @@
 // query's output is the sum.  Nothing per (query, keypoint, camera) reaches
 // device memory.
 //
-// Forward: a wave owns a query at a time.  Phase A takes one (camera,
-// keypoint) pair per lane: fp64 projection, sign tests for the in-view rule,
+// Forward: a wave owns a (query, 64-channel block).  Phase A takes one
+// (camera, keypoint) pair per lane: fp64 projection, sign tests for the in-view rule,
 // then the four taps and their weights (bilinear x attention) for the pairs
 // in view, compacted into a per-wave LDS list of tap records.  Phase C
 // gathers with lanes = channels: each record is one coalesced row of the
@@ -20,12 +20,15 @@
 // of [B, Q, C] leaves coalesced.
 //
 // Backward: the same phase A lists the in-view samples with their fractions
-// and depths.  Per sample, lanes = channels load the four taps once and give
-// (i) the feature gradient, one 64-lane atomic per tap, (ii) dL/dw = <sample,
-// g> and (iii) dL/du, dL/dv = w <dsample/du, g>, w <dsample/dv, g>, three wave
-// reductions; the keypoint gradient is then dL/du du/dp + dL/dv dv/dp with
-// du/dp = (P_1 - u P_3) / h_3 (rows of the 3x3 part of P = K [R | t]),
-// summed over cameras per keypoint in LDS.
+// and depths; a query's 64-channel blocks are spread over up to four waves of
+// one workgroup.  (i) The feature gradient: all samples of a query scatter
+// w x tap weight x g with the query's one g, so the pass's taps are merged per
+// pixel in an LDS hash table (weights added) and each distinct pixel gets one
+// 64-lane atomic per channel block.  Per sample, lanes = channels load the
+// four taps once and give (ii) the wave's part of dL/dw = <sample, g> and
+// (iii) of dL/du, dL/dv = w <dsample/du, g>, w <dsample/dv, g>.  The parts are added in wave order; the keypoint gradient
+// is then dL/du du/dp + dL/dv dv/dp with du/dp = (P_1 - u P_3) / h_3 (rows of
+// the 3x3 part of P = K [R | t]), summed over cameras per keypoint in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -209,6 +212,10 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
   if (ch) a.out[bq * a.C + c] = acc;
 }
 
+constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together
+constexpr int kTabBits = 9;
+constexpr int kTab = 1 << kTabBits;      // per-wave hash table of a pass's tap pixels (at most 4 x 64 keys)
+
 // Per-wave LDS of the backward: the in-view samples of one pass.
 struct SampleRec {
   int p00, dx, dy, idx;   // taps as in Taps; idx = n * Kp + k
@@ -216,123 +223,224 @@ struct SampleRec {
   double u, v, h2;
 };
 
+// Backward: a query's 64-channel blocks are spread over wq_n waves of one
+// workgroup (qw_n = 4 / wq_n queries per workgroup).  Every wave lists the
+// query's in-view samples itself; per sample it loads its channels of the four
+// taps, adds w * tap weight * g to dL/dF with atomics and forms its part of
+// <sample, g>, <d sample/du, g>, <d sample/dv, g>.  After a pass the parts are
+// added in wave order (fixed), lane s of the query's first wave turns sample s's
+// sums into dL/dw and its keypoint's gradient through the projection, and lane
+// k adds the pass's contributions to keypoint k in sample order: dL/dw,
+// dL/doffsets and dL/danchors are deterministic.
 __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
   SampleRec* sS = reinterpret_cast<SampleRec*>(smem + sizeof(double) * 12 * a.N);           // [kWaves][kWave]
-  float* sG = reinterpret_cast<float*>(sS + kWaves * kWave);                                // [kWaves][Kp][3]
+  float* sPart = reinterpret_cast<float*>(sS + kWaves * kWave);                             // [kWaves][kWave][4]
+  float* sCon = sPart + kWaves * kWave * 4;                                                 // [kWaves][kWave][4]
+  int* sKey = reinterpret_cast<int*>(sCon + kWaves * kWave * 4);                            // [kWaves][kTab]
+  float* sWt = reinterpret_cast<float*>(sKey + kWaves * kTab);                               // [kWaves][kTab]
+  int2* sUq = reinterpret_cast<int2*>(sWt + kWaves * kTab);                                  // [kWaves][4 * kWave]
+  float* sG = reinterpret_cast<float*>(sUq + kWaves * 4 * kWave);                            // [kWaves][Kp][3]
   const int b = blockIdx.y;
   stage_projections(sP, a.K, a.R, a.t, b, a.N);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = uniform(threadIdx.x / kWave);
+  const int wq_n = a.wq_n, qs = wid / wq_n, wq = wid - qs * wq_n;
+  const int lead = qs * wq_n;                          // the query's first wave
   SampleRec* smp = sS + wid * kWave;
-  float* gk = sG + wid * a.Kp * 3;
+  int* tkey = sKey + wid * kTab;
+  float* twt = sWt + wid * kTab;
+  int2* uq = sUq + wid * 4 * kWave;
   const int NK = a.N * a.Kp;
   const size_t HWC = (size_t)a.H * a.W * a.C;
   const float* fb = a.feat + (size_t)b * a.N * HWC;
   float* gfb = a.gfeat + (size_t)b * a.N * HWC;
 
-  {
-    // one query per wave, visited in the order q = unit * stride mod Q (stride coprime to Q), which
-    // spreads the waves that run at the same time over the image and so over the atomics' addresses
-    const int unit = blockIdx.x * kWaves + wid;
-    if (unit >= a.Q) return;                          // no barrier follows
-    const int q = (int)(((long long)unit * a.q_stride) % a.Q);
-    const size_t bq = (size_t)b * a.Q + q;
-    const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
-    const float* gq = a.grad + bq * a.C;
+  // queries visited in the order q = unit * stride mod Q (stride coprime to Q), which spreads the
+  // waves that run at the same time over the image and so over the atomics' addresses
+  const int unit = blockIdx.x * (kWaves / wq_n) + qs;
+  const bool active = unit < a.Q;                     // inactive waves still take every barrier
+  const int q = active ? (int)(((long long)unit * a.q_stride) % a.Q) : 0;
+  const size_t bq = (size_t)b * a.Q + q;
+  const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
+  const float* gq = a.grad + bq * a.C;
+  float* gk = sG + qs * a.Kp * 3;
+  if (wq == 0)
     for (int e = lane; e < a.Kp * 3; e += kWave) gk[e] = 0.f;
+  for (int base = 0; base < NK; base += kWave) {
+    // ---- listing, as in the forward; out-of-view pairs get dL/dw = 0 (first wave of the query)
+    const int idx = base + lane;
+    bool valid = false;
+    Proj pr;
+    int n = 0;
+    if (active && idx < NK) {
+      n = idx / a.Kp;
+      const int k = idx - n * a.Kp;
+      const float* o = a.offsets + (bq * a.Kp + k) * 3;
+      pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
+      valid = pr.valid;
+      if (!valid && wq == 0) a.gweights[bq * NK + idx] = 0.f;
+    }
+    const uint64_t m = __ballot(valid);
+    const int cnt = (int)__builtin_popcountll(m);
+    if (valid) {
+      const Taps tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
+      const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      smp[s] = SampleRec{tp.p00, tp.dx, tp.dy, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
+    }
+    for (int e = lane; e < kTab; e += kWave) {
+      tkey[e] = -1;
+      twt[e] = 0.f;
+    }
     wave_lds_sync();
-    for (int base = 0; base < NK; base += kWave) {
-      // ---- phase A, as in the forward; out-of-view pairs get dL/dw = 0 here
-      const int idx = base + lane;
-      bool valid = false;
-      Proj pr;
-      int n = 0;
-      if (idx < NK) {
-        n = idx / a.Kp;
-        const int k = idx - n * a.Kp;
-        const float* o = a.offsets + (bq * a.Kp + k) * 3;
-        pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
-        valid = pr.valid;
-        if (!valid) a.gweights[bq * NK + idx] = 0.f;
+    // ---- the pass's taps merged per pixel: every sample of a query scatters w x tap weight x g with
+    // the same g, so taps on one pixel add their weights and leave as one atomic per channel
+    if (lane < cnt) {
+      const SampleRec sr = smp[lane];
+      const float wa0 = (1.f - sr.a) * sr.w, wa1 = sr.a * sr.w;
+      const float wt[4] = {wa0 * (1.f - sr.b), wa1 * (1.f - sr.b), wa0 * sr.b, wa1 * sr.b};
+      const int px[4] = {sr.p00, sr.p00 + sr.dx, sr.p00 + sr.dy, sr.p00 + sr.dy + sr.dx};
+      for (int t = 0; t < 4; ++t) {
+        if (wt[t] == 0.f) continue;
+        uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - kTabBits);
+        for (;;) {                                  // at most 4 * 64 keys in 2 * 4 * 64 slots: a free one exists
+          const int old = atomicCAS(&tkey[h], -1, px[t]);
+          if (old == -1 || old == px[t]) break;
+          h = (h + 1) & (kTab - 1);
+        }
+        atomicAdd(&twt[h], wt[t]);
       }
-      const uint64_t m = __ballot(valid);
-      const int cnt = (int)__builtin_popcountll(m);
-      if (valid) {
-        const Taps tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
-        const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-        smp[s] = SampleRec{tp.p00, tp.dx, tp.dy, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
+    }
+    wave_lds_sync();
+    int nu = 0;
+    for (int e0 = 0; e0 < kTab; e0 += kWave) {
+      const int key = tkey[e0 + lane];
+      const uint64_t mk = __ballot(key >= 0);
+      if (key >= 0)
+        uq[nu + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u))] =
+            make_int2(key, __float_as_int(twt[e0 + lane]));
+      nu += (int)__builtin_popcountll(mk);
+    }
+    wave_lds_sync();
+    // ---- per in-view sample: this wave's channels of the three sums, four samples at a time with
+    // all their tap loads in flight (past the list's end the last sample is read again, unused)
+    for (int s0 = 0; s0 < cnt; s0 += kSampUnroll) {
+      int p00[kSampUnroll], dx[kSampUnroll], dy[kSampUnroll];
+      float fa[kSampUnroll], fbt[kSampUnroll];
+#pragma unroll
+      for (int i = 0; i < kSampUnroll; ++i) {
+        const SampleRec sr = smp[min(s0 + i, cnt - 1)];
+        p00[i] = uniform(sr.p00);
+        dx[i] = uniform(sr.dx);
+        dy[i] = uniform(sr.dy);
+        fa[i] = sr.a;
+        fbt[i] = sr.b;
       }
+      float ds[kSampUnroll], du[kSampUnroll], dv[kSampUnroll];
+#pragma unroll
+      for (int i = 0; i < kSampUnroll; ++i) ds[i] = du[i] = dv[i] = 0.f;
+      for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) {
+        const float g = gq[c];
+        float F[kSampUnroll][4];
+#pragma unroll
+        for (int i = 0; i < kSampUnroll; ++i) {
+          F[i][0] = fb[(size_t)p00[i] + c];
+          F[i][1] = fb[(size_t)p00[i] + dx[i] + c];
+          F[i][2] = fb[(size_t)p00[i] + dy[i] + c];
+          F[i][3] = fb[(size_t)p00[i] + dy[i] + dx[i] + c];
+        }
+#pragma unroll
+        for (int i = 0; i < kSampUnroll; ++i) {
+          const float a0 = 1.f - fa[i], b0 = 1.f - fbt[i];
+          const float smpv = a0 * b0 * F[i][0] + fa[i] * b0 * F[i][1] + a0 * fbt[i] * F[i][2] + fa[i] * fbt[i] * F[i][3];
+          const float su = b0 * (F[i][1] - F[i][0]) + fbt[i] * (F[i][3] - F[i][2]);
+          const float sv = a0 * (F[i][2] - F[i][0]) + fa[i] * (F[i][3] - F[i][1]);
+          ds[i] = fmaf(g, smpv, ds[i]);
+          du[i] = fmaf(g, su, du[i]);
+          dv[i] = fmaf(g, sv, dv[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kSampUnroll; ++i) {
+        const float x = wave_sum(ds[i]), y = wave_sum(du[i]), z = wave_sum(dv[i]);
+        if (lane == 0 && s0 + i < cnt) *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + i) * 4) = make_float4(x, y, z, 0.f);
+      }
+    }
+    // ---- the feature gradient: one atomic per (merged pixel, channel)
+    for (int e = 0; e < nu; ++e) {
+      const int2 t = uq[e];
+      const int pix = uniform(t.x);
+      const float ws = __int_as_float(uniform(t.y));
+      for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) unsafeAtomicAdd(gfb + (size_t)pix + c, ws * gq[c]);
+    }
+    __syncthreads();
+    // ---- the query's first wave: sums over its waves (wave order), dL/dw, keypoint contributions
+    if (wq == 0 && lane < cnt) {
+      float4 t = *reinterpret_cast<const float4*>(sPart + (lead * kWave + lane) * 4);
+      for (int j = 1; j < wq_n; ++j) {
+        const float4 o = *reinterpret_cast<const float4*>(sPart + ((lead + j) * kWave + lane) * 4);
+        t.x += o.x;
+        t.y += o.y;
+        t.z += o.z;
+      }
+      const SampleRec sr = smp[lane];
+      const int sn = sr.idx / a.Kp;
+      a.gweights[bq * NK + sr.idx] = t.x;
+      // keypoint gradient through the projection: du/dp = (P_1 - u P_3) / h_3, dv/dp likewise
+      const double* P = sP + sn * 12;
+      const double ih = 1.0 / sr.h2;
+      const double lu = (double)sr.w * t.y, lv = (double)sr.w * t.z;
+      float c3[3];
+      for (int r = 0; r < 3; ++r) {
+        const double ju = (P[r] - sr.u * P[8 + r]) * ih, jv = (P[4 + r] - sr.v * P[8 + r]) * ih;
+        c3[r] = (float)(lu * ju + lv * jv);
+      }
+      *reinterpret_cast<float4*>(sCon + (wid * kWave + lane) * 4) = make_float4(c3[0], c3[1], c3[2], 0.f);
+    }
+    if (wq == 0) {
       wave_lds_sync();
-      // ---- per in-view sample: feature scatter, dL/dw, dL/du and dL/dv
-      for (int s = 0; s < cnt; ++s) {
-        const SampleRec sr = smp[s];
-        const int p00 = uniform(sr.p00), dx = uniform(sr.dx), dy = uniform(sr.dy);
-        const float fa = sr.a, fbt = sr.b, w = sr.w;
-        const float w00 = (1.f - fa) * (1.f - fbt), w01 = fa * (1.f - fbt), w10 = (1.f - fa) * fbt, w11 = fa * fbt;
-        float ds = 0.f, du = 0.f, dv = 0.f;
-        for (int c = lane; c < a.C; c += kWave) {
-          const float g = gq[c];
-          const float F00 = fb[(size_t)p00 + c], F01 = fb[(size_t)p00 + dx + c];
-          const float F10 = fb[(size_t)p00 + dy + c], F11 = fb[(size_t)p00 + dy + dx + c];
-          const float smpv = w00 * F00 + w01 * F01 + w10 * F10 + w11 * F11;
-          const float su = (1.f - fbt) * (F01 - F00) + fbt * (F11 - F10);
-          const float sv = (1.f - fa) * (F10 - F00) + fa * (F11 - F01);
-          ds = fmaf(g, smpv, ds);
-          du = fmaf(g, su, du);
-          dv = fmaf(g, sv, dv);
-          const float wg = w * g;
-          unsafeAtomicAdd(gfb + (size_t)p00 + c, w00 * wg);
-          unsafeAtomicAdd(gfb + (size_t)p00 + dx + c, w01 * wg);
-          unsafeAtomicAdd(gfb + (size_t)p00 + dy + c, w10 * wg);
-          unsafeAtomicAdd(gfb + (size_t)p00 + dy + dx + c, w11 * wg);
+      // lane k adds the contributions of this pass's samples of keypoint k, in sample order
+      for (int kk = lane; kk < a.Kp; kk += kWave) {
+        float gx = gk[kk * 3], gy = gk[kk * 3 + 1], gz = gk[kk * 3 + 2];
+        for (int s = 0; s < cnt; ++s) {
+          if (smp[s].idx % a.Kp != kk) continue;
+          const float4 c = *reinterpret_cast<const float4*>(sCon + (wid * kWave + s) * 4);
+          gx += c.x;
+          gy += c.y;
+          gz += c.z;
         }
-        ds = wave_sum(ds);
-        du = wave_sum(du);
-        dv = wave_sum(dv);
-        if (lane == 0) {
-          const int sidx = sr.idx;
-          const int n = sidx / a.Kp, k = sidx - n * a.Kp;
-          a.gweights[bq * NK + sidx] = ds;
-          // keypoint gradient through the projection: du/dp = (P_1 - u P_3) / h_3, dv/dp likewise
-          const double* P = sP + n * 12;
-          const double ih = 1.0 / sr.h2;
-          const double lu = (double)w * du, lv = (double)w * dv;
-          for (int r = 0; r < 3; ++r) {
-            const double ju = (P[r] - sr.u * P[8 + r]) * ih, jv = (P[4 + r] - sr.v * P[8 + r]) * ih;
-            gk[k * 3 + r] += (float)(lu * ju + lv * jv);
-          }
-        }
-        wave_lds_sync();
+        gk[kk * 3] = gx;
+        gk[kk * 3 + 1] = gy;
+        gk[kk * 3 + 2] = gz;
       }
     }
-    // the query's keypoint and anchor gradients
-    wave_lds_sync();
-    float sx = 0.f, sy = 0.f, sz = 0.f;
-    for (int k = lane; k < a.Kp; k += kWave) {
-      const float gx = gk[k * 3], gy = gk[k * 3 + 1], gz = gk[k * 3 + 2];
-      float* go = a.goffsets + (bq * a.Kp + k) * 3;
-      go[0] = gx;
-      go[1] = gy;
-      go[2] = gz;
-      sx += gx;
-      sy += gy;
-      sz += gz;
+    __syncthreads();   // the sample lists and parts are rewritten by the next pass
+  }
+  // ---- the query's keypoint and anchor gradients (first wave)
+  if (!active || wq != 0) return;                      // no barrier follows
+  float sx = 0.f, sy = 0.f, sz = 0.f;
+  for (int k = lane; k < a.Kp; k += kWave) {
+    const float gx = gk[k * 3], gy = gk[k * 3 + 1], gz = gk[k * 3 + 2];
+    float* go = a.goffsets + (bq * a.Kp + k) * 3;
+    go[0] = gx;
+    go[1] = gy;
+    go[2] = gz;
+    sx += gx;
+    sy += gy;
+    sz += gz;
+  }
+  if (a.ganchors != nullptr) {
+    sx = wave_sum(sx);
+    sy = wave_sum(sy);
+    sz = wave_sum(sz);
+    if (lane == 0) {
+      a.ganchors[bq * 3] = sx;
+      a.ganchors[bq * 3 + 1] = sy;
+      a.ganchors[bq * 3 + 2] = sz;
     }
-    if (a.ganchors != nullptr) {
-      sx = wave_sum(sx);
-      sy = wave_sum(sy);
-      sz = wave_sum(sz);
-      if (lane == 0) {
-        a.ganchors[bq * 3] = sx;
-        a.ganchors[bq * 3 + 1] = sy;
-        a.ganchors[bq * 3 + 2] = sz;
-      }
-    }
-    wave_lds_sync();
   }
 }
 
@@ -372,8 +480,14 @@ hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.B == 0 || a.Q == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.Q + kWaves - 1) / kWaves), (unsigned)a.B);
-  const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves + sizeof(float) * 3 * a.Kp * kWaves;
+  // waves per query: one per 64-channel block, up to the workgroup's four (a power of two dividing four)
+  const int blocks = (a.C + kWave - 1) / kWave;
+  a.wq_n = blocks >= 3 ? 4 : (blocks == 2 ? 2 : 1);
+  const int qw_n = kWaves / a.wq_n;
+  const dim3 grid((unsigned)((a.Q + qw_n - 1) / qw_n), (unsigned)a.B);
+  const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves +
+                       2 * sizeof(float) * 4 * kWave * kWaves + (sizeof(int) + sizeof(float)) * kTab * kWaves +
+                       sizeof(int2) * 4 * kWave * kWaves + sizeof(float) * 3 * a.Kp * kWaves;
   hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }
