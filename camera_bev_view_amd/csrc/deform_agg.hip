@@ -56,13 +56,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
+
+// Sum over the 16 lanes of each row: quad swaps, then mirrors across each half and the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kHalfMirror>(x);
+  return x + dpp<kRowMirror>(x);
+}
+
+// x + the same register of the lane in the other row pair (permlane16: rows 0<->1, 2<->3)
+// or the other half-wave (permlane32), pairing value x with value y so one swap serves both:
+// the lanes that kept x hold x's pair sum, the others y's.
+__device__ __forceinline__ float swap16_add(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_add(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  x = swap16_add(x, x);
+  return swap32_add(x, x);
+}
+
+// Twelve wave sums at once, v[3 i + j] = sum j (0..2) of sample i (0..3): each swap halves
+// the values a lane carries, so afterwards the 16 lanes of row i hold sample i's sums z[0..2].
+__device__ __forceinline__ void wave_sum_4x3(const float (&v)[12], float (&z)[3]) {
+  float w[6];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) w[k] = swap32_add(v[k], v[k + 6]);       // lower half: v[k], upper: v[k + 6]
+#pragma unroll
+  for (int k = 0; k < 3; ++k) z[k] = row_sum16(swap16_add(w[k], w[k + 3]));   // row r: v[k + 3 r]
 }
 
 // 1/x in double: hardware estimate and two Newton steps.
@@ -212,7 +245,7 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
   if (ch) a.out[bq * a.C + c] = acc;
 }
 
-constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together
+constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together (one per lane row)
 constexpr int kTabBits = 9;
 constexpr int kTab = 1 << kTabBits;      // per-wave hash table of a pass's tap pixels (at most 4 x 64 keys)
 
@@ -237,11 +270,8 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
   SampleRec* sS = reinterpret_cast<SampleRec*>(smem + sizeof(double) * 12 * a.N);           // [kWaves][kWave]
   float* sPart = reinterpret_cast<float*>(sS + kWaves * kWave);                             // [kWaves][kWave][4]
-  float* sCon = sPart + kWaves * kWave * 4;                                                 // [kWaves][kWave][4]
-  int* sKey = reinterpret_cast<int*>(sCon + kWaves * kWave * 4);                            // [kWaves][kTab]
-  float* sWt = reinterpret_cast<float*>(sKey + kWaves * kTab);                               // [kWaves][kTab]
-  int2* sUq = reinterpret_cast<int2*>(sWt + kWaves * kTab);                                  // [kWaves][4 * kWave]
-  float* sG = reinterpret_cast<float*>(sUq + kWaves * 4 * kWave);                            // [kWaves][Kp][3]
+  int2* sTab = reinterpret_cast<int2*>(sPart + kWaves * kWave * 4);                         // [kWaves][kTab]
+  float* sG = reinterpret_cast<float*>(sTab + kWaves * kTab);                                // [kWaves][Kp][3]
   const int b = blockIdx.y;
   stage_projections(sP, a.K, a.R, a.t, b, a.N);
   __syncthreads();
@@ -251,9 +281,8 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   const int wq_n = a.wq_n, qs = wid / wq_n, wq = wid - qs * wq_n;
   const int lead = qs * wq_n;                          // the query's first wave
   SampleRec* smp = sS + wid * kWave;
-  int* tkey = sKey + wid * kTab;
-  float* twt = sWt + wid * kTab;
-  int2* uq = sUq + wid * 4 * kWave;
+  int2* tab = sTab + wid * kTab;                       // (pixel, merged weight bits); compacted in place
+  float* con = sPart + wid * kWave * 4;                // keypoint contributions, over the parts once read
   const int NK = a.N * a.Kp;
   const size_t HWC = (size_t)a.H * a.W * a.C;
   const float* fb = a.feat + (size_t)b * a.N * HWC;
@@ -291,10 +320,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
       smp[s] = SampleRec{tp.p00, tp.dx, tp.dy, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
     }
-    for (int e = lane; e < kTab; e += kWave) {
-      tkey[e] = -1;
-      twt[e] = 0.f;
-    }
+    for (int e = lane; e < kTab; e += kWave) tab[e] = make_int2(-1, 0);
     wave_lds_sync();
     // ---- the pass's taps merged per pixel: every sample of a query scatters w x tap weight x g with
     // the same g, so taps on one pixel add their weights and leave as one atomic per channel
@@ -307,21 +333,21 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
         if (wt[t] == 0.f) continue;
         uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - kTabBits);
         for (;;) {                                  // at most 4 * 64 keys in 2 * 4 * 64 slots: a free one exists
-          const int old = atomicCAS(&tkey[h], -1, px[t]);
+          const int old = atomicCAS(&tab[h].x, -1, px[t]);
           if (old == -1 || old == px[t]) break;
           h = (h + 1) & (kTab - 1);
         }
-        atomicAdd(&twt[h], wt[t]);
+        atomicAdd(reinterpret_cast<float*>(&tab[h].y), wt[t]);
       }
     }
     wave_lds_sync();
+    // compaction in place: an entry moves only to a lower slot, one the wave has already read
     int nu = 0;
     for (int e0 = 0; e0 < kTab; e0 += kWave) {
-      const int key = tkey[e0 + lane];
-      const uint64_t mk = __ballot(key >= 0);
-      if (key >= 0)
-        uq[nu + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u))] =
-            make_int2(key, __float_as_int(twt[e0 + lane]));
+      const int2 ent = tab[e0 + lane];
+      const uint64_t mk = __ballot(ent.x >= 0);
+      if (ent.x >= 0)
+        tab[nu + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u))] = ent;
       nu += (int)__builtin_popcountll(mk);
     }
     wave_lds_sync();
@@ -363,15 +389,21 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
           dv[i] = fmaf(g, sv, dv[i]);
         }
       }
+      float v[3 * kSampUnroll], z[3];
 #pragma unroll
       for (int i = 0; i < kSampUnroll; ++i) {
-        const float x = wave_sum(ds[i]), y = wave_sum(du[i]), z = wave_sum(dv[i]);
-        if (lane == 0 && s0 + i < cnt) *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + i) * 4) = make_float4(x, y, z, 0.f);
+        v[3 * i] = ds[i];
+        v[3 * i + 1] = du[i];
+        v[3 * i + 2] = dv[i];
       }
+      wave_sum_4x3(v, z);
+      const int row = lane >> 4;
+      if ((lane & 15) == 0 && s0 + row < cnt)
+        *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + row) * 4) = make_float4(z[0], z[1], z[2], 0.f);
     }
     // ---- the feature gradient: one atomic per (merged pixel, channel)
     for (int e = 0; e < nu; ++e) {
-      const int2 t = uq[e];
+      const int2 t = tab[e];
       const int pix = uniform(t.x);
       const float ws = __int_as_float(uniform(t.y));
       for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) unsafeAtomicAdd(gfb + (size_t)pix + c, ws * gq[c]);
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
         const double ju = (P[r] - sr.u * P[8 + r]) * ih, jv = (P[4 + r] - sr.v * P[8 + r]) * ih;
         c3[r] = (float)(lu * ju + lv * jv);
       }
-      *reinterpret_cast<float4*>(sCon + (wid * kWave + lane) * 4) = make_float4(c3[0], c3[1], c3[2], 0.f);
+      *reinterpret_cast<float4*>(con + lane * 4) = make_float4(c3[0], c3[1], c3[2], 0.f);   // this lane's parts are read
     }
     if (wq == 0) {
       wave_lds_sync();
@@ -407,7 +439,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
         float gx = gk[kk * 3], gy = gk[kk * 3 + 1], gz = gk[kk * 3 + 2];
         for (int s = 0; s < cnt; ++s) {
           if (smp[s].idx % a.Kp != kk) continue;
-          const float4 c = *reinterpret_cast<const float4*>(sCon + (wid * kWave + s) * 4);
+          const float4 c = *reinterpret_cast<const float4*>(con + s * 4);
           gx += c.x;
           gy += c.y;
           gz += c.z;
@@ -486,8 +518,8 @@ hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream) {
   const int qw_n = kWaves / a.wq_n;
   const dim3 grid((unsigned)((a.Q + qw_n - 1) / qw_n), (unsigned)a.B);
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves +
-                       2 * sizeof(float) * 4 * kWave * kWaves + (sizeof(int) + sizeof(float)) * kTab * kWaves +
-                       sizeof(int2) * 4 * kWave * kWaves + sizeof(float) * 3 * a.Kp * kWaves;
+                       sizeof(float) * 4 * kWave * kWaves + sizeof(int2) * kTab * kWaves +
+                       sizeof(float) * 3 * a.Kp * kWaves;
   hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }
