@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace fbev {
 namespace {
@@ -51,29 +52,12 @@ static_assert(kMaxGroups <= kFinishPer * kWave, "the finish reads every slice in
 
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ double recip(double x) {
   double r = __builtin_amdgcn_rcp(x);
   r = fma(r, fma(-x, r, 1.0), r);
   r = fma(r, fma(-x, r, 1.0), r);
   return r;
 }
-
-// x of another lane of the same row of 16 (DPP): kQuadSwap1 / kQuadSwap2 swap
-// neighbours / pairs within a quad, kHalfMirror mirrors within 8 lanes,
-// kRowMirror within 16.
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
 
 // Four row sums at once: d[q] holds lane j's part of value q (j = lane % 16);
 // afterwards every lane of quad q of the row (j / 4 == q) holds the row's sum

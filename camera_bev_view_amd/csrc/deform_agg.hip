@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include "deform_agg.h"
+#include "wave_ops.h"
 
 namespace fbev {
 namespace {
@@ -47,46 +48,6 @@ struct TapRec {
   int off;      // element offset of the tap's channel row within the batch sample
   float w;      // bilinear weight x attention weight
 };
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
-
-// Sum over the 16 lanes of each row: quad swaps, then mirrors across each half and the row.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp<kQuadSwap1>(x);
-  x += dpp<kQuadSwap2>(x);
-  x += dpp<kHalfMirror>(x);
-  return x + dpp<kRowMirror>(x);
-}
-
-// x + the same register of the lane in the other row pair (permlane16: rows 0<->1, 2<->3)
-// or the other half-wave (permlane32), pairing value x with value y so one swap serves both:
-// the lanes that kept x hold x's pair sum, the others y's.
-__device__ __forceinline__ float swap16_add(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap32_add(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row_sum16(x);
-  x = swap16_add(x, x);
-  return swap32_add(x, x);
-}
 
 // Twelve wave sums at once, v[3 i + j] = sum j (0..2) of sample i (0..3): each swap halves
 // the values a lane carries, so afterwards the 16 lanes of row i hold sample i's sums z[0..2].

@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include "lift_splat.h"
+#include "wave_ops.h"
 
 namespace fbev {
 namespace {
@@ -47,23 +48,6 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblk) {
   const int xcd = bid & 7, k = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Per camera, in LDS: the x and y rows of M = R^T K^-1 and of the origin
@@ -316,8 +300,7 @@ __device__ __forceinline__ void flush_dots(float* sP, float* sDa, int base, int 
   float acc = 0.f;
 #pragma unroll
   for (int m = 0; m < kWave / 4; ++m) acc += sP[r * kPrdLd + s + 4 * m];
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
+  acc = quad_sum(acc);
   if (s == 0) sDa[base + r] = acc;
   wave_lds_sync();
 }

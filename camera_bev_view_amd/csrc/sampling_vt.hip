@@ -51,6 +51,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace fbev {
 namespace {
@@ -126,18 +127,6 @@ __device__ __forceinline__ void cam_store(double* sP, int e, const CamEntry& ce)
 
 __device__ void stage_cameras(double* sP, const float* K, const float* R, const float* t, int b, int N) {
   for (int e = threadIdx.x; e < N * 12; e += kBlock) cam_store(sP, e, cam_load(K, R, t, b, N, e));
-}
-
-__device__ __forceinline__ int rank_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // 1/x in double: hardware estimate plus two Newton steps.
@@ -365,16 +354,6 @@ struct Lane {
   }
 };
 
-// x + x[lane ^ 16] and x + x[lane ^ 32] with the gfx950 lane-swap instructions.
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 struct FwdArgs {
   Problem p;
   float* out;
@@ -574,12 +553,9 @@ void sampling_vt_fwd(FwdArgs a) {
         const int cl = uniform(items[k].y);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) {
-          float s = acc[i];
-#pragma unroll
-          for (int off = L; off < 16; off <<= 1) s += __shfl_xor(s, off);
-          s = sum_xor16(s);
-          s = sum_xor32(s);
-          acc[i] = s;
+          float s = row_sum_stride<L>(acc[i]);
+          s = swap16_add(s, s);
+          acc[i] = swap32_add(s, s);
         }
         if (slot == 0) {
 #pragma unroll
