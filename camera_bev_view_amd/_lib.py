@@ -19,11 +19,12 @@ FBEV_DTYPE_F32 = 0
 FBEV_DTYPE_BF16 = 1
 FBEV_MAX_CAMERAS = 64
 FBEV_MAX_LEVELS = 4
-ABI_VERSION = 6
+ABI_VERSION = 7
 FBEV_MAX_KEYPOINTS = 256
 
 EXPORTED = ("fbev_forward", "fbev_backward", "fbev_forward_levels", "fbev_backward_levels", "fbev_lss_forward",
-            "fbev_lss_backward", "fbev_deform_forward", "fbev_deform_backward", "fbev_backward_cameras_workspace",
+            "fbev_lss_backward", "fbev_deform_forward", "fbev_deform_backward_workspace", "fbev_deform_backward",
+            "fbev_backward_cameras_workspace",
             "fbev_backward_cameras", "fbev_forward_temporal", "fbev_backward_temporal", "fbev_status_string",
             "fbev_last_error", "fbev_abi_version")
 
@@ -80,8 +81,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fbev_lss_backward.restype = ctypes.c_int
         lib.fbev_deform_forward.argtypes = [f32p, FeatDesc, f32p, f32p, f32p, f32p, f32p, f32p, i32, i32, f32p, vp]
         lib.fbev_deform_forward.restype = ctypes.c_int
+        lib.fbev_deform_backward_workspace.argtypes = [FeatDesc, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.fbev_deform_backward_workspace.restype = ctypes.c_int
         lib.fbev_deform_backward.argtypes = [f32p, f32p, FeatDesc, f32p, f32p, f32p, f32p, f32p, f32p, i32, i32, f32p,
-                                             f32p, f32p, f32p, vp]
+                                             f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
         lib.fbev_deform_backward.restype = ctypes.c_int
         lib.fbev_backward_cameras_workspace.argtypes = [FeatDesc, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
         lib.fbev_backward_cameras_workspace.restype = ctypes.c_int

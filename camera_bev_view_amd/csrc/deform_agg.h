@@ -26,9 +26,19 @@ struct DeformArgs {
   int B, N, C, H, W, Q, Kp;
   int q_stride;            // set by the backward's launcher
   int wq_n;                // waves per query in the backward (set by its launcher)
+  // backward, dL/dF by gather (set by its launcher from the caller's workspace; entries NULL = none)
+  int* pix_count;          // [B N H W] entries per pixel
+  int* pix_first;          // [B N H W] first bucket slot of each pixel
+  int* blk_sum;            // per scan block: sum of its counts
+  int* q_count;            // [B Q] entries each query emitted
+  int* entries;            // [B Q][cap] (pixel, rank within the pixel, merged weight bits)
+  int2* bucket;            // entries by pixel: (b Q + q, weight bits)
+  int cap;                 // entries per query at most (4 N Kp)
 };
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream);
-hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream);
+// Device workspace the backward needs for these sizes (0 when dL/dF has nothing to gather).
+size_t deform_backward_workspace_bytes(const DeformArgs& a);
+hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t stream);
 
 }  // namespace fbev

@@ -23,12 +23,18 @@
 // and depths; a query's 64-channel blocks are spread over up to four waves of
 // one workgroup.  (i) The feature gradient: all samples of a query scatter
 // w x tap weight x g with the query's one g, so the pass's taps are merged per
-// pixel in an LDS hash table (weights added) and each distinct pixel gets one
-// 64-lane atomic per channel block.  Per sample, lanes = channels load the
-// four taps once and give (ii) the wave's part of dL/dw = <sample, g> and
-// (iii) of dL/du, dL/dv = w <dsample/du, g>, w <dsample/dv, g>.  The parts are added in wave order; the keypoint gradient
-// is then dL/du du/dp + dL/dv dv/dp with du/dp = (P_1 - u P_3) / h_3 (rows of
-// the 3x3 part of P = K [R | t]), summed over cameras per keypoint in LDS.
+// pixel in an LDS hash table (weights added) and each distinct pixel becomes
+// one entry (pixel, rank, weight), the rank taken from the pixel's integer
+// counter.  After the main kernel a scan of the counts gives every pixel a
+// bucket, the entries are scattered into the buckets, and a gather kernel sums
+// w x g over each pixel's bucket with lanes = channels and writes every element
+// of dL/dF once: no floating-point atomics, no zero-fill of dL/dF.  Per sample,
+// lanes = channels load the four taps once and give (ii) the wave's part of
+// dL/dw = <sample, g> and (iii) of dL/du, dL/dv = w <dsample/du, g>,
+// w <dsample/dv, g>, reduced twelve at a time (four samples) by lane swaps and
+// DPP.  The parts are added in wave order; the keypoint gradient is then
+// dL/du du/dp + dL/dv dv/dp with du/dp = (P_1 - u P_3) / h_3 (rows of the 3x3
+// part of P = K [R | t]), summed over cameras per keypoint in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -113,6 +119,7 @@ __device__ __forceinline__ Proj project_pair(const double* P, double px, double 
 // tap has weight 0), likewise rows; fractions a = u - x0, b = v - y0.
 struct Taps {
   int p00, dx, dy;   // element offset of tap (y0, x0); steps to x1 and y1 (0 when clamped)
+  int pix, dxp, dyp; // the same as pixel indices within the batch sample (n H W + y W + x)
   float a, b;
   double u, v;
 };
@@ -127,9 +134,12 @@ __device__ __forceinline__ Taps taps_of(const Proj& pr, int n, int H, int W, int
   const int x0 = (int)fu, y0 = (int)fv;
   t.a = (float)(t.u - fu);
   t.b = (float)(t.v - fv);
-  t.p00 = (int)((size_t)n * HWC + ((size_t)y0 * W + x0) * C);
-  t.dx = (x0 + 1 < W) ? C : 0;
-  t.dy = (y0 + 1 < H) ? W * C : 0;
+  t.pix = (n * H + y0) * W + x0;
+  t.dxp = (x0 + 1 < W) ? 1 : 0;
+  t.dyp = (y0 + 1 < H) ? W : 0;
+  t.p00 = (int)((size_t)t.pix * C);
+  t.dx = t.dxp * C;
+  t.dy = t.dyp * C;
   return t;
 }
 
@@ -212,7 +222,7 @@ constexpr int kTab = 1 << kTabBits;      // per-wave hash table of a pass's tap 
 
 // Per-wave LDS of the backward: the in-view samples of one pass.
 struct SampleRec {
-  int p00, dx, dy, idx;   // taps as in Taps; idx = n * Kp + k
+  int pix, dxp, dyp, idx; // taps as pixel indices (as in Taps); idx = n * Kp + k
   float a, b, w, pad;
   double u, v, h2;
 };
@@ -220,8 +230,8 @@ struct SampleRec {
 // Backward: a query's 64-channel blocks are spread over wq_n waves of one
 // workgroup (qw_n = 4 / wq_n queries per workgroup).  Every wave lists the
 // query's in-view samples itself; per sample it loads its channels of the four
-// taps, adds w * tap weight * g to dL/dF with atomics and forms its part of
-// <sample, g>, <d sample/du, g>, <d sample/dv, g>.  After a pass the parts are
+// taps and forms its part of <sample, g>, <d sample/du, g>, <d sample/dv, g>;
+// the query's first wave emits the merged dL/dF entries.  After a pass the parts are
 // added in wave order (fixed), lane s of the query's first wave turns sample s's
 // sums into dL/dw and its keypoint's gradient through the projection, and lane
 // k adds the pass's contributions to keypoint k in sample order: dL/dw,
@@ -247,10 +257,10 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   const int NK = a.N * a.Kp;
   const size_t HWC = (size_t)a.H * a.W * a.C;
   const float* fb = a.feat + (size_t)b * a.N * HWC;
-  float* gfb = a.gfeat + (size_t)b * a.N * HWC;
+  const int pix_base = b * a.N * a.H * a.W;          // first pixel of this batch sample
 
   // queries visited in the order q = unit * stride mod Q (stride coprime to Q), which spreads the
-  // waves that run at the same time over the image and so over the atomics' addresses
+  // waves that run at the same time over the image and so over the pixel counters' addresses
   const int unit = blockIdx.x * (kWaves / wq_n) + qs;
   const bool active = unit < a.Q;                     // inactive waves still take every barrier
   const int q = active ? (int)(((long long)unit * a.q_stride) % a.Q) : 0;
@@ -258,6 +268,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   const double ax = a.anchors[bq * 3], ay = a.anchors[bq * 3 + 1], az = a.anchors[bq * 3 + 2];
   const float* gq = a.grad + bq * a.C;
   float* gk = sG + qs * a.Kp * 3;
+  int ecount = 0;                                      // feature-gradient entries this query has emitted
   if (wq == 0)
     for (int e = lane; e < a.Kp * 3; e += kWave) gk[e] = 0.f;
   for (int base = 0; base < NK; base += kWave) {
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
     if (valid) {
       const Taps tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
       const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-      smp[s] = SampleRec{tp.p00, tp.dx, tp.dy, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
+      smp[s] = SampleRec{tp.pix, tp.dxp, tp.dyp, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
     }
     for (int e = lane; e < kTab; e += kWave) tab[e] = make_int2(-1, 0);
     wave_lds_sync();
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       const SampleRec sr = smp[lane];
       const float wa0 = (1.f - sr.a) * sr.w, wa1 = sr.a * sr.w;
       const float wt[4] = {wa0 * (1.f - sr.b), wa1 * (1.f - sr.b), wa0 * sr.b, wa1 * sr.b};
-      const int px[4] = {sr.p00, sr.p00 + sr.dx, sr.p00 + sr.dy, sr.p00 + sr.dy + sr.dx};
+      const int px[4] = {sr.pix, sr.pix + sr.dxp, sr.pix + sr.dyp, sr.pix + sr.dyp + sr.dxp};
       for (int t = 0; t < 4; ++t) {
         if (wt[t] == 0.f) continue;
         uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - kTabBits);
@@ -320,9 +331,9 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
 #pragma unroll
       for (int i = 0; i < kSampUnroll; ++i) {
         const SampleRec sr = smp[min(s0 + i, cnt - 1)];
-        p00[i] = uniform(sr.p00);
-        dx[i] = uniform(sr.dx);
-        dy[i] = uniform(sr.dy);
+        p00[i] = uniform(sr.pix) * a.C;
+        dx[i] = uniform(sr.dxp) * a.C;
+        dy[i] = uniform(sr.dyp) * a.C;
         fa[i] = sr.a;
         fbt[i] = sr.b;
       }
@@ -362,12 +373,19 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       if ((lane & 15) == 0 && s0 + row < cnt)
         *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + row) * 4) = make_float4(z[0], z[1], z[2], 0.f);
     }
-    // ---- the feature gradient: one atomic per (merged pixel, channel)
-    for (int e = 0; e < nu; ++e) {
-      const int2 t = tab[e];
-      const int pix = uniform(t.x);
-      const float ws = __int_as_float(uniform(t.y));
-      for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) unsafeAtomicAdd(gfb + (size_t)pix + c, ws * gq[c]);
+    // ---- the feature gradient: one entry (pixel, rank, merged weight) per merged pixel, the rank
+    // taken from the pixel's counter; the gather kernels add w * g over each pixel's entries
+    if (wq == 0 && a.entries != nullptr) {
+      for (int e = lane; e < nu; e += kWave) {
+        const int2 t = tab[e];
+        const int gp = pix_base + t.x;
+        const int rank = atomicAdd(a.pix_count + gp, 1);
+        int* E = a.entries + ((size_t)bq * a.cap + ecount + e) * 3;
+        E[0] = gp;
+        E[1] = rank;
+        E[2] = t.y;
+      }
+      ecount += nu;
     }
     __syncthreads();
     // ---- the query's first wave: sums over its waves (wave order), dL/dw, keypoint contributions
@@ -414,6 +432,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   }
   // ---- the query's keypoint and anchor gradients (first wave)
   if (!active || wq != 0) return;                      // no barrier follows
+  if (lane == 0 && a.entries != nullptr) a.q_count[bq] = ecount;
   float sx = 0.f, sy = 0.f, sz = 0.f;
   for (int k = lane; k < a.Kp; k += kWave) {
     const float gx = gk[k * 3], gy = gk[k * 3 + 1], gz = gk[k * 3 + 2];
@@ -442,6 +461,111 @@ __global__ void deform_fill_zero(float* __restrict__ dst, size_t n) {
   for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = 0.f;
 }
 
+// ---- dL/dF by gather: the per-pixel entry counts are scanned into bucket offsets, the entries
+// scattered into their pixels' buckets, and every pixel's channels summed and written once.
+
+constexpr int kScanPer = 16;                       // counts per thread in the scan kernels
+constexpr int kScanBlock = kBlock * kScanPer;      // counts per scan workgroup
+
+// Sum over the workgroup, returned to every thread (one barrier pair).
+__device__ __forceinline__ int block_sum(int v, int* sW) {
+  v = wave_sum(v);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) sW[wid] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < kWaves; ++w) t += sW[w];
+  __syncthreads();
+  return t;
+}
+
+// Per block of kScanBlock pixels: the sum of its entry counts.
+__global__ __launch_bounds__(kBlock) void deform_scan_sums(const int* __restrict__ cnt, int n, int* __restrict__ bsum) {
+  __shared__ int sW[kWaves];
+  const int base = blockIdx.x * kScanBlock;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    const int k = base + i * kBlock + threadIdx.x;
+    s += (k < n) ? cnt[k] : 0;
+  }
+  s = block_sum(s, sW);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = s;
+}
+
+// Exclusive prefix sum of the counts: the preceding blocks' sums, then a scan within the block
+// (thread t owns kScanPer consecutive counts).
+__global__ __launch_bounds__(kBlock) void deform_scan_apply(const int* __restrict__ cnt, int n,
+                                                            const int* __restrict__ bsum, int* __restrict__ first) {
+  __shared__ int sW[kWaves];
+  int pre = 0;
+  for (int j = threadIdx.x; j < (int)blockIdx.x; j += kBlock) pre += bsum[j];
+  pre = block_sum(pre, sW);
+  const int base = blockIdx.x * kScanBlock + threadIdx.x * kScanPer;
+  int v[kScanPer];
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    v[i] = (base + i < n) ? cnt[base + i] : 0;
+    own += v[i];
+  }
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) sW[wid] = incl;
+  __syncthreads();
+  for (int w = 0; w < wid; ++w) pre += sW[w];
+  int run = pre + incl - own;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    if (base + i < n) first[base + i] = run;
+    run += v[i];
+  }
+}
+
+// Entry (pixel p, rank r, w) of query bq into bucket slot first[p] + r; a wave per query.
+__global__ __launch_bounds__(kBlock) void deform_scatter(DeformArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const size_t bq = (size_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (bq >= (size_t)a.B * a.Q) return;
+  const int n = a.q_count[bq];
+  const int* E = a.entries + bq * a.cap * 3;
+  for (int e = lane; e < n; e += kWave)
+    a.bucket[a.pix_first[E[3 * e]] + E[3 * e + 1]] = make_int2((int)bq, E[3 * e + 2]);
+}
+
+// One (pixel, 64-channel block) per wave: dL/dF[p, c] = sum over the pixel's entries of w * g[bq, c],
+// the entries read as wave-uniform values, eight upstream rows in flight.  Every element is written.
+constexpr int kGatherUnroll = 8;
+__global__ __launch_bounds__(kBlock) void deform_gather(DeformArgs a, int npix) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int groups = (a.C + kWave - 1) / kWave;
+  const long long unit = (long long)xcd_block(blockIdx.x, gridDim.x) * kWaves + threadIdx.x / kWave;
+  if (unit >= (long long)npix * groups) return;
+  const int p = (int)(unit / groups);
+  const int c = (int)(unit - (long long)p * groups) * kWave + lane;
+  const bool ch = c < a.C;
+  const int n = uniform(a.pix_count[p]);
+  const int2* bk = a.bucket + uniform(a.pix_first[p]);
+  float acc = 0.f;
+  for (int j = 0; j < n; j += kGatherUnroll) {
+    float w[kGatherUnroll], v[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int2 e = bk[min(j + u, n - 1)];
+      w[u] = (j + u < n) ? __int_as_float(e.y) : 0.f;
+      v[u] = ch ? a.grad[(size_t)e.x * a.C + c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) acc = fmaf(w[u], v[u], acc);
+  }
+  if (ch) a.gfeat[(size_t)p * a.C + c] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream) {
@@ -462,13 +586,71 @@ int query_stride(int Q) {
   return (int)(s % Q);
 }
 
-hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream) {
+namespace {
+
+// Workspace of the dL/dF gather: per-pixel counts and bucket offsets, scan block sums, per-query
+// entry counts, the entries (at most 4 N Kp per query: 4 taps per (camera, keypoint) pair) and the
+// buckets; each part 256-byte aligned.
+struct WsLayout {
+  size_t count, first, bsum, qcount, entries, bucket, total;
+};
+
+bool uses_gather(const DeformArgs& a) {
+  return (size_t)a.B * a.N * a.H * a.W * a.C > 0 && (size_t)a.B * a.Q > 0 && a.N * a.Kp > 0;
+}
+
+WsLayout ws_layout(const DeformArgs& a) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t npix = (size_t)a.B * a.N * a.H * a.W;
+  const size_t nblk = (npix + kScanBlock - 1) / kScanBlock;
+  const size_t nq = (size_t)a.B * a.Q;
+  const size_t ne = nq * 4 * (size_t)a.N * a.Kp;
+  WsLayout L{};
+  size_t o = 0;
+  L.count = o;
+  o = up(o + sizeof(int) * npix);
+  L.first = o;
+  o = up(o + sizeof(int) * npix);
+  L.bsum = o;
+  o = up(o + sizeof(int) * nblk);
+  L.qcount = o;
+  o = up(o + sizeof(int) * nq);
+  L.entries = o;
+  o = up(o + 3 * sizeof(int) * ne);
+  L.bucket = o;
+  o = up(o + sizeof(int2) * ne);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t deform_backward_workspace_bytes(const DeformArgs& a) { return uses_gather(a) ? ws_layout(a).total : 0; }
+
+hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t stream) {
   a.q_stride = query_stride(a.Q);
-  const size_t nF = (size_t)a.B * a.N * a.H * a.W * a.C;
-  if (nF > 0) {
-    const size_t blocks = (nF + 255) / 256;
-    hipLaunchKernelGGL(deform_fill_zero, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream,
-                       a.gfeat, nF);
+  const size_t npix = (size_t)a.B * a.N * a.H * a.W;
+  const size_t nF = npix * a.C;
+  const bool gather = uses_gather(a);
+  a.entries = nullptr;
+  if (gather) {
+    const WsLayout L = ws_layout(a);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    a.pix_count = reinterpret_cast<int*>(w + L.count);
+    a.pix_first = reinterpret_cast<int*>(w + L.first);
+    a.blk_sum = reinterpret_cast<int*>(w + L.bsum);
+    a.q_count = reinterpret_cast<int*>(w + L.qcount);
+    a.entries = reinterpret_cast<int*>(w + L.entries);
+    a.bucket = reinterpret_cast<int2*>(w + L.bucket);
+    a.cap = 4 * a.N * a.Kp;
+  }
+  // the counters start at zero; without entries to gather, dL/dF is zero
+  float* zero = gather ? reinterpret_cast<float*>(a.pix_count) : a.gfeat;
+  const size_t nz = gather ? npix : nF;
+  if (nz > 0) {
+    const size_t blocks = (nz + 255) / 256;
+    hipLaunchKernelGGL(deform_fill_zero, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream, zero,
+                       nz);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -482,6 +664,16 @@ hipError_t launch_deform_backward(DeformArgs a, hipStream_t stream) {
                        sizeof(float) * 4 * kWave * kWaves + sizeof(int2) * kTab * kWaves +
                        sizeof(float) * 3 * a.Kp * kWaves;
   hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !gather) return e;
+  const int np = (int)npix;
+  const unsigned nblk = (unsigned)((npix + kScanBlock - 1) / kScanBlock);
+  hipLaunchKernelGGL(deform_scan_sums, dim3(nblk), dim3(kBlock), 0, stream, a.pix_count, np, a.blk_sum);
+  hipLaunchKernelGGL(deform_scan_apply, dim3(nblk), dim3(kBlock), 0, stream, a.pix_count, np, a.blk_sum, a.pix_first);
+  const size_t nq = (size_t)a.B * a.Q;
+  hipLaunchKernelGGL(deform_scatter, dim3((unsigned)((nq + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a);
+  const size_t units = npix * blocks;
+  hipLaunchKernelGGL(deform_gather, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a, np);
   return hipGetLastError();
 }
 

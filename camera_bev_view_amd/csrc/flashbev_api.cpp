@@ -376,7 +376,7 @@ fbev_status lss_backward_impl(const float* grad_out, const float* depth, const f
 // Deformable Aggregation arguments: features [B,N,H,W,C] fp32, Q queries with
 // anchors [B,Q,3], Kp keypoint offsets [B,Q,Kp,3] and weights [B,Q,N,Kp].
 fbev_status check_deform(const fbev_feat_desc& fd, int32_t Q, int32_t Kp, const float* K, const float* R,
-                         const float* t, fbev::DeformArgs& a) {
+                         const float* t, fbev::DeformArgs& a, bool cams = true) {
   if (fd.B < 0 || fd.N < 0 || fd.C < 0 || fd.H < 0 || fd.W < 0 || Q < 0 || Kp < 0)
     return fail(FBEV_ERR_INVALID_ARGUMENT, "negative size (B=%d N=%d C=%d H=%d W=%d Q=%d Kp=%d)", fd.B, fd.N, fd.C,
                 fd.H, fd.W, Q, Kp);
@@ -386,7 +386,7 @@ fbev_status check_deform(const fbev_feat_desc& fd, int32_t Q, int32_t Kp, const 
     return fail(FBEV_ERR_INVALID_ARGUMENT, "feature map %dx%d above %d", fd.H, fd.W, FBEV_MAX_GRID);
   if (Kp > FBEV_MAX_KEYPOINTS)
     return fail(FBEV_ERR_INVALID_ARGUMENT, "Kp=%d keypoints exceeds FBEV_MAX_KEYPOINTS=%d", Kp, FBEV_MAX_KEYPOINTS);
-  if ((int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
+  if (cams && (int64_t)fd.B * fd.N > 0 && (K == nullptr || R == nullptr || t == nullptr))
     return fail(FBEV_ERR_INVALID_ARGUMENT, "K, R and t must be non-NULL when B*N > 0");
   const int64_t per_sample = (int64_t)fd.N * fd.H * fd.W * fd.C;
   if (per_sample >= (int64_t)1 << 31)
@@ -430,12 +430,36 @@ fbev_status deform_forward_impl(const float* features, fbev_feat_desc fd, const 
   return device_status(fbev::launch_deform_forward(a, static_cast<hipStream_t>(stream)), "fbev_deform_forward launch");
 }
 
+// The backward's dL/dF gather indexes pixels and entries (at most 4 N Kp per query) with 32 bits.
+fbev_status check_deform_backward(const fbev_feat_desc& fd, int32_t Q, int32_t Kp, const float* K, const float* R,
+                                  const float* t, fbev::DeformArgs& a, bool cams = true) {
+  const fbev_status s = check_deform(fd, Q, Kp, K, R, t, a, cams);
+  if (s != FBEV_OK) return s;
+  const int64_t npix = (int64_t)fd.B * fd.N * fd.H * fd.W;
+  if (npix >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "%lld feature pixels (limit 2^31 - 1)", (long long)npix);
+  const int64_t entries = (int64_t)fd.B * Q * 4 * fd.N * Kp;
+  if (entries >= (int64_t)1 << 31)
+    return fail(FBEV_ERR_UNSUPPORTED, "B*Q*4*N*Kp = %lld gradient entries (limit 2^31 - 1)", (long long)entries);
+  return FBEV_OK;
+}
+
+fbev_status deform_workspace_impl(fbev_feat_desc fd, int32_t Q, int32_t Kp, size_t* bytes) {
+  if (bytes == nullptr) return fail(FBEV_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  fbev::DeformArgs a{};
+  const fbev_status s = check_deform_backward(fd, Q, Kp, nullptr, nullptr, nullptr, a, false);
+  if (s != FBEV_OK) return s;
+  *bytes = fbev::deform_backward_workspace_bytes(a);
+  return FBEV_OK;
+}
+
 fbev_status deform_backward_impl(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
                                  const float* R, const float* t, const float* anchors, const float* offsets,
                                  const float* weights, int32_t Q, int32_t Kp, float* grad_features,
-                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream) {
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   fbev::DeformArgs a{};
-  fbev_status s = check_deform(fd, Q, Kp, K, R, t, a);
+  fbev_status s = check_deform_backward(fd, Q, Kp, K, R, t, a);
   if (s != FBEV_OK) return s;
   const int64_t n_feat = (int64_t)fd.B * fd.N * fd.H * fd.W * fd.C;
   const int64_t n_q = (int64_t)fd.B * Q;
@@ -459,7 +483,13 @@ fbev_status deform_backward_impl(const float* grad_out, const float* features, f
   a.gweights = grad_weights;
   a.goffsets = grad_offsets;
   a.ganchors = grad_anchors;
-  return device_status(fbev::launch_deform_backward(a, static_cast<hipStream_t>(stream)),
+  const size_t need = fbev::deform_backward_workspace_bytes(a);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(FBEV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return device_status(fbev::launch_deform_backward(a, workspace, static_cast<hipStream_t>(stream)),
                        "fbev_deform_backward launch");
 }
 
@@ -539,12 +569,17 @@ fbev_status fbev_deform_forward(const float* features, fbev_feat_desc fd, const 
   return deform_forward_impl(features, fd, K, R, t, anchors, offsets, weights, Q, Kp, out, stream);
 }
 
+fbev_status fbev_deform_backward_workspace(fbev_feat_desc fd, int32_t Q, int32_t Kp, size_t* bytes) {
+  return deform_workspace_impl(fd, Q, Kp, bytes);
+}
+
 fbev_status fbev_deform_backward(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
                                  const float* R, const float* t, const float* anchors, const float* offsets,
                                  const float* weights, int32_t Q, int32_t Kp, float* grad_features,
-                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream) {
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   return deform_backward_impl(grad_out, features, fd, K, R, t, anchors, offsets, weights, Q, Kp, grad_features,
-                              grad_weights, grad_offsets, grad_anchors, stream);
+                              grad_weights, grad_offsets, grad_anchors, workspace, workspace_bytes, stream);
 }
 
 const char* fbev_status_string(fbev_status s) {

@@ -44,12 +44,6 @@ constexpr int kCg = 64;                   // channels per group (one per lane)
 constexpr int kLd = kCg + 1;              // padded LDS row of one cell's channels
 constexpr int kCamD = 16;                 // doubles per camera: M rows x, y (3 each), origin x, y, BEV wedge (6)
 
-__device__ __forceinline__ int xcd_tile(int bid, int nblk) {
-  const int xcd = bid & 7, k = bid >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
-  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
-
 // Per camera, in LDS: the x and y rows of M = R^T K^-1 and of the origin
 // o = -R^T t, so the ego x-y of the point at camera depth d on pixel (u, v)'s
 // ray is o + d M [u, v, 1] (tutorial, "Splat" step 1).
@@ -488,7 +482,7 @@ __device__ __forceinline__ void splat_tile(const LssArgs& a, const double* sCam,
 }
 
 __device__ __forceinline__ void decode_tile(const LssArgs& a, int& b, int& i0, int& j0) {
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(blockIdx.x, gridDim.x);
   const int jt = tile % a.tiles_y;
   const int r1 = tile / a.tiles_y;
   const int it = r1 % a.tiles_x;

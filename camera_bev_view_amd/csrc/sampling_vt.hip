@@ -91,15 +91,6 @@ struct Rec {
   float w;   // bilinear weight / valid-camera count
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of tiles so neighbouring BEV cells (which read the same
-// image region) share one L2.
-__device__ __forceinline__ int xcd_tile(int bid, int nblk) {
-  const int xcd = bid & 7, k = bid >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
-  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
-
 // P_n = K_n [R_n | t_n] in double, 12 entries per camera, row-major 3x4.  Entry
 // e = 12 n + 4 r + c is the dot product of row r of K_n with column c of [R_n | t_n].
 struct CamEntry {
@@ -394,7 +385,7 @@ void sampling_vt_fwd(FwdArgs a) {
   cur += sizeof(int2) * kItems * kWaves;
   float* sOut = reinterpret_cast<float*>(cur);
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(blockIdx.x, gridDim.x);
   const int yt = tile % a.tiles_y;
   const int bx = tile / a.tiles_y;
   const int x = bx % p.X;
@@ -633,7 +624,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   cur += sizeof(int) * kWaves;
   int* sFlag = reinterpret_cast<int*>(cur);                  // [0] more rounds, [1] occupied slots, [2] slots taken
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(blockIdx.x, gridDim.x);
   const int yt = tile % a.tiles_y;
   const int r1 = tile / a.tiles_y;
   const int xt = r1 % a.tiles_x;

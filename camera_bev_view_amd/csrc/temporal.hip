@@ -28,6 +28,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace fbev {
 namespace {
@@ -35,15 +36,6 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kChunk = 8;                // channels per thread
 constexpr int kMaxWin = 33;              // candidate cells per axis in the backward, at most
-
-// Workgroups are dealt round-robin to the eight XCDs; renumbering them so that
-// each XCD takes a contiguous run of units keeps neighbouring cell blocks, which
-// read the same rows of the source map, in one L2.
-__device__ __forceinline__ int xcd_unit(int bid, int nblk) {
-  const int xcd = bid & 7, k = bid >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
-  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
 
 struct AlignArgs {
   const float* src;        // forward: prev [B, Cp, X, Y]; backward: grad [B, out_ch, X, Y]
@@ -102,7 +94,7 @@ __device__ __forceinline__ Src source_of(const AlignArgs& a, const IndexMap& im,
 }
 
 __global__ __launch_bounds__(kBlock) void bev_align_fwd(AlignArgs a) {
-  const int u = xcd_unit(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
+  const int u = xcd_block(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
   const int blk = u % a.nblk, rest = u / a.nblk;
   const int chunk = rest % a.nchunk, b = rest / a.nchunk;
   const int XY = a.X * a.Y;
@@ -130,7 +122,7 @@ __global__ __launch_bounds__(kBlock) void bev_align_fwd(AlignArgs a) {
 }
 
 __global__ __launch_bounds__(kBlock) void bev_align_bwd(AlignArgs a) {
-  const int u = xcd_unit(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
+  const int u = xcd_block(blockIdx.x, gridDim.x);        // unit = (cell block, channel chunk, sample)
   const int blk = u % a.nblk, rest = u / a.nblk;
   const int chunk = rest % a.nchunk, b = rest / a.nchunk;
   const int XY = a.X * a.Y;

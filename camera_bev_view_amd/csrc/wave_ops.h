@@ -24,10 +24,11 @@ __device__ __forceinline__ int rank_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// x of the lane that DPP control Ctrl names, within the lane's row of 16.
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+// x of the lane that DPP control Ctrl names, within the lane's row of 16 (T: float or int).
+template <int Ctrl, typename T>
+__device__ __forceinline__ T dpp(T x) {
+  static_assert(sizeof(T) == 4, "32-bit lanes");
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, false));
 }
 constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]: lane ^ 2
@@ -37,13 +38,15 @@ constexpr int kRowRor4 = 0x124;       // rotate the row by 4 lanes
 constexpr int kRowRor8 = 0x128;       // rotate the row by 8 lanes
 
 // Sum over the four lanes of a quad.
-__device__ __forceinline__ float quad_sum(float x) {
+template <typename T>
+__device__ __forceinline__ T quad_sum(T x) {
   x += dpp<kQuadSwap1>(x);
   return x + dpp<kQuadSwap2>(x);
 }
 
 // Sum over the 16 lanes of a row.
-__device__ __forceinline__ float row_sum16(float x) {
+template <typename T>
+__device__ __forceinline__ T row_sum16(T x) {
   x = quad_sum(x);
   x += dpp<kHalfMirror>(x);
   return x + dpp<kRowMirror>(x);
@@ -51,8 +54,8 @@ __device__ __forceinline__ float row_sum16(float x) {
 
 // Sum over the lanes of a row that agree modulo L (L = 1, 2, 4, 8 or 16): rotations by 8, 4, ...,
 // L pair every lane with the others of its residue class.
-template <int L>
-__device__ __forceinline__ float row_sum_stride(float x) {
+template <int L, typename T>
+__device__ __forceinline__ T row_sum_stride(T x) {
   static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "a power of two up to 16");
   if constexpr (L <= 8) x += dpp<kRowRor8>(x);
   if constexpr (L <= 4) x += dpp<kRowRor4>(x);
@@ -64,20 +67,35 @@ __device__ __forceinline__ float row_sum_stride(float x) {
 // x + the register of the lane one row over (permlane16: rows 0 <-> 1, 2 <-> 3) or one
 // half-wave over (permlane32), with x and y swapped in one instruction: the lanes of the
 // rows (halves) that kept x hold x's pair sum, the others y's.
-__device__ __forceinline__ float swap16_add(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+template <typename T>
+__device__ __forceinline__ T swap16_add(T x, T y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y),
+                                                  false, false);
+  const uint32_t a = r[0], b = r[1];   // both halves as plain values before the casts
+  return __builtin_bit_cast(T, a) + __builtin_bit_cast(T, b);
 }
-__device__ __forceinline__ float swap32_add(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+template <typename T>
+__device__ __forceinline__ T swap32_add(T x, T y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y),
+                                                  false, false);
+  const uint32_t a = r[0], b = r[1];
+  return __builtin_bit_cast(T, a) + __builtin_bit_cast(T, b);
 }
 
 // Sum over the wave, in every lane.
-__device__ __forceinline__ float wave_sum(float x) {
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
   x = row_sum16(x);
   x = swap16_add(x, x);
   return swap32_add(x, x);
+}
+
+// Block bid of nblk renumbered so that the blocks the dispatcher sends to one XCD (bid mod 8,
+// round-robin) take one contiguous range: neighbouring work shares that XCD's L2.
+__device__ __forceinline__ int xcd_block(int bid, int nblk) {
+  const int xcd = bid & 7, k = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
 
 }  // namespace fbev

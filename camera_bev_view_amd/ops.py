@@ -395,8 +395,9 @@ def deform_forward(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: 
 
 def deform_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Tensor, R: torch.Tensor,
                     t: torch.Tensor, anchors: torch.Tensor, offsets: torch.Tensor, weights: torch.Tensor, *,
-                    with_anchors: bool = True):
-    """fbev_deform_backward: (dL/dfeatures, dL/dweights, dL/doffsets, dL/danchors or None)."""
+                    with_anchors: bool = True, workspace: Optional[torch.Tensor] = None):
+    """fbev_deform_backward: (dL/dfeatures, dL/dweights, dL/doffsets, dL/danchors or None).
+    ``workspace`` (a uint8 device tensor) is allocated when not given or too small."""
     B, N, H, W, C, Q, Kp, dev = _check_deform(features, K, R, t, anchors, offsets, weights)
     if tuple(grad_out.shape) != (B, Q, C) or grad_out.dtype != torch.float32 or not grad_out.is_contiguous() \
             or grad_out.device != dev:
@@ -406,7 +407,12 @@ def deform_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Ten
     gO = torch.empty_like(offsets)
     gA = torch.empty_like(anchors) if with_anchors else None
     lib = _lib.load()
-    _lib.check(lib.fbev_deform_backward(_ptr(grad_out), _ptr(features), _lib.feat_desc(B, N, C, H, W), _ptr(K),
-                                        _ptr(R), _ptr(t), _ptr(anchors), _ptr(offsets), _ptr(weights), Q, Kp,
-                                        _ptr(gF), _ptr(gW), _ptr(gO), _ptr(gA), _stream(dev)))
+    fd = _lib.feat_desc(B, N, C, H, W)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.fbev_deform_backward_workspace(fd, Q, Kp, ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=dev)
+    _lib.check(lib.fbev_deform_backward(_ptr(grad_out), _ptr(features), fd, _ptr(K), _ptr(R), _ptr(t),
+                                        _ptr(anchors), _ptr(offsets), _ptr(weights), Q, Kp, _ptr(gF), _ptr(gW),
+                                        _ptr(gO), _ptr(gA), _ptr(workspace), workspace.numel(), _stream(dev)))
     return gF, gW, gO, gA

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 6
+#define FBEV_ABI_VERSION 7
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
@@ -325,19 +325,33 @@ fbev_status fbev_deform_forward(const float* features, fbev_feat_desc fd, const 
  * Gradients of fbev_deform_forward with the in-view mask held fixed (the page
  * asks for a sampling chain that gradients pass through):
  *   grad_features : [B,N,H,W,C] fp32 — each in-view sample adds w * tap weight * g
- *                   to its four taps (zeroed on `stream`, then fp32 atomics).
+ *                   to its four taps.  Computed as a gather: a query's taps on one
+ *                   pixel are merged, each (query, pixel) pair becomes an entry in the
+ *                   pixel's bucket, and every element is the sum over its bucket
+ *                   (written once; the order within a bucket varies run to run, so
+ *                   the last bits may too).
  *   grad_weights  : [B,Q,N,Kp] fp32 — <sample, g> for pairs in view, 0 otherwise.
  *   grad_offsets  : [B,Q,Kp,3] fp32 — sum over cameras of w (<ds/du, g> du/dp + <ds/dv, g> dv/dp),
  *                   the bilinear sample's derivative inside its pixel square times the
  *                   projection's Jacobian du/dp = (P_1 - u P_3) / h_3 (P = K [R | t]).
  *   grad_anchors  : [B,Q,3] fp32 — the sum of grad_offsets over k; may be NULL.
+ *   workspace     : device scratch of at least the size that
+ *                   fbev_deform_backward_workspace() reports for these sizes (may be
+ *                   NULL when that is 0), 16-byte aligned; its contents are not needed
+ *                   before or after the call.  Calls that share a workspace must not
+ *                   overlap.  It holds per-pixel counts and offsets and up to
+ *                   4 N Kp entries of 20 bytes per query.
  * All outputs are fully overwritten; grad_out is [B,Q,C]; other arguments as
- * for fbev_deform_forward.
+ * for fbev_deform_forward.  A workspace smaller than required gives
+ * FBEV_ERR_INVALID_ARGUMENT; B N H W or B Q 4 N Kp of 2^31 or more gives
+ * FBEV_ERR_UNSUPPORTED.
  */
+fbev_status fbev_deform_backward_workspace(fbev_feat_desc fd, int32_t Q, int32_t Kp, size_t* bytes);
 fbev_status fbev_deform_backward(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
                                  const float* R, const float* t, const float* anchors, const float* offsets,
                                  const float* weights, int32_t Q, int32_t Kp, float* grad_features,
-                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* stream);
+                                 float* grad_weights, float* grad_offsets, float* grad_anchors, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* fbev_status_string(fbev_status s);

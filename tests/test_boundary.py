@@ -218,9 +218,15 @@ def dfwd(lib, feat=FAKE, desc=(1, 6, 64, 16, 44), K=FAKE, A=FAKE, D=FAKE, Wt=FAK
 
 
 def dbwd(lib, grad=FAKE, feat=FAKE, desc=(1, 6, 64, 16, 44), A=FAKE, D=FAKE, Wt=FAKE, Q=10, Kp=4, gF=FAKE, gW=FAKE,
-         gO=FAKE, gA=None):
+         gO=FAKE, gA=None, ws=FAKE, ws_bytes=1 << 30):
     return lib.fbev_deform_backward(grad, feat, _lib.feat_desc(*desc), FAKE, FAKE, FAKE, A, D, Wt, Q, Kp, gF, gW, gO,
-                                    gA, None)
+                                    gA, ws, ws_bytes, None)
+
+
+def deform_workspace(lib, desc=(1, 6, 64, 16, 44), Q=10, Kp=4):
+    n = ctypes.c_size_t(12345)
+    st = lib.fbev_deform_backward_workspace(_lib.feat_desc(*desc), Q, Kp, ctypes.byref(n))
+    return st, n.value
 
 
 @pytest.mark.parametrize("kwargs,status,msg", [
@@ -252,6 +258,11 @@ def test_deform_forward_validation(lib, kwargs, status, msg):
     (dict(Wt=None), 1, "weights is NULL"),
     (dict(grad=None), 1, "features and grad_out"),
     (dict(feat=None), 1, "features and grad_out"),
+    (dict(ws=None), 1, "workspace of 0 bytes given"),
+    (dict(ws_bytes=100), 1, "workspace of 100 bytes given"),
+    (dict(ws=FAKE + 8), 1, "16-byte aligned"),
+    (dict(desc=(8, 64, 1, 2048, 2048)), 2, "feature pixels"),
+    (dict(Q=1 << 24, Kp=64), 2, "gradient entries"),
 ])
 def test_deform_backward_validation(lib, kwargs, status, msg):
     assert dbwd(lib, **kwargs) == status
@@ -263,7 +274,23 @@ def test_deform_empty_problems_return_ok_without_device_work(lib):
     assert dfwd(lib, Q=0, A=None, D=None, Wt=None, out=None) == 0
     assert dfwd(lib, desc=(1, 6, 0, 16, 44), out=None) == 0
     assert dbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, feat=None, A=None, D=None, Wt=None, gF=None, gW=None,
-                gO=None) == 0
+                gO=None, ws=None) == 0
+
+
+def test_deform_workspace_size(lib):
+    st, n = deform_workspace(lib)
+    # counts and offsets per pixel, one count per query, 4 N Kp entries of 12 + 8 bytes per query, 256-byte parts
+    npix, nq, ne = 6 * 16 * 44, 10, 10 * 4 * 6 * 4
+    up = lambda x: -(-x // 256) * 256
+    assert st == 0 and n == 2 * up(4 * npix) + up(4) + up(4 * nq) + up(12 * ne) + up(8 * ne)
+    # nothing to gather: no workspace
+    assert deform_workspace(lib, Q=0) == (0, 0)
+    assert deform_workspace(lib, Kp=0) == (0, 0)
+    assert deform_workspace(lib, desc=(1, 6, 0, 16, 44)) == (0, 0)
+    assert deform_workspace(lib, desc=(0, 6, 64, 16, 44)) == (0, 0)
+    assert deform_workspace(lib, Q=-1)[0] == 1
+    assert deform_workspace(lib, Q=1 << 24, Kp=64)[0] == 2
+    assert lib.fbev_deform_backward_workspace(_lib.feat_desc(1, 6, 64, 16, 44), 10, 4, None) == 1
 
 
 def cbwd(lib, grad=FAKE, feat=FAKE, desc=(1, 6, 64, 16, 44), K=FAKE, rng=RNG, X=200, Y=200, Z=8, gK=FAKE, gR=FAKE,
