@@ -219,11 +219,13 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
 constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together (one per lane row)
 constexpr int kTabBits = 9;
 constexpr int kTab = 1 << kTabBits;      // per-wave hash table of a pass's tap pixels (at most 4 x 64 keys)
+constexpr int kTabMinBits = 6;           // a pass uses 2^bits slots, at least twice its taps
 
 // Per-wave LDS of the backward: the in-view samples of one pass.
 struct SampleRec {
   int pix, dxp, dyp, idx; // taps as pixel indices (as in Taps); idx = n * Kp + k
-  float a, b, w, pad;
+  float a, b, w;
+  int k;                  // keypoint
   double u, v, h2;
 };
 
@@ -290,12 +292,17 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
     if (valid) {
       const Taps tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
       const int s = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-      smp[s] = SampleRec{tp.pix, tp.dxp, tp.dyp, idx, tp.a, tp.b, a.weights[bq * NK + idx], 0.f, tp.u, tp.v, pr.h2};
+      smp[s] = SampleRec{tp.pix, tp.dxp, tp.dyp, idx, tp.a, tp.b, a.weights[bq * NK + idx], idx - n * a.Kp,
+                         tp.u, tp.v, pr.h2};
     }
-    for (int e = lane; e < kTab; e += kWave) tab[e] = make_int2(-1, 0);
+    // the table: 2^tb slots with tb the smallest width above twice the pass's 4 cnt taps (at least 64)
+    int tb = kTabMinBits;
+    while ((1 << tb) < 8 * cnt) ++tb;
+    const int tsize = 1 << tb;
+    for (int e = lane; e < tsize; e += kWave) tab[e] = make_int2(-1, 0);
     wave_lds_sync();
     // ---- the pass's taps merged per pixel: every sample of a query scatters w x tap weight x g with
-    // the same g, so taps on one pixel add their weights and leave as one atomic per channel
+    // the same g, so taps on one pixel add their weights and leave as one dL/dF entry
     if (lane < cnt) {
       const SampleRec sr = smp[lane];
       const float wa0 = (1.f - sr.a) * sr.w, wa1 = sr.a * sr.w;
@@ -303,11 +310,11 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       const int px[4] = {sr.pix, sr.pix + sr.dxp, sr.pix + sr.dyp, sr.pix + sr.dyp + sr.dxp};
       for (int t = 0; t < 4; ++t) {
         if (wt[t] == 0.f) continue;
-        uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - kTabBits);
-        for (;;) {                                  // at most 4 * 64 keys in 2 * 4 * 64 slots: a free one exists
+        uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - tb);
+        for (;;) {                                  // at most 4 cnt keys in 8 cnt slots or more: a free one exists
           const int old = atomicCAS(&tab[h].x, -1, px[t]);
           if (old == -1 || old == px[t]) break;
-          h = (h + 1) & (kTab - 1);
+          h = (h + 1) & (tsize - 1);
         }
         atomicAdd(reinterpret_cast<float*>(&tab[h].y), wt[t]);
       }
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
     wave_lds_sync();
     // compaction in place: an entry moves only to a lower slot, one the wave has already read
     int nu = 0;
-    for (int e0 = 0; e0 < kTab; e0 += kWave) {
+    for (int e0 = 0; e0 < tsize; e0 += kWave) {
       const int2 ent = tab[e0 + lane];
       const uint64_t mk = __ballot(ent.x >= 0);
       if (ent.x >= 0)
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       a.gweights[bq * NK + sr.idx] = t.x;
       // keypoint gradient through the projection: du/dp = (P_1 - u P_3) / h_3, dv/dp likewise
       const double* P = sP + sn * 12;
-      const double ih = 1.0 / sr.h2;
+      const double ih = recip(sr.h2);
       const double lu = (double)sr.w * t.y, lv = (double)sr.w * t.z;
       float c3[3];
       for (int r = 0; r < 3; ++r) {
@@ -417,7 +424,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       for (int kk = lane; kk < a.Kp; kk += kWave) {
         float gx = gk[kk * 3], gy = gk[kk * 3 + 1], gz = gk[kk * 3 + 2];
         for (int s = 0; s < cnt; ++s) {
-          if (smp[s].idx % a.Kp != kk) continue;
+          if (smp[s].k != kk) continue;
           const float4 c = *reinterpret_cast<const float4*>(con + s * 4);
           gx += c.x;
           gy += c.y;
@@ -464,8 +471,10 @@ __global__ void deform_fill_zero(float* __restrict__ dst, size_t n) {
 // ---- dL/dF by gather: the per-pixel entry counts are scanned into bucket offsets, the entries
 // scattered into their pixels' buckets, and every pixel's channels summed and written once.
 
+constexpr int kScanThreads = 1024;                 // threads of a scan workgroup
+constexpr int kScanWaves = kScanThreads / kWave;
 constexpr int kScanPer = 16;                       // counts per thread in the scan kernels
-constexpr int kScanBlock = kBlock * kScanPer;      // counts per scan workgroup
+constexpr int kScanBlock = kScanThreads * kScanPer;   // counts per scan workgroup
 
 // Sum over the workgroup, returned to every thread (one barrier pair).
 __device__ __forceinline__ int block_sum(int v, int* sW) {
@@ -474,32 +483,41 @@ __device__ __forceinline__ int block_sum(int v, int* sW) {
   if ((threadIdx.x & (kWave - 1)) == 0) sW[wid] = v;
   __syncthreads();
   int t = 0;
-  for (int w = 0; w < kWaves; ++w) t += sW[w];
+  for (int w = 0; w < kScanWaves; ++w) t += sW[w];
   __syncthreads();
   return t;
 }
 
 // Per block of kScanBlock pixels: the sum of its entry counts.
-__global__ __launch_bounds__(kBlock) void deform_scan_sums(const int* __restrict__ cnt, int n, int* __restrict__ bsum) {
-  __shared__ int sW[kWaves];
+__global__ __launch_bounds__(kScanThreads) void deform_scan_sums(const int* __restrict__ cnt, int n,
+                                                                 int* __restrict__ bsum) {
+  __shared__ int sW[kScanWaves];
   const int base = blockIdx.x * kScanBlock;
   int s = 0;
 #pragma unroll
   for (int i = 0; i < kScanPer; ++i) {
-    const int k = base + i * kBlock + threadIdx.x;
+    const int k = base + i * kScanThreads + threadIdx.x;
     s += (k < n) ? cnt[k] : 0;
   }
   s = block_sum(s, sW);
   if (threadIdx.x == 0) bsum[blockIdx.x] = s;
 }
 
-// Exclusive prefix sum of the counts: the preceding blocks' sums, then a scan within the block
-// (thread t owns kScanPer consecutive counts).
-__global__ __launch_bounds__(kBlock) void deform_scan_apply(const int* __restrict__ cnt, int n,
-                                                            const int* __restrict__ bsum, int* __restrict__ first) {
-  __shared__ int sW[kWaves];
+// Exclusive prefix sum of the counts: the preceding blocks' sums (bsum == NULL: added up from the
+// counts themselves, for a few blocks), then a scan within the block (thread t owns kScanPer
+// consecutive counts).
+constexpr int kScanDirect = 16;                    // blocks at most for the one-launch scan
+__global__ __launch_bounds__(kScanThreads) void deform_scan_apply(const int* __restrict__ cnt, int n,
+                                                                  const int* __restrict__ bsum,
+                                                                  int* __restrict__ first) {
+  __shared__ int sW[kScanWaves];
   int pre = 0;
-  for (int j = threadIdx.x; j < (int)blockIdx.x; j += kBlock) pre += bsum[j];
+  if (bsum != nullptr) {
+    for (int j = threadIdx.x; j < (int)blockIdx.x; j += kScanThreads) pre += bsum[j];
+  } else {
+#pragma unroll 8
+    for (int j = threadIdx.x; j < (int)blockIdx.x * kScanBlock; j += kScanThreads) pre += cnt[j];
+  }
   pre = block_sum(pre, sW);
   const int base = blockIdx.x * kScanBlock + threadIdx.x * kScanPer;
   int v[kScanPer];
@@ -564,6 +582,63 @@ __global__ __launch_bounds__(kBlock) void deform_gather(DeformArgs a, int npix) 
     for (int u = 0; u < kGatherUnroll; ++u) acc = fmaf(w[u], v[u], acc);
   }
   if (ch) a.gfeat[(size_t)p * a.C + c] = acc;
+}
+
+// The same for C % 4 == 0 with 16-byte aligned rows: lanes = (entry slot e, channel quad q), a wave
+// covers up to 256 channels of its pixel as Qw quads (Qw = 16, 32 or 64, the power of two at or
+// above the block's quads) and takes E = 64 / Qw entries per float4 load; eight loads in flight and
+// the next step's entries read ahead.  The E slots are summed by lane swaps at the end.
+template <int Qw>
+__global__ __launch_bounds__(kBlock) void deform_gather4(DeformArgs a, int npix) {
+  constexpr int E = kWave / Qw;
+  constexpr int kStep = kGatherUnroll * E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = lane / Qw, q = lane - e * Qw;
+  const int groups = (a.C + 4 * kWave - 1) / (4 * kWave);
+  const long long unit = (long long)xcd_block(blockIdx.x, gridDim.x) * kWaves + threadIdx.x / kWave;
+  if (unit >= (long long)npix * groups) return;
+  const int p = (int)(unit / groups);
+  const int c = (int)(unit - (long long)p * groups) * 4 * kWave + 4 * q;
+  const bool ch = c < a.C;
+  const int n = uniform(a.pix_count[p]);
+  const int2* bk = a.bucket + uniform(a.pix_first[p]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int2 en[kGatherUnroll];
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) en[u] = (n > 0) ? bk[min(u * E + e, n - 1)] : make_int2(0, 0);
+  for (int j = 0; j < n; j += kStep) {
+    float4 v[kGatherUnroll];
+    float w[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      w[u] = (j + u * E + e < n) ? __int_as_float(en[u].y) : 0.f;
+      v[u] = ch ? *reinterpret_cast<const float4*>(a.grad + (size_t)en[u].x * a.C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (j + kStep < n) {
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) en[u] = bk[min(j + kStep + u * E + e, n - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      acc.x = fmaf(w[u], v[u].x, acc.x);
+      acc.y = fmaf(w[u], v[u].y, acc.y);
+      acc.z = fmaf(w[u], v[u].z, acc.z);
+      acc.w = fmaf(w[u], v[u].w, acc.w);
+    }
+  }
+  if constexpr (E == 4) {                           // slots in the four rows of 16 lanes
+    acc.x = swap16_add(acc.x, acc.x);
+    acc.y = swap16_add(acc.y, acc.y);
+    acc.z = swap16_add(acc.z, acc.z);
+    acc.w = swap16_add(acc.w, acc.w);
+  }
+  if constexpr (E >= 2) {                           // slots in the two half-waves
+    acc.x = swap32_add(acc.x, acc.x);
+    acc.y = swap32_add(acc.y, acc.y);
+    acc.z = swap32_add(acc.z, acc.z);
+    acc.w = swap32_add(acc.w, acc.w);
+  }
+  if (e == 0 && ch) *reinterpret_cast<float4*>(a.gfeat + (size_t)p * a.C + c) = acc;
 }
 
 }  // namespace
@@ -668,12 +743,31 @@ hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t str
   if (e != hipSuccess || !gather) return e;
   const int np = (int)npix;
   const unsigned nblk = (unsigned)((npix + kScanBlock - 1) / kScanBlock);
-  hipLaunchKernelGGL(deform_scan_sums, dim3(nblk), dim3(kBlock), 0, stream, a.pix_count, np, a.blk_sum);
-  hipLaunchKernelGGL(deform_scan_apply, dim3(nblk), dim3(kBlock), 0, stream, a.pix_count, np, a.blk_sum, a.pix_first);
+  if (nblk <= kScanDirect) {
+    hipLaunchKernelGGL(deform_scan_apply, dim3(nblk), dim3(kScanThreads), 0, stream, a.pix_count, np, nullptr,
+                       a.pix_first);
+  } else {
+    hipLaunchKernelGGL(deform_scan_sums, dim3(nblk), dim3(kScanThreads), 0, stream, a.pix_count, np, a.blk_sum);
+    hipLaunchKernelGGL(deform_scan_apply, dim3(nblk), dim3(kScanThreads), 0, stream, a.pix_count, np, a.blk_sum,
+                       a.pix_first);
+  }
   const size_t nq = (size_t)a.B * a.Q;
   hipLaunchKernelGGL(deform_scatter, dim3((unsigned)((nq + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a);
-  const size_t units = npix * blocks;
-  hipLaunchKernelGGL(deform_gather, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a, np);
+  const bool vec4 = a.C % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.grad) | reinterpret_cast<uintptr_t>(a.gfeat)) & 15) == 0;
+  if (vec4) {
+    const size_t units = npix * ((a.C + 4 * kWave - 1) / (4 * kWave));
+    const dim3 g4((unsigned)((units + kWaves - 1) / kWaves));
+    if (a.C <= 64)
+      hipLaunchKernelGGL(deform_gather4<16>, g4, dim3(kBlock), 0, stream, a, np);
+    else if (a.C <= 128)
+      hipLaunchKernelGGL(deform_gather4<32>, g4, dim3(kBlock), 0, stream, a, np);
+    else
+      hipLaunchKernelGGL(deform_gather4<64>, g4, dim3(kBlock), 0, stream, a, np);
+  } else {
+    const size_t units = npix * blocks;
+    hipLaunchKernelGGL(deform_gather, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a,
+                       np);
+  }
   return hipGetLastError();
 }
 
