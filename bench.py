@@ -347,8 +347,7 @@ def main_deform(args):
     fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems)
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems)
     dom_k, dom, dom_bytes = (["deform_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        (["deform_fill_zero", "deform_bwd", "deform_scan_sums", "deform_scan_apply", "deform_scatter",
-          "deform_gather"], bwd, bwd_bytes)
+        (["deform_fill_zero", "deform_bwd", "deform_scan_apply", "deform_scatter", "deform_gather4"], bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient, seeded anchors and "
                       "offsets, flat-Dirichlet weights",
