@@ -139,3 +139,29 @@ def test_deform_degenerate_sizes():
     gF, gW, gO, gA = ops.deform_backward(torch.empty((1, 10, 0), device="cuda"), Fc, K, R, t, A, D, Wt)
     torch.cuda.synchronize()
     assert gF.numel() == 0 and not gW.any() and not gO.any() and not gA.any()
+
+
+def test_deform_many_pixels_two_kernel_scan():
+    """More than 16 scan blocks of 16 384 pixels (2 x 6 x 128 x 176 = 270 336): the bucket offsets come from
+    the two-launch scan (block sums, then the blocks' own scans)."""
+    deform_parity(wl.random_deform_case(21, 2, 6, 4, 128, 176, 40, 4, spread=20.0), "270k pixels, two-launch scan")
+
+
+def test_deform_unaligned_upstream_uses_lane_per_channel_gather():
+    """An upstream gradient that is not 16-byte aligned takes the lanes = channels gather; its dL/dF matches
+    the float4 gather's (same entries, bucket order aside) and the oracle."""
+    inp = wl.random_deform_case(22, 1, 6, 16, 16, 44, 120, 6)
+    say("[case] deform unaligned upstream gradient")
+    F, K, R, t, A, D, Wt = to_dev(inp)
+    g = torch.from_numpy(inp.grad_out).cuda()
+    big = torch.empty(g.numel() + 1, dtype=torch.float32, device="cuda")
+    g_off = big[1:].view(g.shape)
+    g_off.copy_(g)
+    assert g_off.is_contiguous() and g_off.data_ptr() % 16 != 0
+    gF4, gW4, gO4, _ = ops.deform_backward(g, F, K, R, t, A, D, Wt)
+    gF1, gW1, gO1, _ = ops.deform_backward(g_off, F, K, R, t, A, D, Wt)
+    torch.cuda.synchronize()
+    assert torch.equal(gW4, gW1) and torch.equal(gO4, gO1)
+    assert torch.allclose(gF4, gF1, rtol=1e-5, atol=1e-6)
+    rF, _, _, _ = da.deform_backward(inp.grad_out, inp.F, inp.K, inp.R, inp.t, inp.anchors, inp.offsets, inp.weights)
+    assert rel_l2(gF1.cpu().numpy().transpose(0, 1, 4, 2, 3), rF) <= BWD_REL_L2
