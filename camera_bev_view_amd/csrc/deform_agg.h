@@ -34,6 +34,7 @@ struct DeformArgs {
   int* entries;            // [B Q][cap] (pixel, rank within the pixel, merged weight bits)
   int2* bucket;            // entries by pixel: (b Q + q, weight bits)
   int cap;                 // entries per query at most (4 N Kp)
+  int tab_max;             // hash-table slots per wave (set by the backward's launcher)
 };
 
 hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream);

@@ -217,9 +217,7 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
 }
 
 constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together (one per lane row)
-constexpr int kTabBits = 9;
-constexpr int kTab = 1 << kTabBits;      // per-wave hash table of a pass's tap pixels (at most 4 x 64 keys)
-constexpr int kTabMinBits = 6;           // a pass uses 2^bits slots, at least twice its taps
+constexpr int kTabMinBits = 6;           // a pass uses 2^bits slots, at least 4/3 of its 4 cnt taps (at most 3/4 full)
 
 // Per-wave LDS of the backward: the in-view samples of one pass.
 struct SampleRec {
@@ -238,13 +236,15 @@ struct SampleRec {
 // sums into dL/dw and its keypoint's gradient through the projection, and lane
 // k adds the pass's contributions to keypoint k in sample order: dL/dw,
 // dL/doffsets and dL/danchors are deterministic.
-__global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
+// Five waves per SIMD (at most 96 VGPRs): with the table sized to the pass bound, a dense workload's
+// 27 KB of LDS then fits five workgroups per CU.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void deform_bwd(DeformArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
   SampleRec* sS = reinterpret_cast<SampleRec*>(smem + sizeof(double) * 12 * a.N);           // [kWaves][kWave]
   float* sPart = reinterpret_cast<float*>(sS + kWaves * kWave);                             // [kWaves][kWave][4]
-  int2* sTab = reinterpret_cast<int2*>(sPart + kWaves * kWave * 4);                         // [kWaves][kTab]
-  float* sG = reinterpret_cast<float*>(sTab + kWaves * kTab);                                // [kWaves][Kp][3]
+  int2* sTab = reinterpret_cast<int2*>(sPart + kWaves * kWave * 4);                         // [kWaves][tab_max]
+  float* sG = reinterpret_cast<float*>(sTab + kWaves * a.tab_max);                           // [kWaves][Kp][3]
   const int b = blockIdx.y;
   stage_projections(sP, a.K, a.R, a.t, b, a.N);
   __syncthreads();
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
   const int wq_n = a.wq_n, qs = wid / wq_n, wq = wid - qs * wq_n;
   const int lead = qs * wq_n;                          // the query's first wave
   SampleRec* smp = sS + wid * kWave;
-  int2* tab = sTab + wid * kTab;                       // (pixel, merged weight bits); compacted in place
+  int2* tab = sTab + wid * a.tab_max;                       // (pixel, merged weight bits); compacted in place
   float* con = sPart + wid * kWave * 4;                // keypoint contributions, over the parts once read
   const int NK = a.N * a.Kp;
   const size_t HWC = (size_t)a.H * a.W * a.C;
@@ -295,9 +295,9 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       smp[s] = SampleRec{tp.pix, tp.dxp, tp.dyp, idx, tp.a, tp.b, a.weights[bq * NK + idx], idx - n * a.Kp,
                          tp.u, tp.v, pr.h2};
     }
-    // the table: 2^tb slots with tb the smallest width above twice the pass's 4 cnt taps (at least 64)
+    // the table: 2^tb slots, the fewest (at least 64) that keep the pass's at most 4 cnt keys to 3/4 of them
     int tb = kTabMinBits;
-    while ((1 << tb) < 8 * cnt) ++tb;
+    while ((1 << tb) * 3 < 16 * cnt) ++tb;
     const int tsize = 1 << tb;
     for (int e = lane; e < tsize; e += kWave) tab[e] = make_int2(-1, 0);
     wave_lds_sync();
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kBlock) void deform_bwd(DeformArgs a) {
       for (int t = 0; t < 4; ++t) {
         if (wt[t] == 0.f) continue;
         uint32_t h = ((uint32_t)px[t] * 2654435761u) >> (32 - tb);
-        for (;;) {                                  // at most 4 cnt keys in 8 cnt slots or more: a free one exists
+        for (;;) {                                  // at most 4 cnt keys in 16 cnt / 3 slots or more: a free one exists
           const int old = atomicCAS(&tab[h].x, -1, px[t]);
           if (old == -1 || old == px[t]) break;
           h = (h + 1) & (tsize - 1);
@@ -735,8 +735,14 @@ hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t str
   a.wq_n = blocks >= 3 ? 4 : (blocks == 2 ? 2 : 1);
   const int qw_n = kWaves / a.wq_n;
   const dim3 grid((unsigned)((a.Q + qw_n - 1) / qw_n), (unsigned)a.B);
+  {  // the widest table a pass can need: at most 64 samples, and at most N Kp
+    const int cmax = a.N * a.Kp < kWave ? a.N * a.Kp : kWave;
+    int tb = kTabMinBits;
+    while ((1 << tb) * 3 < 16 * cmax) ++tb;
+    a.tab_max = 1 << tb;
+  }
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves +
-                       sizeof(float) * 4 * kWave * kWaves + sizeof(int2) * kTab * kWaves +
+                       sizeof(float) * 4 * kWave * kWaves + sizeof(int2) * a.tab_max * kWaves +
                        sizeof(float) * 3 * a.Kp * kWaves;
   hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
   hipError_t e = hipGetLastError();
