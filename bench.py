@@ -83,6 +83,27 @@ def measured_traffic(kernel, workload: str):
     return k.get("bytes_per_launch") if k else None
 
 
+def measured_pass_traffic(kernels, workload: str):
+    """HBM bytes of one whole pass whose launches repeat a kernel name at different sizes (a multi-level
+    backward): the record's per-pass figure for exactly this launch list, or None (stale or absent)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    w = rec.get("workloads", {}).get(workload, {})
+    sources = w.get("sources") or {}
+    try:
+        if not sources or any(sha != kernel_source_hash(os.path.join(ROOT, src)) for src, sha in sources.items()):
+            return None
+    except OSError:
+        return None
+    for p in w.get("passes", []):
+        if p.get("kernels") == list(kernels):
+            return p.get("bytes_per_pass")
+    return None
+
+
 def pass_roofline(kernels, rate, nbytes, workload, exact_traffic=True):
     """The ``roofline`` object of one timed pass: algorithmic bytes over the pass's HIP-event time.
     ``kernels`` lists the pass's launches in order (their rocprofv3 durations add up to the pass);
@@ -91,7 +112,7 @@ def pass_roofline(kernels, rate, nbytes, workload, exact_traffic=True):
     achieved = rate["hbm_gbps_algorithmic"]
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(kernels, workload) if exact_traffic else None,
+            "traffic": measured_traffic(kernels, workload) if exact_traffic else measured_pass_traffic(kernels, workload),
             "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
 
 
