@@ -34,6 +34,8 @@ constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]: lane ^ 2
 constexpr int kHalfMirror = 0x141;    // lane j <-> 7 - j within each half-row
 constexpr int kRowMirror = 0x140;     // lane j <-> 15 - j within the row
+constexpr int kRowRor1 = 0x121;       // rotate the row by 1 lane
+constexpr int kRowRor2 = 0x122;       // rotate the row by 2 lanes
 constexpr int kRowRor4 = 0x124;       // rotate the row by 4 lanes
 constexpr int kRowRor8 = 0x128;       // rotate the row by 8 lanes
 
@@ -59,8 +61,8 @@ __device__ __forceinline__ T row_sum_stride(T x) {
   static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "a power of two up to 16");
   if constexpr (L <= 8) x += dpp<kRowRor8>(x);
   if constexpr (L <= 4) x += dpp<kRowRor4>(x);
-  if constexpr (L <= 2) x += dpp<0x122>(x);
-  if constexpr (L <= 1) x += dpp<0x121>(x);
+  if constexpr (L <= 2) x += dpp<kRowRor2>(x);
+  if constexpr (L <= 1) x += dpp<kRowRor1>(x);
   return x;
 }
 
