@@ -83,36 +83,14 @@ def measured_traffic(kernel, workload: str):
     return k.get("bytes_per_launch") if k else None
 
 
-def measured_pass_traffic(kernels, workload: str):
-    """HBM bytes of one whole pass whose launches repeat a kernel name at different sizes (a multi-level
-    backward): the record's per-pass figure for exactly this launch list, or None (stale or absent)."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    w = rec.get("workloads", {}).get(workload, {})
-    sources = w.get("sources") or {}
-    try:
-        if not sources or any(sha != kernel_source_hash(os.path.join(ROOT, src)) for src, sha in sources.items()):
-            return None
-    except OSError:
-        return None
-    for p in w.get("passes", []):
-        if p.get("kernels") == list(kernels):
-            return p.get("bytes_per_pass")
-    return None
-
-
-def pass_roofline(kernels, rate, nbytes, workload, exact_traffic=True):
+def pass_roofline(kernels, rate, nbytes, workload):
     """The ``roofline`` object of one timed pass: algorithmic bytes over the pass's HIP-event time.
     ``kernels`` lists the pass's launches in order (their rocprofv3 durations add up to the pass);
-    ``traffic`` sums their counter bytes (None when a launch of a different size repeats a name, or
-    when the counters are missing or stale)."""
+    ``traffic`` sums their counter bytes (None when the counters are missing or stale)."""
     achieved = rate["hbm_gbps_algorithmic"]
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(kernels, workload) if exact_traffic else measured_pass_traffic(kernels, workload),
+            "traffic": measured_traffic(kernels, workload),
             "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
 
 
@@ -598,10 +576,10 @@ def main():
                      logical_samples_per_s=logical)
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems, bilinear_samples_per_s=samples,
                      logical_samples_per_s=logical)
-    # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch
-    # per feature level)
+    # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch,
+    # all feature levels)
     dom_k, dom, dom_bytes = (["sampling_vt_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        (["fill_zero_f32"] + ["sampling_vt_bwd"] * nlev, bwd, bwd_bytes)
+        (["fill_zero_f32", "sampling_vt_bwd"], bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step,
                       "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
@@ -610,7 +588,7 @@ def main():
                        "B": B, "N": N, "C": C, "H": H, "W": W, "levels": nlev, "X": X, "Y": Y, "Z": Z,
                        "valid_samples_per_pass": valid_tuples})
     line.update({"bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3), "forward": fwd, "backward": bwd,
-                 "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload, exact_traffic=(nlev == 1))})
+                 "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload)})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = baseline(inp, args.cpu_rows or X)

@@ -578,7 +578,6 @@ struct BwdArgs {
   const float* grad;
   float* dF;
   int tiles_x, tiles_y;
-  int level;         // feature level this launch scatters (multi-level: one launch per level)
 };
 
 // Hash-table slot of pixel `pix` (inserted if absent), or -1 when the probe
@@ -669,13 +668,14 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int wid = uniform(threadIdx.x / kWave);   // wave-uniform for the compiler too
   int2* region = sRegion + wid * kBwdRegion;
   int2* pend = sPend + wid * kBwdPend;
-  // A multi-level backward runs one launch per level: every lane then works on
-  // that level (tap pass, merging and table as in a single-level launch), and a
-  // tap's weight carries the 1/L of the level mean.
+  // A multi-level backward takes the levels one after another inside each
+  // workgroup (tap pass, merging and table as in a single-level backward, the
+  // gradient tile and cameras staged once), and a tap's weight carries the 1/L
+  // of the level mean.
   const int nlev = 1;
   const LaneRole role = lane_role(lane, p.N, 1);
   const int zpc = role.zpc, zl = role.zl, ln = role.ln;
-  const int vs = lane, vl = ML ? a.level : 0;        // phase-B lane role: (sample, level)
+  const int vs = lane;                               // phase-B lane role: one listed sample
   const float lmean = ML ? (float)p.L : 1.0f;
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   const int items_per_cell = (p.Z > 0) ? (p.Z + zpc - 1) / zpc : 0;
@@ -692,9 +692,18 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
     return a.grad[(((size_t)b * p.out_ch + c_lo + c) * p.X + x_base + dx) * p.Y + y_base + dy];
   };
 
+  bool grad_staged = false;
+  for (int vl = 0; vl < (ML ? p.L : 1); ++vl) {      // feature level; each starts with a fresh table
+  if (vl > 0) {
+    for (int e = threadIdx.x; e < kSlots; e += kBlock) {
+      sTag[e] = -1;
+      sCnt[e] = 0;
+    }
+    if (threadIdx.x == 0) sFlag[2] = 0;
+    __syncthreads();
+  }
   int it = 0, ci = 0, zc = 0;                       // item counter, its cell and first bin
   int cdx = wid / ncy, cdy = wid - (wid / ncy) * ncy;   // the cell's place in the tile
-  bool grad_staged = false;
   for (;;) {
     // ---- list taps in batches until this wave's region is full or the table is
     // loaded past kFillMax (the pixels of the remaining items go to a later round)
@@ -952,6 +961,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
     if (threadIdx.x == 0) sFlag[2] = 0;
     __syncthreads();
   }
+  }   // levels
 }
 
 __global__ void fill_zero_f32(float* __restrict__ dst, size_t n) {
@@ -1085,18 +1095,12 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
                        sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
                        sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
   if (p.L == 1) {
-    a.level = 0;
     hipLaunchKernelGGL(sampling_vt_bwd<false>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream,
                        a);
     return hipGetLastError();
   }
-  for (int l = 0; l < p.L; ++l) {
-    a.level = l;
-    hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace fbev
