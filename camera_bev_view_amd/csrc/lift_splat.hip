@@ -593,16 +593,24 @@ __global__ __launch_bounds__(kBlock) void lift_splat_bwd(LssArgs a) {
   splat_tile<true>(a, sCam, L, sLen, sScr + wid * kScratchFloats, tile, b, i0, j0, wid, lane);
 }
 
-__global__ void lss_fill_zero(float* __restrict__ dst, size_t n) {
+// Zeroes two buffers in one launch (the backward's two gradients): element k < n0 of the first, then
+// the n1 elements of the second.
+__global__ void lss_fill_zero(float* __restrict__ d0, size_t n0, float* __restrict__ d1, size_t n1) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = 0.f;
+  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n0 + n1; k += stride) {
+    if (k < n0)
+      d0[k] = 0.f;
+    else
+      d1[k - n0] = 0.f;
+  }
 }
 
-hipError_t fill(float* dst, size_t n, hipStream_t stream) {
+hipError_t fill(float* d0, size_t n0, float* d1, size_t n1, hipStream_t stream) {
+  const size_t n = n0 + n1;
   if (n == 0) return hipSuccess;
   const size_t blocks = (n + 255) / 256;
   const unsigned nb = (unsigned)(blocks < 2048 ? blocks : 2048);
-  hipLaunchKernelGGL(lss_fill_zero, dim3(nb), dim3(256), 0, stream, dst, n);
+  hipLaunchKernelGGL(lss_fill_zero, dim3(nb), dim3(256), 0, stream, d0, n0, d1, n1);
   return hipGetLastError();
 }
 
@@ -640,9 +648,7 @@ hipError_t launch_lss_forward(LssArgs a, hipStream_t stream) {
 
 hipError_t launch_lss_backward(LssArgs a, hipStream_t stream) {
   const size_t npix = (size_t)a.B * a.N * a.H * a.W;
-  hipError_t e = hipSuccess;
-  if (a.gdep != nullptr) e = fill(a.gdep, npix * a.D, stream);
-  if (e == hipSuccess && a.gctx != nullptr) e = fill(a.gctx, npix * a.C, stream);
+  hipError_t e = fill(a.gdep, a.gdep != nullptr ? npix * a.D : 0, a.gctx, a.gctx != nullptr ? npix * a.C : 0, stream);
   if (e != hipSuccess) return e;
   set_scan_constants(a);
   a.tiles_x = (a.X + kTX - 1) / kTX;
