@@ -197,14 +197,13 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
   p.feat = nullptr;
   p.elem_bytes = 4;
   p.vec_bytes = 4;
-  if (n_feat > 0) {
-    s = device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
-                      "fbev_backward launch");
-    if (s != FBEV_OK) return s;
+  if (n_prev == 0) {
+    if (n_feat == 0) return FBEV_OK;
+    return device_status(fbev::launch_backward(p, grad_out, grad_features, static_cast<hipStream_t>(stream)),
+                         "fbev_backward launch");
   }
-  if (n_prev == 0) return FBEV_OK;
-  return device_status(fbev::launch_align_backward(p, grad_out, Cp, ego, grad_prev, fd.C,
-                                                   static_cast<hipStream_t>(stream)),
+  return device_status(fbev::launch_backward_temporal(p, grad_out, n_feat > 0 ? grad_features : nullptr, Cp, ego,
+                                                      grad_prev, fd.C, static_cast<hipStream_t>(stream)),
                        "fbev_backward_temporal launch");
 }
 

@@ -46,5 +46,9 @@ hipError_t launch_align_forward(const Problem& p, const float* prev, int Cp, con
                                 hipStream_t stream);
 hipError_t launch_align_backward(const Problem& p, const float* grad, int Cp, const float* ego, float* gprev, int c0,
                                  hipStream_t stream);
+// The temporal backward: dL/dF of the current frame's channels and dL/dprev of the aligned previous
+// map, in one launch after the zero-fill when both parts have work (separate launches otherwise).
+hipError_t launch_backward_temporal(const Problem& p, const float* grad_out, float* grad_feat, int Cp, const float* ego,
+                                    float* grad_prev, int c0, hipStream_t stream);
 
 }  // namespace fbev

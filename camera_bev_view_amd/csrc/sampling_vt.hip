@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bev_align.h"
 #include "kernels.h"
 #include "wave_ops.h"
 
@@ -595,12 +596,13 @@ __device__ __forceinline__ int table_slot(int* sTag, int pix, int& fresh) {
   return -1;
 }
 
+// One workgroup of the backward: tile `bid` of `nblk` (renumbered per XCD), channel group `group`.
 template <bool ML>
-__global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
+__device__ __forceinline__ void sampling_vt_bwd_tile(const BwdArgs& a, unsigned char* smem, int bid, int nblk,
+                                                     int group) {
   static_assert(kSlots == (1 << kSlotBits), "table size matches the hash width");
   static_assert(4 * kWaves * kBwdRegion < (1 << 16), "sorted positions and per-slot counts fit 16 bits");
   const Problem& p = a.p;
-  extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
   unsigned char* cur = smem + sizeof(double) * 12 * p.N;
   float* sG = reinterpret_cast<float*>(cur);                 // [kBwdCells][kBwdGLd] grad tile, channels last
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   cur += sizeof(int) * kWaves;
   int* sFlag = reinterpret_cast<int*>(cur);                  // [0] more rounds, [1] occupied slots, [2] slots taken
 
-  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(bid, nblk);
   const int yt = tile % a.tiles_y;
   const int r1 = tile / a.tiles_y;
   const int xt = r1 % a.tiles_x;
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   const int x_base = xt * kBwdTX, y_base = yt * kBwdTY;
   const int ncx = min(kBwdTX, p.X - x_base), ncy = min(kBwdTY, p.Y - y_base);
   const int n_cells = ncx * ncy;
-  const int c_lo = blockIdx.y * kBwdCg;
+  const int c_lo = group * kBwdCg;
   const int Cg = min(kBwdCg, p.C - c_lo);
 
   // grad tile [Cg][n_cells] (rows of ncy consecutive y): the loads are issued first and
@@ -964,6 +966,28 @@ __global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
   }   // levels
 }
 
+template <bool ML>
+__global__ __launch_bounds__(kBlock) void sampling_vt_bwd(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  sampling_vt_bwd_tile<ML>(a, smem, blockIdx.x, gridDim.x, blockIdx.y);
+}
+
+// The temporal backward in one launch: workgroups [0, groups * tiles_pad) are the Sampling-VT backward's
+// (channel group, tile) units, tiles padded to a multiple of 8 so that both parts keep their XCD
+// numbering; the rest resample the previous map's gradient.  The dispatcher hands out workgroups in
+// order, so the resampling units fill the slots that the backward's last tiles leave idle.
+__global__ __launch_bounds__(kBlock) void temporal_bwd(BwdArgs a, AlignArgs al, int tiles, int tiles_pad,
+                                                       int svt_blocks, int align_blocks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int v = blockIdx.x;
+  if (v < svt_blocks) {
+    const int group = v / tiles_pad, t = v - group * tiles_pad;
+    if (t < tiles) sampling_vt_bwd_tile<false>(a, smem, t, tiles, group);
+    return;
+  }
+  align_bwd_body(al, v - svt_blocks, align_blocks);
+}
+
 __global__ void fill_zero_f32(float* __restrict__ dst, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1072,34 +1096,80 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
   return hipSuccess;
 }
 
-hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream) {
+namespace {
+
+size_t bwd_shmem(const Problem& p) {
+  return sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int2) * kSlots +
+         sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
+         sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
+}
+
+// dL/dF := 0 on the stream (the backward then adds with atomics).
+hipError_t zero_grad(const Problem& p, float* grad_feat, hipStream_t stream) {
   const size_t nF = (size_t)p.B * p.N * p.P * p.C;
   if (nF == 0) return hipSuccess;
-  {
-    const size_t blocks = (nF / 4 + 255) / 256;
-    const unsigned nb = (unsigned)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
-    hipLaunchKernelGGL(fill_zero_f32, dim3(nb), dim3(256), 0, stream, grad_feat, nF);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const size_t blocks = (nF / 4 + 255) / 256;
+  const unsigned nb = (unsigned)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
+  hipLaunchKernelGGL(fill_zero_f32, dim3(nb), dim3(256), 0, stream, grad_feat, nF);
+  return hipGetLastError();
+}
+
+BwdArgs bwd_args(const Problem& p, const float* grad_out, float* grad_feat, long long& tiles) {
   BwdArgs a;
   a.p = p;
   a.grad = grad_out;
   a.dF = grad_feat;
   a.tiles_x = (p.X + kBwdTX - 1) / kBwdTX;
   a.tiles_y = (p.Y + kBwdTY - 1) / kBwdTY;
-  const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
+  tiles = (long long)p.B * a.tiles_x * a.tiles_y;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream) {
+  const size_t nF = (size_t)p.B * p.N * p.P * p.C;
+  if (nF == 0) return hipSuccess;
+  hipError_t e = zero_grad(p, grad_feat, stream);
+  if (e != hipSuccess) return e;
+  long long tiles = 0;
+  const BwdArgs a = bwd_args(p, grad_out, grad_feat, tiles);
   if (tiles == 0 || p.Z == 0 || p.C == 0) return hipSuccess;
   const int groups = (p.C + kBwdCg - 1) / kBwdCg;
-  const size_t shmem = sizeof(double) * 12 * p.N + sizeof(float) * kBwdCells * kBwdGLd + sizeof(int2) * kSlots +
-                       sizeof(int) * kSlots * 2 + sizeof(int2) * kBwdPend * kWaves + sizeof(int2) * kBwdRegion * kWaves * 2 +
-                       sizeof(int4) * kOver * kWaves + sizeof(int) * kWaves + sizeof(int) * 4;
+  const size_t shmem = bwd_shmem(p);
   if (p.L == 1) {
     hipLaunchKernelGGL(sampling_vt_bwd<false>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream,
                        a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(sampling_vt_bwd<true>, dim3((unsigned)tiles, (unsigned)groups), dim3(kBlock), shmem, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_temporal(const Problem& p, const float* grad_out, float* grad_feat, int Cp, const float* ego,
+                                    float* grad_prev, int c0, hipStream_t stream) {
+  const size_t nF = (size_t)p.B * p.N * p.P * p.C;
+  long long tiles = 0;
+  const BwdArgs a = bwd_args(p, grad_out, grad_feat, tiles);
+  const bool current = nF > 0 && tiles > 0 && p.Z > 0 && p.C > 0;
+  const bool previous = p.B > 0 && Cp > 0 && p.X > 0 && p.Y > 0;
+  if (!current || !previous || p.L != 1) {       // one part alone: its own launches
+    hipError_t e = launch_backward(p, grad_out, grad_feat, stream);
+    if (e == hipSuccess && previous) e = launch_align_backward(p, grad_out, Cp, ego, grad_prev, c0, stream);
+    return e;
+  }
+  hipError_t e = zero_grad(p, grad_feat, stream);
+  if (e != hipSuccess) return e;
+  AlignArgs al = align_args(p, Cp, ego, c0);
+  al.src = grad_out;
+  al.dst = grad_prev;
+  const long long align_blocks = align_grid(al).x;
+  const int groups = (p.C + kBwdCg - 1) / kBwdCg;
+  const long long tiles_pad = (tiles + 7) / 8 * 8;
+  const long long svt_blocks = groups * tiles_pad;
+  if (svt_blocks + align_blocks >= (1ll << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(temporal_bwd, dim3((unsigned)(svt_blocks + align_blocks)), dim3(kBlock), bwd_shmem(p), stream, a,
+                     al, (int)tiles, (int)tiles_pad, (int)svt_blocks, (int)align_blocks);
   return hipGetLastError();
 }
 
