@@ -161,14 +161,15 @@ fbev_status forward_impl(const void* features, fbev_dtype dtype, fbev_feat_desc 
   p.feat = features;
   p.elem_bytes = es;
   p.vec_bytes = ((fd.C * es) % 16 == 0 && (addr & 15) == 0) ? 16 : 4;
-  if (n_out > 0 || (counts != nullptr && n_cnt > 0)) {
-    s = device_status(fbev::launch_forward(p, n_out > 0 ? out : nullptr, n_cnt > 0 ? counts : nullptr,
-                                           static_cast<hipStream_t>(stream)),
-                      "fbev_forward launch");
-    if (s != FBEV_OK) return s;
+  const bool current = n_out > 0 || (counts != nullptr && n_cnt > 0);
+  if (n_prev == 0) {
+    if (!current) return FBEV_OK;
+    return device_status(fbev::launch_forward(p, n_out > 0 ? out : nullptr, n_cnt > 0 ? counts : nullptr,
+                                              static_cast<hipStream_t>(stream)),
+                         "fbev_forward launch");
   }
-  if (n_prev == 0) return FBEV_OK;
-  return device_status(fbev::launch_align_forward(p, prev, Cp, ego, out, fd.C, static_cast<hipStream_t>(stream)),
+  return device_status(fbev::launch_forward_temporal(p, out, n_cnt > 0 ? counts : nullptr, current, Cp, prev, ego,
+                                                     fd.C, static_cast<hipStream_t>(stream)),
                        "fbev_forward_temporal launch");
 }
 

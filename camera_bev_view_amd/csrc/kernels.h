@@ -46,6 +46,11 @@ hipError_t launch_align_forward(const Problem& p, const float* prev, int Cp, con
                                 hipStream_t stream);
 hipError_t launch_align_backward(const Problem& p, const float* grad, int Cp, const float* ego, float* gprev, int c0,
                                  hipStream_t stream);
+// The temporal forward: the current frame's channels (when `current`: output channels or counts to
+// write) and the aligned previous map after them, its resampling riding with the forward's last launch
+// when the channel layout allows (a separate launch otherwise).
+hipError_t launch_forward_temporal(const Problem& p, float* out, uint8_t* counts, bool current, int Cp,
+                                   const float* prev, const float* ego, int c0, hipStream_t stream);
 // The temporal backward: dL/dF of the current frame's channels and dL/dprev of the aligned previous
 // map, in one launch after the zero-fill when both parts have work (separate launches otherwise).
 hipError_t launch_backward_temporal(const Problem& p, const float* grad_out, float* grad_feat, int Cp, const float* ego,

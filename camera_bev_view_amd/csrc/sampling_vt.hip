@@ -367,15 +367,14 @@ struct FwdWaves {
 
 // Forward kernel.  L lanes cover one tap's channel group with D dwords each
 // (L * D * 4 == group bytes); S = 64 / L slots; T = S / 4 samples per step.
+// One workgroup of the forward: tile `bid` of `nblk` (renumbered per XCD).
 template <int D, int L, bool BF16, bool ML>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FwdWaves<D, BF16, ML>::value)))
-void sampling_vt_fwd(FwdArgs a) {
+__device__ __forceinline__ void sampling_vt_fwd_tile(const FwdArgs& a, unsigned char* smem, int bid, int nblk) {
   using Ln = Lane<D, BF16>;
   constexpr int kVec = Ln::kVec;
   constexpr int S = kWave / L;
   static_assert(S >= 4 && (S & 3) == 0, "lanes per tap divide the wave");
   const Problem& p = a.p;
-  extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);
   unsigned char* cur = smem + sizeof(double) * 12 * p.N;
   int2* sPend = reinterpret_cast<int2*>(cur);
@@ -386,7 +385,7 @@ void sampling_vt_fwd(FwdArgs a) {
   cur += sizeof(int2) * kItems * kWaves;
   float* sOut = reinterpret_cast<float*>(cur);
 
-  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(bid, nblk);
   const int yt = tile % a.tiles_y;
   const int bx = tile / a.tiles_y;
   const int x = bx % p.X;
@@ -572,6 +571,28 @@ void sampling_vt_fwd(FwdArgs a) {
         __builtin_nontemporal_store(sOut[c * kTileLd + yl], ob + c * c_stride + yl);
     }
   }
+}
+
+template <int D, int L, bool BF16, bool ML>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FwdWaves<D, BF16, ML>::value)))
+void sampling_vt_fwd(FwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  sampling_vt_fwd_tile<D, L, BF16, ML>(a, smem, blockIdx.x, gridDim.x);
+}
+
+// The temporal forward's last channel group in one launch: workgroups [0, tiles_pad) are the forward's
+// tiles (padded to a multiple of 8, so both parts keep their XCD numbering), the rest resample the
+// previous map into the output's last channels, filling the slots the forward's last tiles leave idle.
+template <int D, int L, bool BF16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FwdWaves<D, BF16, false>::value)))
+void temporal_fwd(FwdArgs a, AlignArgs al, int tiles, int tiles_pad, int align_blocks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int v = blockIdx.x;
+  if (v < tiles_pad) {
+    if (v < tiles) sampling_vt_fwd_tile<D, L, BF16, false>(a, smem, v, tiles);
+    return;
+  }
+  align_fwd_body(al, v - tiles_pad, align_blocks);
 }
 
 struct BwdArgs {
@@ -1045,7 +1066,30 @@ void pick_layout(int bytes, int& D, int& L) {
 
 }  // namespace
 
-hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
+namespace {
+
+// The temporal forward's last channel group with the resampling units appended (16 lanes per tap,
+// D = 1, 2, 4 or 8 dwords per lane); false for other layouts, which then take separate launches.
+template <bool BF16>
+bool dispatch_temporal_fwd(int D, int L, const FwdArgs& a, const AlignArgs& al, int tiles, size_t shmem,
+                           hipStream_t stream) {
+  if (L != 16 || (D != 1 && D != 2 && D != 4 && D != 8)) return false;
+  const int tiles_pad = (tiles + 7) / 8 * 8;
+  const long long align_blocks = (long long)al.nblk * al.nchunk * al.B;
+  if ((long long)tiles_pad + align_blocks >= (1ll << 31)) return false;
+  const dim3 grid((unsigned)(tiles_pad + align_blocks));
+  const int ab = (int)align_blocks;
+  if (D == 1) hipLaunchKernelGGL((temporal_fwd<1, 16, BF16>), grid, dim3(kBlock), shmem, stream, a, al, tiles, tiles_pad, ab);
+  if (D == 2) hipLaunchKernelGGL((temporal_fwd<2, 16, BF16>), grid, dim3(kBlock), shmem, stream, a, al, tiles, tiles_pad, ab);
+  if (D == 4) hipLaunchKernelGGL((temporal_fwd<4, 16, BF16>), grid, dim3(kBlock), shmem, stream, a, al, tiles, tiles_pad, ab);
+  if (D == 8) hipLaunchKernelGGL((temporal_fwd<8, 16, BF16>), grid, dim3(kBlock), shmem, stream, a, al, tiles, tiles_pad, ab);
+  return true;
+}
+
+// The forward over all channel groups; with `al` the resampling of a temporal forward rides with the
+// last group's launch when its layout allows (*al_done is set then).
+hipError_t forward_groups(const Problem& p, float* out, uint8_t* counts, const AlignArgs* al, bool* al_done,
+                          hipStream_t stream) {
   FwdArgs a;
   a.p = p;
   a.out = out;
@@ -1085,8 +1129,14 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
     const size_t shmem = sizeof(double) * 12 * p.N + sizeof(int2) * kPend * kWaves + sizeof(Rec) * kRec * kWaves +
                          sizeof(int2) * kItems * kWaves + sizeof(float) * (size_t)(Cg > 0 ? Cg : 1) * kTileLd;
     const dim3 grid((unsigned)tiles);
-    const bool ok = (es == 2) ? dispatch_fwd<true>(D, L, a, grid, shmem, stream)
-                              : dispatch_fwd<false>(D, L, a, grid, shmem, stream);
+    bool fused = false;
+    if (al != nullptr && c + Cg >= p.C && tiles < (1ll << 31)) {
+      fused = (es == 2) ? dispatch_temporal_fwd<true>(D, L, a, *al, (int)tiles, shmem, stream)
+                        : dispatch_temporal_fwd<false>(D, L, a, *al, (int)tiles, shmem, stream);
+      if (fused) *al_done = true;
+    }
+    const bool ok = fused || ((es == 2) ? dispatch_fwd<true>(D, L, a, grid, shmem, stream)
+                                        : dispatch_fwd<false>(D, L, a, grid, shmem, stream));
     if (!ok) return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1094,6 +1144,29 @@ hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStre
     first = false;
   } while (c < p.C);
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
+  return forward_groups(p, out, counts, nullptr, nullptr, stream);
+}
+
+hipError_t launch_forward_temporal(const Problem& p, float* out, uint8_t* counts, bool current, int Cp,
+                                   const float* prev, const float* ego, int c0, hipStream_t stream) {
+  const bool previous = p.B > 0 && Cp > 0 && p.X > 0 && p.Y > 0;
+  bool al_done = !previous;
+  if (current) {
+    AlignArgs al = align_args(p, Cp, ego, c0);
+    al.src = prev;
+    al.dst = out;
+    align_grid(al);
+    const hipError_t e = forward_groups(p, p.C > 0 ? out : nullptr, counts, (previous && p.L == 1) ? &al : nullptr,
+                                        &al_done, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (al_done) return hipSuccess;
+  return launch_align_forward(p, prev, Cp, ego, out, c0, stream);
 }
 
 namespace {
