@@ -476,8 +476,8 @@ def main_temporal(args):
     bwd_bytes = out_elems * 4 + feat_bytes + B * Cp * X * Y * 4 + cams       # upstream gradient, dL/dF, dL/dprev
     fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems)
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems)
-    dom_k, dom, dom_bytes = (["sampling_vt_fwd", "bev_align_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        (["fill_zero_f32", "sampling_vt_bwd", "bev_align_bwd"], bwd, bwd_bytes)
+    dom_k, dom, dom_bytes = (["temporal_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
+        (["fill_zero_f32", "temporal_bwd"], bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
                       "seeded planar ego motion",
