@@ -83,6 +83,7 @@ def test_temporal_workload():
 TEMPORAL_CASES = [
     # label, B, N, C, H, W, X, Y, Z, Cp, yaw, shift
     ("two samples, ragged grid and chunk tail", 2, 6, 12, 8, 22, 23, 37, 4, 13, None, None),
+    ("two samples, one launch per direction", 2, 6, 32, 8, 22, 21, 34, 4, 11, 8.0, (1.5, -0.5)),
     ("one previous channel, strong turn", 1, 6, 8, 8, 22, 30, 30, 3, 1, 35.0, (3.0, -2.0)),
     ("no current channels", 1, 6, 0, 8, 22, 20, 24, 3, 9, 10.0, (1.0, 1.0)),
     ("backwards motion off the grid", 1, 6, 4, 8, 22, 16, 16, 3, 5, -3.0, (-40.0, 0.0)),
