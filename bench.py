@@ -97,7 +97,9 @@ def pass_roofline(kernels, rate, nbytes, workload):
 def time_passes(args, dev, passes, label):
     """W untimed warm-up steps, then K timed steps of ``passes`` (callables, run in order on the
     current stream) bracketed by synchronizations; HIP events around every pass.  Returns
-    (ms per step over the whole timed region, [mean ms of each pass])."""
+    (ms per step over the whole timed region, [mean ms of each pass]).  With --cold a 1 GiB buffer is
+    overwritten before every timed step (more than the L2s and the 256 MB Infinity Cache hold), so each
+    step starts with its inputs in HBM only; the step time is then the sum of each step's own passes."""
     import numpy as np
     import torch
     log(f"[bench] warmup {args.warmup} steps on {label}")
@@ -111,10 +113,13 @@ def time_passes(args, dev, passes, label):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+    log(f"[bench] timing {args.steps} steps" + (" (cold: cache sweep before each)" if args.cold else ""))
     torch.cuda.synchronize()
     t_start.record(stream)
     for k in range(args.steps):
+        if sweep is not None:
+            sweep.fill_(float(k))
         for i, f in enumerate(passes):
             ev[k][i].record(stream)
             f()
@@ -122,6 +127,8 @@ def time_passes(args, dev, passes, label):
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    if args.cold:
+        ms_step = float(np.mean([e[0].elapsed_time(e[n]) for e in ev]))
     pass_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(n)]
     log(f"[bench] done: {ms_step * 1e3:.2f} us/step (passes " + ", ".join(f"{m * 1e3:.2f}" for m in pass_ms) + " us)")
     return ms_step, pass_ms
@@ -140,6 +147,8 @@ def pass_rates(ms, nbytes, **counts):
 
 def bench_line(args, value, ms_step, dtype, data, config):
     """The JSON line's fixed fields, in order."""
+    if args.cold:
+        config = dict(config, cache="cold: 1 GiB overwritten before every timed step")
     return {"metric": METRIC, "value": value, "unit": "BEV output elems/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": dtype, "data": data, "config": config}
@@ -501,6 +510,7 @@ def main():
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--cpu-rows", type=int, default=None, help="X-rows of the CPU-oracle sample (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="overwrite 1 GiB before every timed step (cold caches)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
