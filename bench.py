@@ -516,8 +516,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by batch sample or BEV rows with no exchange in the forward; "
-              "multi-GPU runs are not part of this build)", file=sys.stderr)
+              "(the path would shard by batch sample or BEV rows with no exchange in the forward; "
+              "only the one-GPU measurement is implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
