@@ -47,10 +47,25 @@ LSS_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "lift_splat.hip")
 DEFORM_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "deform_agg.hip")
 CAMERA_SRC = os.path.join(ROOT, "camera_bev_view_amd", "csrc", "camera_grad.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# The host dispatch chooses lane layouts, tile shapes and instantiations: counters taken before a change
+# to these files no longer describe the launched kernels, so every traffic record must carry their hashes.
+DISPATCH_SRCS = ("camera_bev_view_amd/csrc/kernels.h", "camera_bev_view_amd/csrc/flashbev_api.cpp")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def kernel_source_hash(path: str = KERNEL_SRC) -> str:
@@ -74,6 +89,8 @@ def measured_traffic(kernel, workload: str):
     w = rec.get("workloads", {}).get(workload, {})
     sources = w.get("sources") or {w.get("source", os.path.relpath(KERNEL_SRC, ROOT)):
                                    w.get("source_sha256", rec.get("source_sha256"))}
+    if any(d not in sources for d in DISPATCH_SRCS):
+        return None
     try:
         if any(sha != kernel_source_hash(os.path.join(ROOT, src)) for src, sha in sources.items()):
             return None
@@ -188,7 +205,7 @@ def cpu_baseline_levels(inp, rows):
         "kind": "oracle",
         "sample": f"fp64 numpy multi-level oracle, forward + backward over X-rows 0..{rows - 1} of {inp.X} "
                   f"({B * C * rows * inp.Y} outputs), wall {wall:.2f} s, process CPU {cpu:.2f} s, "
-                  f"{len(os.sched_getaffinity(0))} cores available",
+                  f"{len(os.sched_getaffinity(0))} cores available, {cpu_model()}",
     }
 
 
@@ -212,7 +229,7 @@ def cpu_baseline(inp, rows):
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, forward + backward over X-rows 0..{rows - 1} of {inp.X} "
                   f"({B * C * rows * inp.Y} outputs), wall {wall:.2f} s, process CPU {cpu:.2f} s, "
-                  f"{len(os.sched_getaffinity(0))} cores available",
+                  f"{len(os.sched_getaffinity(0))} cores available, {cpu_model()}",
     }
 
 
@@ -238,7 +255,8 @@ def cpu_baseline_lss(inp, min_seconds=10.0):
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
         "sample": f"fp64 numpy Lift-Splat oracle, {reps} whole forward + backward steps of the workload, "
-                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available, "
+                  f"{cpu_model()}",
     }
 
 
@@ -321,7 +339,7 @@ def cpu_baseline_deform(inp, max_queries, min_seconds=10.0):
         "kind": "oracle",
         "sample": f"fp64 numpy Deformable Aggregation oracle, {reps} forward + backward passes over queries "
                   f"0..{Qs - 1} of {inp.anchors.shape[1]} (output elements = queries x channels), wall {wall:.2f} s, "
-                  f"process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+                  f"process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available, {cpu_model()}",
         "in_view_samples_in_sample": in_view,
     }
 
@@ -389,7 +407,8 @@ def cpu_baseline_cameras(inp, min_seconds=10.0):
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
         "sample": f"fp64 numpy camera-gradient oracle, {reps} whole passes over the {inp.X}x{inp.Y}x{inp.Z} grid, "
-                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available",
+                  f"wall {wall:.2f} s, process CPU {cpu:.2f} s, {len(os.sched_getaffinity(0))} cores available, "
+                  f"{cpu_model()}",
     }
 
 
@@ -452,7 +471,7 @@ def cpu_baseline_temporal(ti, min_seconds=10.0):
         "kind": "oracle",
         "sample": f"fp64 numpy temporal oracle (Sampling-VT + resampled previous map), {reps} forward + backward "
                   f"passes over the whole {cur.X}x{cur.Y} grid, wall {wall:.2f} s, process CPU {cpu:.2f} s, "
-                  f"{len(os.sched_getaffinity(0))} cores available",
+                  f"{len(os.sched_getaffinity(0))} cores available, {cpu_model()}",
     }
 
 

@@ -103,6 +103,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fbev_last_error.restype = ctypes.c_char_p
         lib.fbev_abi_version.argtypes = []
         lib.fbev_abi_version.restype = ctypes.c_int32
+        got = lib.fbev_abi_version()
+        if got != ABI_VERSION:
+            raise FlashBevError(-1, f"{path} reports ABI {got}, this binding expects {ABI_VERSION}; rebuild it")
         _lib = lib
         return lib
 

@@ -195,6 +195,12 @@ fbev_status backward_impl(const float* grad_out, fbev_feat_desc fd, int32_t L, c
   if (batch_elems >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's gradient spans %lld elements (limit 2^31 - 1)",
                 (long long)batch_elems);
+  // The resampling adjoint gathers, for each previous cell, the current cells within a window of
+  // half-width |cos| + |sin| * (cell aspect) around the inverse-mapped centre (index units); a rigid
+  // motion fits the window for every turn only when the cells' aspect ratio stays below 15.
+  if (n_prev > 0 && (p.dx / p.dy >= 15.0 || p.dy / p.dx >= 15.0))
+    return fail(FBEV_ERR_UNSUPPORTED, "cell aspect ratio dx/dy = %g: the previous-map gradient needs it in (1/15, 15)",
+                p.dx / p.dy);
   p.feat = nullptr;
   p.elem_bytes = 4;
   p.vec_bytes = 4;

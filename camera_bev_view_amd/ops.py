@@ -29,6 +29,23 @@ def _check_cams(K: torch.Tensor, R: torch.Tensor, t: torch.Tensor, B: int, N: in
             raise ValueError(f"{name} must be a contiguous float32 tensor on {device}")
 
 
+def _check_device_tensor(name: str, x: torch.Tensor, device=None) -> None:
+    """x must live in device memory (on ``device`` when given): the library dereferences it on the GPU."""
+    if not x.is_cuda or (device is not None and x.device != device):
+        raise ValueError(f"{name} must be a device tensor" + (f" on {device}" if device is not None else ""))
+
+
+def _check_out(name: str, out: torch.Tensor, shape, device) -> None:
+    if tuple(out.shape) != tuple(shape) or out.dtype != torch.float32 or not out.is_contiguous() \
+            or out.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on {device}")
+
+
+def _check_workspace(ws: torch.Tensor, device) -> None:
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -51,8 +68,8 @@ def forward(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: torch.T
     _check_cams(K, R, t, B, N, dev)
     if out is None:
         out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
-    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    else:
+        _check_out("out", out, (B, C, X, Y), dev)
     counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
     lib = _lib.load()
     _lib.check(lib.fbev_forward(_ptr(features), _DTYPES[features.dtype], _lib.feat_desc(B, N, C, H, W),
@@ -67,6 +84,7 @@ def backward(grad_out: torch.Tensor, feat_shape: Sequence[int], K: torch.Tensor,
     B, N, H, W, C = (int(v) for v in feat_shape)
     if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32:
         raise ValueError("grad_out must be float32 [B,C,X,Y]")
+    _check_device_tensor("grad_out", grad_out)
     grad_out = grad_out.contiguous()
     dev = grad_out.device
     _check_cams(K, R, t, B, N, dev)
@@ -89,12 +107,15 @@ def camera_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Ten
     dev = features.device
     if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32:
         raise ValueError("grad_out must be float32 [B,C,X,Y]")
+    _check_device_tensor("grad_out", grad_out, dev)
     grad_out = grad_out.contiguous()
     _check_cams(K, R, t, B, N, dev)
     lib = _lib.load()
     fd = _lib.feat_desc(B, N, C, H, W)
     need = ctypes.c_size_t(0)
     _lib.check(lib.fbev_backward_cameras_workspace(fd, X, Y, Z, ctypes.byref(need)))
+    if workspace is not None:
+        _check_workspace(workspace, dev)
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=dev)
     gK = torch.empty((B, N, 3, 3), dtype=torch.float32, device=dev)
@@ -166,8 +187,8 @@ def forward_temporal(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t
     Cp = _check_temporal(prev_bev, ego, B, X, Y, dev)
     if out is None:
         out = torch.empty((B, C + Cp, X, Y), dtype=torch.float32, device=dev)
-    elif tuple(out.shape) != (B, C + Cp, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, C + Cp, X, Y] tensor")
+    else:
+        _check_out("out", out, (B, C + Cp, X, Y), dev)
     counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
     lib = _lib.load()
     _lib.check(lib.fbev_forward_temporal(_ptr(features), _DTYPES[features.dtype], _lib.feat_desc(B, N, C, H, W),
@@ -183,6 +204,7 @@ def backward_temporal(grad_out: torch.Tensor, feat_shape: Sequence[int], K: torc
     B, N, H, W, C = (int(v) for v in feat_shape)
     if tuple(grad_out.shape) != (B, C + Cp, X, Y) or grad_out.dtype != torch.float32:
         raise ValueError("grad_out must be float32 [B, C + Cp, X, Y]")
+    _check_device_tensor("grad_out", grad_out)
     grad_out = grad_out.contiguous()
     dev = grad_out.device
     _check_cams(K, R, t, B, N, dev)
@@ -263,8 +285,8 @@ def forward_levels(packed: torch.Tensor, shapes: Sequence[Sequence[int]], K: tor
     _check_cams(K, R, t, B, N, dev)
     if out is None:
         out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
-    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    else:
+        _check_out("out", out, (B, C, X, Y), dev)
     counts = torch.empty((B, X, Y, Z), dtype=torch.uint8, device=dev) if with_counts else None
     lib = _lib.load()
     _lib.check(lib.fbev_forward_levels(_ptr(packed), _DTYPES[packed.dtype], _lib.feat_desc(B, N, C, H, W),
@@ -283,6 +305,7 @@ def backward_levels(grad_out: torch.Tensor, B: int, N: int, C: int, shapes: Sequ
     H, W = (int(v) for v in shapes[0])
     ratios = level_ratios(H, W, shapes)
     P = sum(int(h) * int(w) for (h, w) in shapes)
+    _check_device_tensor("grad_out", grad_out)
     dev = grad_out.device
     _check_cams(K, R, t, B, N, dev)
     gF = torch.empty((B, N, P, C), dtype=torch.float32, device=dev)
@@ -319,8 +342,8 @@ def lss_forward(depth: torch.Tensor, context: torch.Tensor, K: torch.Tensor, R: 
     _check_cams(K, R, t, B, N, dev)
     if out is None:
         out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
-    elif tuple(out.shape) != (B, C, X, Y) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,C,X,Y] tensor")
+    else:
+        _check_out("out", out, (B, C, X, Y), dev)
     lib = _lib.load()
     _lib.check(lib.fbev_lss_forward(_ptr(depth), _ptr(context), _lib.feat_desc(B, N, C, H, W), D, float(d_min),
                                     float(d_step), _ptr(K), _ptr(R), _ptr(t), _lib.bev_range(bev_range), X, Y,
@@ -385,8 +408,8 @@ def deform_forward(features: torch.Tensor, K: torch.Tensor, R: torch.Tensor, t: 
     B, N, H, W, C, Q, Kp, dev = _check_deform(features, K, R, t, anchors, offsets, weights)
     if out is None:
         out = torch.empty((B, Q, C), dtype=torch.float32, device=dev)
-    elif tuple(out.shape) != (B, Q, C) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,Q,C] tensor")
+    else:
+        _check_out("out", out, (B, Q, C), dev)
     lib = _lib.load()
     _lib.check(lib.fbev_deform_forward(_ptr(features), _lib.feat_desc(B, N, C, H, W), _ptr(K), _ptr(R), _ptr(t),
                                        _ptr(anchors), _ptr(offsets), _ptr(weights), Q, Kp, _ptr(out), _stream(dev)))
@@ -410,6 +433,8 @@ def deform_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Ten
     fd = _lib.feat_desc(B, N, C, H, W)
     need = ctypes.c_size_t(0)
     _lib.check(lib.fbev_deform_backward_workspace(fd, Q, Kp, ctypes.byref(need)))
+    if workspace is not None:
+        _check_workspace(workspace, dev)
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=dev)
     _lib.check(lib.fbev_deform_backward(_ptr(grad_out), _ptr(features), fd, _ptr(K), _ptr(R), _ptr(t),

@@ -453,9 +453,9 @@ def make_temporal_inputs(name: str = "temporal") -> TemporalInputs:
 
 def random_temporal_case(seed: int, B: int, N: int, C: int, H: int, W: int, X: int, Y: int, Z: int, Cp: int,
                          rng6=(-30.0, 30.0, -30.0, 30.0, -4.0, 3.0), yaw_deg: Optional[float] = None,
-                         shift=None) -> TemporalInputs:
+                         shift=None, dtype: str = "f32") -> TemporalInputs:
     """An arbitrary-size seeded temporal case; ``yaw_deg`` / ``shift`` fix the motion."""
-    cur = random_case(5000 + seed, B, N, C, H, W, X, Y, Z, rng6=rng6, with_grad=False)
+    cur = random_case(5000 + seed, B, N, C, H, W, X, Y, Z, rng6=rng6, dtype=dtype, with_grad=False)
     prev = np.random.default_rng([5000 + seed, 1]).standard_normal((B, Cp, X, Y), dtype=np.float32)
     g = np.random.default_rng([5000 + seed, 2]).standard_normal((B, C + Cp, X, Y), dtype=np.float32)
     return TemporalInputs(cur, prev, make_ego_motion(5000 + seed, B, yaw_deg, shift), g)

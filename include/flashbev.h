@@ -181,9 +181,13 @@ fbev_status fbev_forward_temporal(const void* features, fbev_dtype dtype, fbev_f
  * deterministic) = the adjoint of the resampling: every current cell passes
  * grad_out[b, C + c, i, j] times its bilinear weights to its four taps.  The
  * adjoint is computed as a gather over the current cells whose sample can
- * reach a previous cell; motions whose inverse stretches the grid by more than
- * 16 cells per cell (far from rigid) are not supported and leave those cells'
- * gradient at 0.  No gradient with respect to the ego motion.
+ * reach a previous cell, within 16 cells per axis of the inverse-mapped cell.
+ * A rigid motion stays inside that window whatever its turn when the cell
+ * aspect ratio dx/dy lies in (1/15, 15); other grids give
+ * FBEV_ERR_UNSUPPORTED when Cp > 0.  A non-rigid motion (ego is read on the
+ * device, so the host cannot check it) whose inverse stretches the grid past
+ * the window leaves those previous cells' gradient at 0.  No gradient with
+ * respect to the ego motion.
  *   grad_out : [B,C+Cp,X,Y] fp32, device, read only.
  */
 fbev_status fbev_backward_temporal(const float* grad_out, fbev_feat_desc fd, const float* K, const float* R,

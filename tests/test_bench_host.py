@@ -45,14 +45,29 @@ def test_traffic_counters_follow_their_sources(tmp_path, monkeypatch):
     src.write_bytes(b"kernel source v1")
     rel = os.path.relpath(src, bench.ROOT)
     sha = hashlib.sha256(b"kernel source v1").hexdigest()
-    rec = {"workloads": {"w": {"sources": {rel: sha},
-                               "kernels": {"a": {"bytes_per_launch": 100}, "b": {"bytes_per_launch": 23}}}}}
+    disp = tmp_path / "dispatch.cpp"
+    disp.write_bytes(b"dispatch v1")
+    drel = os.path.relpath(disp, bench.ROOT)
+    dsha = hashlib.sha256(b"dispatch v1").hexdigest()
+    monkeypatch.setattr(bench, "DISPATCH_SRCS", (drel,))
+    rec = {"workloads": {"w": {"sources": {rel: sha, drel: dsha},
+                               "kernels": {"a": {"bytes_per_launch": 100}, "b": {"bytes_per_launch": 23}}},
+                         "nodispatch": {"sources": {rel: sha}, "kernels": {"a": {"bytes_per_launch": 100}}}}}
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("a", "nodispatch") is None     # no hash of the dispatch code: stale
     assert bench.measured_traffic("a", "w") == 100
     assert bench.measured_traffic(["a", "b"], "w") == 123
     assert bench.measured_traffic(["a", "missing"], "w") is None
     assert bench.measured_traffic("a", "other") is None
+    disp.write_bytes(b"dispatch v2")              # the dispatch changed since the counters were taken
+    assert bench.measured_traffic("a", "w") is None
+    disp.write_bytes(b"dispatch v1")
+    assert bench.measured_traffic("a", "w") == 100
     src.write_bytes(b"kernel source v2")          # the kernel changed since the counters were taken
     assert bench.measured_traffic("a", "w") is None
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

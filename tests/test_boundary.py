@@ -349,8 +349,8 @@ def tfwd(lib, feat=FAKE, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8, prev=FAKE, 
                                      _lib.bev_range(RNG), X, Y, Z, prev, Cp, ego, out, None, None)
 
 
-def tbwd(lib, grad=FAKE, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8, Cp=64, ego=FAKE, gF=FAKE, gP=FAKE):
-    return lib.fbev_backward_temporal(grad, _lib.feat_desc(*desc), FAKE, FAKE, FAKE, _lib.bev_range(RNG), X, Y, Z, Cp,
+def tbwd(lib, grad=FAKE, desc=(1, 6, 64, 16, 44), X=200, Y=200, Z=8, Cp=64, ego=FAKE, gF=FAKE, gP=FAKE, rng=RNG):
+    return lib.fbev_backward_temporal(grad, _lib.feat_desc(*desc), FAKE, FAKE, FAKE, _lib.bev_range(rng), X, Y, Z, Cp,
                                       ego, gF, gP, None)
 
 
@@ -373,6 +373,9 @@ def test_temporal_forward_validation(lib, kwargs, status, msg):
     (dict(ego=None), 1, "ego is NULL"),
     (dict(grad=None), 1, "grad_out is NULL"),
     (dict(gF=None), 1, "grad_features is NULL"),
+    # 0.5 m x 10 m cells: a turn's inverse spans 1 + 20 cells along x, past the gather window
+    (dict(X=200, Y=10), 2, "cell aspect ratio"),
+    (dict(X=7, Y=200, rng=(-50.0, 50.0, -1.0, 1.0, -5.0, 3.0)), 2, "cell aspect ratio"),
 ])
 def test_temporal_backward_validation(lib, kwargs, status, msg):
     assert tbwd(lib, **kwargs) == status
@@ -383,3 +386,21 @@ def test_temporal_empty_problems_return_ok_without_device_work(lib):
     assert tfwd(lib, desc=(0, 6, 64, 16, 44), feat=None, prev=None, ego=None, out=None) == 0
     assert tfwd(lib, X=0, prev=None, ego=None, out=None) == 0
     assert tbwd(lib, desc=(0, 6, 64, 16, 44), grad=None, ego=None, gF=None, gP=None) == 0
+
+
+NO_GPU_HOST = not os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(not NO_GPU_HOST, reason="forces HIP's launch failure by having no device; needs a GPU-less host")
+def test_launch_failure_maps_to_device_error(lib):
+    """Valid arguments on a host without a GPU: validation passes, the HIP launch itself fails, and the
+    call returns FBEV_ERR_DEVICE with HIP's reason in fbev_last_error (nothing is dereferenced)."""
+    assert fwd(lib) == _lib.FBEV_ERR_DEVICE
+    msg = lib.fbev_last_error().decode()
+    assert msg.startswith("fbev_forward launch: ") and len(msg) > len("fbev_forward launch: ")
+    assert bwd(lib) == _lib.FBEV_ERR_DEVICE
+    assert lib.fbev_last_error().decode().startswith("fbev_backward launch: ")
+    assert lib.fbev_status_string(_lib.FBEV_ERR_DEVICE) == b"device error"
+    # a later valid-argument error replaces the text
+    assert fwd(lib, X=-1) == _lib.FBEV_ERR_INVALID_ARGUMENT
+    assert "negative grid size" in lib.fbev_last_error().decode()

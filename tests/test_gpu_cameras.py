@@ -52,7 +52,21 @@ def camera_parity(inp, label, rows=None):
             assert errs[n] <= BWD_REL_L2, f"{label}: dL/d{n} rel L2 {errs[n]:.3e}"
         else:
             assert not got[n].any(), f"{label}: dL/d{n} should be zero"
+    elementwise_check(got, ref, label)
     return got, ref
+
+
+def elementwise_check(got, ref, label):
+    """Per camera, each of its 21 entries (dL/dK 9, dL/dR 9, dL/dt 3) within
+    1e-4 + 1e-3 * (the largest of that camera's 21 reference magnitudes)."""
+    g = np.concatenate([got["K"].reshape(*got["K"].shape[:2], 9), got["R"].reshape(*got["R"].shape[:2], 9),
+                        got["t"]], axis=-1).astype(np.float64)
+    r = np.concatenate([ref["K"].reshape(*ref["K"].shape[:2], 9), ref["R"].reshape(*ref["R"].shape[:2], 9),
+                        ref["t"]], axis=-1).astype(np.float64)
+    bound = 1e-4 + 1e-3 * np.abs(r).max(axis=-1, keepdims=True)
+    d = np.abs(g - r)
+    say(f"[parity] cameras {label}: worst entry |d| / bound = {(d / bound).max(initial=0):.3f}")
+    assert (d <= bound).all(), f"{label}: {int((d > bound).sum())} camera-gradient entries outside the bound"
 
 
 def test_tiny_full():

@@ -71,7 +71,9 @@ def deform_parity(inp, label, backward=True):
     assert not bad_w.any(), f"{label}: {int(bad_w.sum())} dL/dweights outside tolerance"
     k_ok = ~near.any(axis=1)                                        # [B, Q, K]
     tol_o = ATOL + RTOL * max(1.0, np.abs(rO).max(initial=0))
-    bad_o = (np.abs(gO - rO) > tol_o * 10) & k_ok[..., None]
+    ratio_o = float((np.abs(gO - rO) * k_ok[..., None]).max(initial=0) / tol_o)
+    say(f"[parity] deform {label}: dL/doffsets worst |d| / (1e-4 + 1e-5 max|ref|) = {ratio_o:.3f}")
+    bad_o = (np.abs(gO - rO) > tol_o) & k_ok[..., None]
     assert not bad_o.any(), f"{label}: {int(bad_o.sum())} dL/doffsets outside tolerance"
 
 

@@ -74,6 +74,8 @@ def lss_parity(inp, label, backward=True):
     say(f"[parity] lss {label}: forward max|d|={diff.max(initial=0):.3e} excluded cells={int(cells.sum())} "
         f"near-edge points={int(near.sum())} nonzero outputs={int((ref != 0).sum())}")
     assert not bad.any(), f"{label}: {int(bad.sum())} outputs outside tolerance, worst {diff[bad].max():.3e}"
+    # the exclusion may only drop a handful of cells: at most 9 (one point's neighbourhood), or 0.1% of a larger grid
+    assert int(cells.sum()) <= max(9, (B * inp.X * inp.Y) // 1000), f"{label}: {int(cells.sum())} cells excluded"
     if not backward:
         return got, ref
     gd, gc = ops.lss_backward(torch.from_numpy(inp.grad_out).cuda(), dep, ctx, K, R, t, inp.rng6, inp.X, inp.Y,

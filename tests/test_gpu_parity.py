@@ -98,6 +98,13 @@ def test_fwdbwd_workload():
     assert abs(lhs - rhs) <= 1e-5 * abs(lhs)
 
 
+def test_nuscenes_backward_full():
+    """The bench's own backward (nuScenes-shaped, 200x200x8, single level) in full: relative L2
+    and element-wise max |d| <= 1e-4 + 1e-5 max|ref| over every element of dL/dF."""
+    inp = wl.make_inputs("nuscenes", with_grad=True)
+    backward_parity(inp, "nuscenes 1x6x64x16x44 -> 200x200x8 bwd (full)")
+
+
 RAGGED = [
     # dtype, B, N, C, H, W, X, Y, Z      what it exercises
     ("f32", 1, 6, 20, 16, 44, 37, 45, 5),     # 5 chunks/pixel, 12 slots (linear slot sum), ragged tile

@@ -54,6 +54,8 @@ def temporal_parity(ti, label, backward=True, exact=False):
     say(f"[parity] temporal {label}: current max|d|={diff[:, :C].max(initial=0):.3e} aligned max|d|="
         f"{np.where(border_ok[:, None], diff[:, C:], 0).max(initial=0):.3e} excluded cells "
         f"{int((~cell_ok).sum())} / {int((~border_ok).sum())}")
+    # the border exclusion may only drop a handful of cells: at most 4, or 0.1% of a larger grid
+    assert int((~border_ok).sum()) <= max(4, (B * X * Y) // 1000), f"{label}: {int((~border_ok).sum())} excluded"
     assert not bad_cur.any(), f"{label}: {int(bad_cur.sum())} current-frame outputs outside tolerance"
     assert not bad_prev.any(), f"{label}: {int(bad_prev.sum())} aligned outputs outside tolerance"
     if not backward:
@@ -87,13 +89,21 @@ TEMPORAL_CASES = [
     ("one previous channel, strong turn", 1, 6, 8, 8, 22, 30, 30, 3, 1, 35.0, (3.0, -2.0)),
     ("no current channels", 1, 6, 0, 8, 22, 20, 24, 3, 9, 10.0, (1.0, 1.0)),
     ("backwards motion off the grid", 1, 6, 4, 8, 22, 16, 16, 3, 5, -3.0, (-40.0, 0.0)),
+    # bf16 features with the resampling fused into the forward's last (16-lane) channel group
+    ("bf16 features, fused last group", 1, 6, 64, 16, 44, 40, 36, 6, 7, 12.0, (2.0, 1.0), "bf16"),
+    # fp32 with two channel groups (256 + 64): the first launched alone, the last one fused with the resampling
+    ("two channel groups, last fused", 1, 6, 320, 8, 22, 19, 41, 4, 6, -9.0, (-1.0, 2.5)),
+    # 256 + 4 channels: the last group's 4-lane layout has no fused form, so the resampling runs on its own
+    ("two channel groups, separate resampling", 1, 6, 260, 8, 22, 17, 23, 4, 3, 5.0, (0.5, -1.5)),
 ]
 
 
 @pytest.mark.parametrize("case", TEMPORAL_CASES, ids=[c[0] for c in TEMPORAL_CASES])
 def test_temporal_cases(case):
-    label, B, N, C, H, W, X, Y, Z, Cp, yaw, shift = case
-    temporal_parity(wl.random_temporal_case(len(label), B, N, C, H, W, X, Y, Z, Cp, yaw_deg=yaw, shift=shift), label)
+    label, B, N, C, H, W, X, Y, Z, Cp, yaw, shift = case[:12]
+    dtype = case[12] if len(case) > 12 else "f32"
+    temporal_parity(wl.random_temporal_case(len(label), B, N, C, H, W, X, Y, Z, Cp, yaw_deg=yaw, shift=shift,
+                                            dtype=dtype), label)
 
 
 def test_identity_and_quarter_turn_are_exact():

@@ -204,3 +204,34 @@ def test_points_in_different_cells_add_up():
     dep[0, 0, 5, 4, 11] = 1.0                                # a second point in another cell
     a = ls.lss_forward(dep, ctx, K, R, t, rng6, 200, 200, D_MIN, D_STEP)["out"]
     assert np.isclose(a.sum(), 2 * cvec.sum())               # two points, each carrying c: summed, not averaged
+
+
+def test_near_cell_edge_pins_distances_and_units():
+    """Points placed at known metric distances from a cell edge: a 2 m cell grid over [-10, 10) gives
+    edges at every even coordinate; eps is in metres, on both axes and at the grid's outer edges."""
+    rng6 = (-10.0, 10.0, -10.0, 10.0, -5.0, 3.0)
+    X = Y = 10                                      # 2 m cells
+    eps = ls.EDGE_EPS_M
+    centre = np.array([1.0, -3.0, 0.0])             # a cell centre: 1 m from every edge
+    cases = [
+        ((centre[0], centre[1]), False),
+        ((2.0 + 0.5 * eps, centre[1]), True),       # just inside eps of the x = 2 edge
+        ((2.0 - 0.5 * eps, centre[1]), True),       # either side of it
+        ((2.0 + 4.0 * eps, centre[1]), False),      # just outside eps
+        ((centre[0], -4.0 + 0.5 * eps), True),      # the y axis
+        ((centre[0], -4.0 + 4.0 * eps), False),
+        ((-10.0 + 0.5 * eps, centre[1]), True),     # the grid's outer edges
+        ((10.0 - 0.5 * eps, centre[1]), True),
+        ((centre[0], 10.0 - 4.0 * eps), False),
+    ]
+    pts = np.array([[x, y, 0.0] for (x, y), _ in cases])
+    want = np.array([w for _, w in cases])
+    assert np.array_equal(ls.near_cell_edge(pts, rng6, X, Y), want)
+    # a wider eps in metres flags a point 0.1 m from an edge of a 2 m cell, a narrower one does not
+    p = np.array([[2.1, centre[1], 0.0]])
+    assert ls.near_cell_edge(p, rng6, X, Y, eps=0.15)[0]
+    assert not ls.near_cell_edge(p, rng6, X, Y, eps=0.05)[0]
+    # unequal cells: 1 m along x, 4 m along y; a point 0.3 m off a y edge is flagged only for eps > 0.3
+    p = np.array([[0.5, 2.3, 0.0]])                 # x: a 1 m cell's centre; y: 0.3 m above the y = 2 edge
+    assert ls.near_cell_edge(p, rng6, 20, 5, eps=0.31)[0]
+    assert not ls.near_cell_edge(p, rng6, 20, 5, eps=0.29)[0]

@@ -165,3 +165,36 @@ def test_mutation_is_caught(monkeypatch, name, attr, fn):
     assert _pins_pass(), "pins must pass on the unmodified oracle"
     monkeypatch.setattr(tp, attr, fn)
     assert not _pins_pass(), f"planted mistake not caught: {name}"
+
+
+def test_near_border_pins_distances():
+    """A pure shift along x by s cells moves every source index to i + s; the box's edges are at
+    0 and X - 1, so a shift of -(1 - d) puts column 1 at distance d from the lower edge and a
+    shift of +(1 - d) puts column X - 2 at distance d from the upper edge."""
+    rng6 = (-10.0, 10.0, -8.0, 8.0, -5.0, 3.0)
+    X, Y = 10, 8                                       # 2 m cells along both axes
+    prev = np.zeros((1, 1, X, Y))
+    e = svt.EDGE_EPS_PX
+    for d, flagged in ((0.5 * e, True), (4.0 * e, False)):
+        for sign in (-1.0, 1.0):
+            s = sign * (1.0 - d)                      # cells
+            A = np.array([[[1.0, 0.0, 2.0 * s], [0.0, 1.0, 0.0]]])
+            nb = tp.align_prev_bev(prev, A, rng6)["near_border"][0]
+            row = 1 if sign < 0 else X - 2
+            inner = nb[:, 1:Y - 1]                    # columns whose source is off the y edges
+            assert bool(inner[row].all()) == flagged, (d, sign)
+            # the other rows are at least one cell inside or outside the box: never flagged there
+            others = np.ones(X, bool)
+            others[row] = False
+            assert not inner[others].any(), (d, sign)
+            # columns 0 and Y - 1 sit exactly on the y edges: flagged wherever the source row is in the box
+            si = np.arange(X) + s
+            in_box = (si > -e) & (si < X - 1 + e)
+            assert np.array_equal(nb[:, 0], in_box) and np.array_equal(nb[:, Y - 1], in_box), (d, sign)
+    # the same along y, with the box's edges at 0 and Y - 1
+    A = np.array([[[1.0, 0.0, 0.0], [0.0, 1.0, 2.0 * (1.0 - 0.5 * e)]]])
+    nb = tp.align_prev_bev(prev, A, rng6)["near_border"][0]
+    assert nb[1:X - 1, Y - 2].all() and not nb[1:X - 1, :Y - 2].any() and not nb[1:X - 1, Y - 1].any()
+    # sources far outside the box are never flagged, however close to a grid line
+    A = np.array([[[1.0, 0.0, 2.0 * 20.0], [0.0, 1.0, 0.0]]])
+    assert not tp.align_prev_bev(prev, A, rng6)["near_border"].any()
