@@ -32,7 +32,10 @@ def _device():
     torch.cuda.init()
 
 
-def temporal_parity(ti, label, backward=True, exact=False):
+def temporal_parity(ti, label, backward=True, exact=False, on_grid_lines=False):
+    """``on_grid_lines``: a motion that maps the current grid onto the previous one (the identity, a quarter
+    turn of a square grid), so every border cell's source sits on the box's edge and the exclusion bound
+    does not apply; such cases are compared bit for bit inside the border by their test."""
     cur = ti.cur
     B, N, C, H, W = cur.F.shape
     X, Y, Z = cur.X, cur.Y, cur.Z
@@ -55,7 +58,8 @@ def temporal_parity(ti, label, backward=True, exact=False):
         f"{np.where(border_ok[:, None], diff[:, C:], 0).max(initial=0):.3e} excluded cells "
         f"{int((~cell_ok).sum())} / {int((~border_ok).sum())}")
     # the border exclusion may only drop a handful of cells: at most 4, or 0.1% of a larger grid
-    assert int((~border_ok).sum()) <= max(4, (B * X * Y) // 1000), f"{label}: {int((~border_ok).sum())} excluded"
+    if not on_grid_lines:
+        assert int((~border_ok).sum()) <= max(4, (B * X * Y) // 1000), f"{label}: {int((~border_ok).sum())} excluded"
     assert not bad_cur.any(), f"{label}: {int(bad_cur.sum())} current-frame outputs outside tolerance"
     assert not bad_prev.any(), f"{label}: {int(bad_prev.sum())} aligned outputs outside tolerance"
     if not backward:
@@ -111,10 +115,10 @@ def test_identity_and_quarter_turn_are_exact():
     centred grid is numpy's rot90."""
     sq = (-10.0, 10.0, -10.0, 10.0, -4.0, 3.0)
     ti = wl.random_temporal_case(3, 1, 6, 4, 8, 22, 20, 20, 3, 6, rng6=sq, yaw_deg=0.0, shift=(0.0, 0.0))
-    out = temporal_parity(ti, "identity", backward=False)
+    out = temporal_parity(ti, "identity", backward=False, on_grid_lines=True)
     assert np.array_equal(out.cpu().numpy()[:, 4:, 1:-1, 1:-1], ti.prev[:, :, 1:-1, 1:-1])
     ti = wl.random_temporal_case(4, 1, 6, 4, 8, 22, 20, 20, 3, 6, rng6=sq, yaw_deg=90.0, shift=(0.0, 0.0))
-    out = temporal_parity(ti, "quarter turn", backward=False)
+    out = temporal_parity(ti, "quarter turn", backward=False, on_grid_lines=True)
     rot = np.rot90(ti.prev, k=-1, axes=(2, 3))
     assert np.abs(out.cpu().numpy()[:, 4:, 1:-1, 1:-1] - rot[:, :, 1:-1, 1:-1]).max() <= 1e-6
 
