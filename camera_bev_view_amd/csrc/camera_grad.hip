@@ -32,10 +32,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "wave_ops.h"
 
 namespace fbev {
+
+// Device scratch of the allocation-free variant (fbev_backward_cameras_noalloc): the partial dL/dP
+// slices of the main kernel.  Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kCameraScratchBytes];
+
 namespace {
 
 constexpr int kWave = 64;
@@ -343,6 +352,30 @@ size_t camera_grad_workspace_bytes(const Problem& p) {
   int tiles_y, groups, units;
   unit_counts(p, tiles_y, groups, units);
   return work_bytes(p, workgroups_per_sample(p, units));
+}
+
+hipError_t camera_scratch(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[device] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_camera_backward(const Problem& p, const float* grad_out, float* gK, float* gR, float* gt,

@@ -15,6 +15,8 @@
 #include "lift_splat.h"
 #include "deform_agg.h"
 
+static_assert(fbev::kCameraScratchBytes == FBEV_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -254,7 +256,7 @@ fbev_status cameras_workspace_impl(fbev_feat_desc fd, int32_t X, int32_t Y, int3
 fbev_status backward_cameras_impl(const float* grad_out, const float* features, fbev_feat_desc fd, const float* K,
                                   const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
                                   int32_t Z, float* grad_K, float* grad_R, float* grad_t, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  size_t workspace_bytes, void* stream, bool use_scratch = false) {
   fbev::Problem p{};
   fbev_status s = check_cameras(fd, X, Y, Z, p);
   if (s != FBEV_OK) return s;
@@ -271,6 +273,22 @@ fbev_status backward_cameras_impl(const float* grad_out, const float* features, 
   const uintptr_t addr = reinterpret_cast<uintptr_t>(features);
   if (n_feat > 0 && (addr & 3) != 0) return fail(FBEV_ERR_UNSUPPORTED, "features must be 4-byte aligned");
   const size_t need = fbev::camera_grad_workspace_bytes(p);
+  if (use_scratch) {
+    if (need > fbev::kCameraScratchBytes)
+      return fail(FBEV_ERR_UNSUPPORTED, "needs %zu bytes of scratch, the allocation-free variant holds %zu", need,
+                  fbev::kCameraScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      // the device the work is enqueued on: the stream's (the current device for the null stream)
+      int dev = -1;
+      hipError_t e = (stream != nullptr) ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                         : hipGetDevice(&dev);
+      if (e == hipSuccess) e = fbev::camera_scratch(dev, &workspace);
+      if (e != hipSuccess) return device_status(e, "fbev_backward_cameras_noalloc scratch lookup");
+      workspace_bytes = fbev::kCameraScratchBytes;
+    }
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(FBEV_ERR_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 need);
@@ -547,6 +565,14 @@ fbev_status fbev_backward_cameras(const float* grad_out, const float* features, 
                                   size_t workspace_bytes, void* stream) {
   return backward_cameras_impl(grad_out, features, fd, K, R, t, bev_range, X, Y, Z, grad_K, grad_R, grad_t, workspace,
                                workspace_bytes, stream);
+}
+
+fbev_status fbev_backward_cameras_noalloc(const float* grad_out, const float* features, fbev_feat_desc fd,
+                                          const float* K, const float* R, const float* t, fbev_range bev_range,
+                                          int32_t X, int32_t Y, int32_t Z, float* grad_K, float* grad_R,
+                                          float* grad_t, void* stream) {
+  return backward_cameras_impl(grad_out, features, fd, K, R, t, bev_range, X, Y, Z, grad_K, grad_R, grad_t, nullptr, 0,
+                               stream, true);
 }
 
 fbev_status fbev_backward_levels(const float* grad_out, fbev_feat_desc fd, int32_t L, const int32_t* ratios,

@@ -36,6 +36,10 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
 size_t camera_grad_workspace_bytes(const Problem& p);
 hipError_t launch_camera_backward(const Problem& p, const float* grad_out, float* gK, float* gR, float* gt, void* work,
                                   hipStream_t stream);
+// The allocation-free variant's device scratch: kCameraScratchBytes on every GPU, its device address for
+// `device` looked up once (hipGetSymbolAddress with that device current) and kept for later calls.
+constexpr size_t kCameraScratchBytes = (size_t)4 << 20;
+hipError_t camera_scratch(int device, void** ptr);
 
 // Temporal fusion: the previous BEV map prev [B, Cp, X, Y] resampled at the
 // current cells mapped by the planar motion ego [B, 2, 3] (current ego x, y ->

@@ -127,6 +127,28 @@ def camera_backward(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Ten
     return gK, gR, gt
 
 
+def camera_backward_noalloc(grad_out: torch.Tensor, features: torch.Tensor, K: torch.Tensor, R: torch.Tensor,
+                            t: torch.Tensor, bev_range: Sequence[float], X: int, Y: int, Z: int,
+                            grad_K: torch.Tensor, grad_R: torch.Tensor, grad_t: torch.Tensor) -> None:
+    """fbev_backward_cameras_noalloc: camera_backward into the caller's grad_K [B,N,3,3], grad_R [B,N,3,3] and
+    grad_t [B,N,3] with the library's fixed device scratch instead of a workspace (nothing is allocated)."""
+    if features.dim() != 5 or features.dtype != torch.float32 or not features.is_cuda or not features.is_contiguous():
+        raise ValueError("features must be a contiguous float32 device tensor [B,N,H,W,C]")
+    B, N, H, W, C = features.shape
+    dev = features.device
+    if tuple(grad_out.shape) != (B, C, X, Y) or grad_out.dtype != torch.float32 or not grad_out.is_contiguous():
+        raise ValueError("grad_out must be a contiguous float32 [B,C,X,Y] tensor")
+    _check_device_tensor("grad_out", grad_out, dev)
+    _check_cams(K, R, t, B, N, dev)
+    for name, x, shape in (("grad_K", grad_K, (B, N, 3, 3)), ("grad_R", grad_R, (B, N, 3, 3)),
+                           ("grad_t", grad_t, (B, N, 3))):
+        _check_out(name, x, shape, dev)
+    lib = _lib.load()
+    _lib.check(lib.fbev_backward_cameras_noalloc(_ptr(grad_out), _ptr(features), _lib.feat_desc(B, N, C, H, W),
+                                                 _ptr(K), _ptr(R), _ptr(t), _lib.bev_range(bev_range), X, Y, Z,
+                                                 _ptr(grad_K), _ptr(grad_R), _ptr(grad_t), _stream(dev)))
+
+
 class SamplingVT(torch.autograd.Function):
     """Autograd wrapper: gradients with respect to the features and, for fp32 features, the cameras."""
 

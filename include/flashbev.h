@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FBEV_ABI_VERSION 7
+#define FBEV_ABI_VERSION 8
 #define FBEV_MAX_CAMERAS 64
 #define FBEV_MAX_GRID 65536
 #define FBEV_MAX_LEVELS 4
@@ -199,6 +199,28 @@ fbev_status fbev_backward_cameras(const float* grad_out, const float* features, 
                                   const float* R, const float* t, fbev_range bev_range, int32_t X, int32_t Y,
                                   int32_t Z, float* grad_K, float* grad_R, float* grad_t, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * fbev_backward_cameras without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * fbev_backward_cameras minus the workspace; this call allocates nothing.
+ *
+ * The partial sums live in a fixed device scratch of FBEV_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) that the library holds on every GPU it runs on until the process
+ * ends; its address is looked up on the first call on each device.  Problems
+ * that need more than that (what fbev_backward_cameras_workspace reports: at
+ * most N * 172032 bytes for B <= 27, so up to 24 cameras always fit there)
+ * return FBEV_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU shares that GPU's scratch, and each
+ * call overwrites all of it that it reads: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be serialized
+ * by the caller.  The scratch needs no clearing between calls.
+ */
+#define FBEV_NOALLOC_SCRATCH_BYTES (4 << 20)
+fbev_status fbev_backward_cameras_noalloc(const float* grad_out, const float* features, fbev_feat_desc fd,
+                                          const float* K, const float* R, const float* t, fbev_range bev_range,
+                                          int32_t X, int32_t Y, int32_t Z, float* grad_K, float* grad_R,
+                                          float* grad_t, void* stream);
 
 /*
  * Multi-level (feature-pyramid) variants.  The pages name a multi-scale fused

@@ -149,6 +149,14 @@ int main() {
   expect_rejected(cg(P, bytes - 1), l, FBEV_ERR_INVALID_ARGUMENT);
   expect_rejected(cg(nullptr, bytes), l, FBEV_ERR_INVALID_ARGUMENT);
 
+  // the allocation-free variant: no workspace argument; an oversize problem is refused before any launch
+  EXPECT(run([&] { return fbev_backward_cameras_noalloc(FP, FP, fd, FP, FP, FP, RNG, 200, 200, 8, FP, FP, FP,
+                                                        nullptr); }, &l) == FBEV_OK && l);
+  expect_rejected(run([&] { return fbev_backward_cameras_noalloc(FP, FP, {1, 30, 4, 8, 22}, FP, FP, FP, RNG, 200, 200,
+                                                                 8, FP, FP, FP, nullptr); }, &l),
+                  l, FBEV_ERR_UNSUPPORTED);
+  EXPECT(std::strstr(fbev_last_error(), "allocation-free variant holds") != nullptr);
+
   // ---- Lift-Splat
   auto lf = [&](int D, float dmin, float dstep, int X) {
     return run([&] { return fbev_lss_forward(FP, FP, fd, D, dmin, dstep, FP, FP, FP, RNG, X, 200, FP, nullptr); },

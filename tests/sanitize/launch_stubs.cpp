@@ -15,6 +15,14 @@ hipError_t stub_status = hipSuccess;
 extern "C" const char* hipGetErrorString(hipError_t e) {
   return e == hipSuccess ? "no error" : "stub launch failure";
 }
+extern "C" hipError_t hipGetDevice(int* d) {
+  *d = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* d) {
+  *d = 0;
+  return hipSuccess;
+}
 
 namespace fbev {
 namespace {
@@ -34,9 +42,16 @@ hipError_t launch_backward_temporal(const Problem&, const float*, float*, int, c
                                     hipStream_t) {
   return reached();
 }
-size_t camera_grad_workspace_bytes(const Problem& p) { return (size_t)96 * (size_t)(p.N > 0 ? p.N : 1); }
+// the real size for one batch sample and a grid of at least 1792 units: 12 fp64 partial sums per camera and
+// workgroup, 1792 workgroups
+size_t camera_grad_workspace_bytes(const Problem& p) { return (size_t)8 * 12 * 1792 * (size_t)(p.N > 0 ? p.N : 1); }
 hipError_t launch_camera_backward(const Problem&, const float*, float*, float*, float*, void*, hipStream_t) {
   return reached();
+}
+hipError_t camera_scratch(int device, void** ptr) {
+  if (device != 0) return hipErrorInvalidDevice;
+  *ptr = reinterpret_cast<void*>(0x20000);
+  return hipSuccess;
 }
 hipError_t launch_lss_forward(LssArgs, hipStream_t) { return reached(); }
 hipError_t launch_lss_backward(LssArgs, hipStream_t) { return reached(); }
