@@ -29,6 +29,12 @@ struct Problem {
 };
 
 hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream);
+// The single-level forward over bin runs (sampling_vt_runs.hip): p.L == 1.
+hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hipStream_t stream);
+// The single-level backward over bin runs with a per-block counting sort (sampling_vt_runs.hip), onto a
+// zero-filled dL/dF; for maps of at most 256 x 256 pixels.
+bool backward_runs_supported(const Problem& p);
+hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream);
 hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream);
 
 // Camera gradients (single level, fp32 features): dL/dK, dL/dR [B,N,3,3] and

@@ -1149,6 +1149,7 @@ hipError_t forward_groups(const Problem& p, float* out, uint8_t* counts, const A
 }  // namespace
 
 hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
+  if (p.L == 1) return launch_forward_runs(p, out, counts, stream);
   return forward_groups(p, out, counts, nullptr, nullptr, stream);
 }
 
@@ -1208,6 +1209,7 @@ hipError_t launch_backward(const Problem& p, const float* grad_out, float* grad_
   long long tiles = 0;
   const BwdArgs a = bwd_args(p, grad_out, grad_feat, tiles);
   if (tiles == 0 || p.Z == 0 || p.C == 0) return hipSuccess;
+  if (backward_runs_supported(p)) return launch_backward_runs(p, grad_out, grad_feat, stream);
   const int groups = (p.C + kBwdCg - 1) / kBwdCg;
   const size_t shmem = bwd_shmem(p);
   if (p.L == 1) {

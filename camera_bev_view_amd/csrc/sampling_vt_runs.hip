@@ -1,0 +1,1057 @@
+// Single-level fused Sampling-VT forward and backward for gfx950, organised around bin runs.
+//
+// The operator is the dense Sampling-VT of the FlashBEV reading notes ("Core
+// Idea"; "Method" items 1-4): per BEV cell, project every height bin's voxel
+// centre through every camera, keep the in-view samples, bilinearly sample,
+// average over the valid cameras per bin and sum over the bins; nothing per
+// (camera, bin, channel) is written to device memory.
+//
+// Bin runs.  For a fixed cell (x, y) and camera n, the homogeneous image
+// coordinates h = P [x, y, z_k, 1] (P = K [R | t]) are affine in the bin index
+// k, and each of the five in-view conditions of the SparseDriveV2 notes'
+// projection rule ("Deformable Aggregation" step 2: depth h_3 > 0, and
+// 0 <= u <= W-1, 0 <= v <= H-1 written as h_1 >= 0, (W-1) h_3 - h_1 >= 0,
+// h_2 >= 0, (H-1) h_3 - h_2 >= 0) is a half-line in k.  So the bins camera n
+// sees from a cell form one interval [lo, hi]: a "run".  The runs come from
+// five fp64 multiplications per (cell, camera) by per-camera reciprocals, and
+// the valid-camera count of bin k is the number of the cell's runs holding k.
+// (This decides validity as the per-bin sign tests do except where a test's
+// value is within rounding of zero, i.e. for a sample within ~1e-12 px of an
+// image edge.)
+//
+// Per wave: eight consecutive cells of one x-row.  Phase A: lane = (cell,
+// camera), the run, and an exclusive prefix of the run lengths, so the wave's
+// samples have indices 0 .. T-1 in (cell, camera, bin) order.  Then rounds of
+// 64 samples: phase B, lane = sample: its count, the exact projection (fp64
+// reciprocal, two Newton steps), floor and fractions, the four taps with
+// weights / count; pixel rows shared by consecutive bins of one run are merged
+// (along a cell's vertical line the projected row is monotone, so a shared row
+// is a run of consecutive samples; the first keeps it and takes the others'
+// weights) and the kept taps compacted.  Phase C, the gather: lanes = (slot,
+// chunk), a tap's channel group read as one coalesced channels-last row per
+// 16-lane (or L-lane) slot, fp32 accumulation, and at a cell's last tap the
+// slots are summed with lane swaps into the workgroup's output tile in LDS.
+// The tile (32 cells of one x-row) leaves as full 128-byte lines of the
+// [B, C, X, Y] output.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "wave_ops.h"
+
+namespace fbev {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kBlock = kWave * kWaves;
+constexpr int kTileY = 32;               // cells per tile along y: one 128-byte output line per (channel, x-row)
+constexpr int kCpw = kTileY / kWaves;    // cells per wave
+constexpr int kOutLd = kCpw + 1;         // padded LDS row of a wave's output tile (one channel, its cells)
+constexpr int kRound = kWave;            // samples per round, one per lane
+constexpr int kOutOfRange = 0x7ffffff0;  // buffer offset the range check turns into a zero load
+
+// Per camera, in LDS: P = K [R | t] (row-major 3 x 4), and for the five in-view
+// conditions f_i(k) = alpha_i + beta_i k (alpha from the cell, beta per
+// camera): beta_i and 1 / beta_i (0 when beta_i == 0).
+struct CamRec {
+  double P[12];
+  double beta[5];
+  double inv[5];
+};
+
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
+}
+
+// Camera table, staged by the whole workgroup: entry e = 12 n + 4 r + c of P = K [R | t] per thread (fp64
+// from the fp32 inputs), then per camera the per-bin steps of the five condition forms (dz = bin height)
+// and their reciprocals.  Ends with the workgroup barrier.
+__device__ void stage_cameras(CamRec* cams, const Problem& p, int b) {
+  for (int e = threadIdx.x; e < p.N * 12; e += blockDim.x) {
+    const int n = e / 12, rc = e - n * 12, r = rc >> 2, col = rc & 3;
+    const size_t bn = (size_t)b * p.N + n;
+    const float* K = p.K + bn * 9 + r * 3;
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      acc = fma((double)K[k], (double)(col < 3 ? p.R[bn * 9 + k * 3 + col] : p.t[bn * 3 + k]), acc);
+    cams[n].P[rc] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.N * 5; e += blockDim.x) {
+    const int n = e / 5, i = e - n * 5;
+    const double* P = cams[n].P;
+    const double s0 = P[2] * p.dz, s1 = P[6] * p.dz, s2 = P[10] * p.dz;
+    const double be = (i == 0) ? s2                                       // depth
+                    : (i == 1) ? s0                                       // u >= 0
+                    : (i == 2) ? fma((double)(p.W - 1), s2, -s0)          // u <= W - 1
+                    : (i == 3) ? s1                                       // v >= 0
+                               : fma((double)(p.H - 1), s2, -s1);         // v <= H - 1
+    cams[n].beta[i] = be;
+    cams[n].inv[i] = (be != 0.0) ? 1.0 / be : 0.0;
+  }
+  __syncthreads();
+}
+
+// The bins [lo, hi] of camera `c` in view from the cell at (px, py); lo > hi when none.
+__device__ __forceinline__ void bin_run(const CamRec& c, double px, double py, double z0, int Z, double Wm1,
+                                        double Hm1, int& lo_out, int& hi_out) {
+  const double h0 = fma(c.P[0], px, fma(c.P[1], py, fma(c.P[2], z0, c.P[3])));
+  const double h1 = fma(c.P[4], px, fma(c.P[5], py, fma(c.P[6], z0, c.P[7])));
+  const double h2 = fma(c.P[8], px, fma(c.P[9], py, fma(c.P[10], z0, c.P[11])));
+  double alpha[5];
+  alpha[0] = h2;
+  alpha[1] = h0;
+  alpha[2] = fma(Wm1, h2, -h0);
+  alpha[3] = h1;
+  alpha[4] = fma(Hm1, h2, -h1);
+  double lo = 0.0, hi = (double)(Z - 1);
+  bool none = false;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const double be = c.beta[i];
+    // root of alpha + beta k, clamped far outside [0, Z) before any rounding to an integer
+    const double root = fmin(fmax(-alpha[i] * c.inv[i], -2.0), (double)Z + 1.0);
+    if (be > 0.0) {
+      lo = fmax(lo, i == 0 ? floor(root) + 1.0 : ceil(root));      // depth: strictly positive
+    } else if (be < 0.0) {
+      hi = fmin(hi, i == 0 ? ceil(root) - 1.0 : floor(root));
+    } else {
+      none = none || (i == 0 ? !(alpha[i] > 0.0) : !(alpha[i] >= 0.0));
+    }
+  }
+  if (none || lo > hi) {
+    lo_out = 1;
+    hi_out = 0;
+  } else {
+    lo_out = (int)lo;
+    hi_out = (int)hi;
+  }
+}
+
+struct Rec {
+  int off;   // byte offset of the tap's pixel in the sample's features
+  float w;   // bilinear weight / valid-camera count
+};
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+
+// D consecutive dwords of one tap, accumulated into fp32 registers.
+template <int D, bool BF16>
+struct Lane {
+  static constexpr int kVec = BF16 ? 2 * D : D;
+  struct Raw {
+    uint32_t d[D];
+  };
+  __device__ static Raw load(__amdgpu_buffer_rsrc_t rs, int off) {
+    Raw r;
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= D; i += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * i, 0, 0);
+      r.d[i] = v[0];
+      r.d[i + 1] = v[1];
+      r.d[i + 2] = v[2];
+      r.d[i + 3] = v[3];
+    }
+    if constexpr (D % 4 == 2) {
+      typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4 * i, 0, 0);
+      r.d[i] = v[0];
+      r.d[i + 1] = v[1];
+      i += 2;
+    }
+#pragma unroll
+    for (; i < D; ++i) r.d[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * i, 0, 0);
+    return r;
+  }
+  __device__ static void fma_into(float* acc, const Raw& v, float w) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if constexpr (BF16) {
+        acc[2 * i] = fmaf(w, __uint_as_float(v.d[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(v.d[i] & 0xffff0000u), acc[2 * i + 1]);
+      } else {
+        acc[i] = fmaf(w, __uint_as_float(v.d[i]), acc[i]);
+      }
+    }
+  }
+};
+
+struct RunArgs {
+  Problem p;
+  float* out;
+  uint8_t* counts;
+  int c_lo;          // first channel of this launch's group
+  int Cg;            // channels of the group
+  int tiles_y;       // ceil(Y / kTileY)
+  int write_counts;
+};
+
+// Sample descriptor: bin k (16 bits), camera n (6 bits), cell of the wave (up to 6 bits).
+__device__ __forceinline__ int desc_pack(int k, int n, int cl) { return k | (n << 16) | (cl << 22); }
+
+// The cells a wave works on: cell cl (0 <= cl < n) is (x0 + cl / ny, y0 + cl % ny); cells outside the grid
+// have no samples.
+struct CellSet {
+  int x0, y0, ny, n;
+  __device__ int x(int cl) const { return x0 + cl / ny; }
+  __device__ int y(int cl) const { return y0 + cl % ny; }
+};
+
+// Phase B for one sample: the four taps (byte offsets of their pixels, weights
+// / count).  u, v are clamped to the pixel-centre box before the floor so that
+// rounding at an edge never reaches outside the map; the clamped second tap at
+// the last column / row repeats the first with weight 0.
+__device__ __forceinline__ void sample_taps(const CamRec& c, double px, double py, double pz, float rc, int H, int W,
+                                            int pix_base, int pix_bytes, Rec (&t)[4], int& top, int& bot,
+                                            int& xy) {
+  const double h0 = fma(c.P[0], px, fma(c.P[1], py, fma(c.P[2], pz, c.P[3])));
+  const double h1 = fma(c.P[4], px, fma(c.P[5], py, fma(c.P[6], pz, c.P[7])));
+  const double h2 = fma(c.P[8], px, fma(c.P[9], py, fma(c.P[10], pz, c.P[11])));
+  const double r = recip(h2);
+  const double u = fmin(fmax(h0 * r, 0.0), (double)(W - 1));
+  const double v = fmin(fmax(h1 * r, 0.0), (double)(H - 1));
+  const double fu = floor(u), fv = floor(v);
+  const int x0 = (int)fu, y0 = (int)fv;
+  const float fa = (float)(u - fu), fb = (float)(v - fv);
+  const int p00 = pix_base + y0 * W + x0;
+  const int dxp = (x0 + 1 < W) ? 1 : 0;
+  const int dyp = (y0 + 1 < H) ? W : 0;
+  const float wa0 = (1.0f - fa) * rc, wa1 = fa * rc;
+  const float wb0 = 1.0f - fb, wb1 = fb;
+  t[0] = Rec{p00 * pix_bytes, wa0 * wb0};
+  t[1] = Rec{(p00 + dxp) * pix_bytes, wa1 * wb0};
+  t[2] = Rec{(p00 + dyp) * pix_bytes, wa0 * wb1};
+  t[3] = Rec{(p00 + dyp + dxp) * pix_bytes, wa1 * wb1};
+  top = p00;
+  bot = dyp ? p00 + dyp : -1;      // no bottom row at the last image row (its weights are 0)
+  xy = x0 | (y0 << 16);
+}
+
+// Phase A for the wave's cells: the run [lo, hi] of every (cell, camera) pair (cell-major, lo | hi << 16)
+// and the index of its first sample (sStart[npair] = the total); returns the wave's sample total.
+__device__ int wave_runs(const CamRec* sCam, const Problem& p, const CellSet& cs, int* sRun, int* sStart,
+                         int lane) {
+  const int N = p.N, npair = cs.n * N;
+  const double z0 = p.oz + 0.5 * p.dz;
+  const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
+  int total = 0;
+  for (int pb = 0; pb < npair; pb += kWave) {
+    const int pi = pb + lane;
+    const int cl = pi / (N > 0 ? N : 1), n = pi - cl * N;
+    int lo = 1, hi = 0;
+    if (pi < npair && cs.x(cl) < p.X && cs.y(cl) < p.Y) {
+      const double px = p.ox + ((double)cs.x(cl) + 0.5) * p.dx;
+      const double py = p.oy + ((double)cs.y(cl) + 0.5) * p.dy;
+      bin_run(sCam[n], px, py, z0, p.Z, Wm1, Hm1, lo, hi);
+    }
+    const int len = max(hi - lo + 1, 0);
+    const int incl = wave_scan_incl(len);
+    if (pi < npair) {
+      sRun[pi] = lo | (hi << 16);
+      sStart[pi] = total + incl - len;
+    }
+    total += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  if (lane == 0) sStart[npair] = total;
+  wave_lds_sync();
+  return total;
+}
+
+// The descriptors of samples [r0, r0 + 64) of the wave: each run lane writes its bins in that range.
+__device__ void emit_round(const int* sRun, const int* sStart, int npair, int N, int r0, int* sDesc, int lane) {
+  for (int pb = 0; pb < npair; pb += kWave) {
+    const int pi = pb + lane;
+    if (pi < npair) {
+      const int s0 = sStart[pi], s1 = sStart[pi + 1];
+      const int lo = sRun[pi] & 0xffff;
+      const int cl = pi / (N > 0 ? N : 1), n = pi - cl * N;
+      const int j0 = max(s0, r0), j1 = min(s1, r0 + kRound);
+      for (int j = j0; j < j1; ++j) sDesc[j - r0] = desc_pack(lo + (j - s0), n, cl);
+    }
+  }
+}
+
+// Phase B and the row merging for the round's samples (lane = sample, nsmp of them): the sample's four taps
+// (Rec offsets = pixel index * pix_bytes) with weights / count, then rows shared with the neighbouring samples
+// of the same run (same cell and camera, consecutive bins) merged: a row is kept by the first sample of the
+// run that has it, which adds the weights of the following samples for as long as each of them has the row.
+// On return tp holds the lane's (merged) taps, keep_top / keep_bot say which rows it keeps; sTap has been
+// read by every lane (the caller may overwrite it after a wave sync).
+struct Sample {
+  int cl, n, xy;              // cell of the wave, camera, top-left tap pixel (x | y << 16)
+  bool keep_top, keep_bot;
+  Rec tp[4];
+};
+
+__device__ Sample round_samples(const CamRec* sCam, const Problem& p, const CellSet& cs, const int* sRun,
+                                const int* sDesc, Rec* sTap, int nsmp, int pix_bytes, int lane) {
+  const int N = p.N;
+  Sample sm;
+  sm.cl = -1;
+  sm.n = 0;
+  sm.xy = 0;
+  int dsc = 0, top = -1, bot = -1;
+  if (lane < nsmp) {
+    dsc = sDesc[lane];
+    const int k = dsc & 0xffff, n = (dsc >> 16) & 63, cl = dsc >> 22;
+    int cnt = 0;
+    for (int m = 0; m < N; ++m) {
+      const int r = sRun[cl * N + m];
+      cnt += ((r & 0xffff) <= k && k <= (r >> 16)) ? 1 : 0;
+    }
+    const double px = p.ox + ((double)cs.x(cl) + 0.5) * p.dx;
+    const double py = p.oy + ((double)cs.y(cl) + 0.5) * p.dy;
+    const double pz = p.oz + ((double)k + 0.5) * p.dz;
+    sample_taps(sCam[n], px, py, pz, __builtin_amdgcn_rcpf((float)cnt), p.H, p.W, n * p.P, pix_bytes, sm.tp, top,
+                bot, sm.xy);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sTap[4 * lane + t] = sm.tp[t];
+    sm.cl = cl;
+    sm.n = n;
+  }
+  const int run_id = dsc >> 16;
+  const int prev_run = lane_prev(run_id, -1), prev_top = lane_prev(top, -2), prev_bot = lane_prev(bot, -2);
+  const bool same_prev = lane > 0 && lane < nsmp && prev_run == run_id;
+  bool keep_top = lane < nsmp, keep_bot = lane < nsmp && bot >= 0;
+  if (same_prev) {
+    keep_top = keep_top && top != prev_top && top != prev_bot;
+    keep_bot = keep_bot && bot != prev_top && bot != prev_bot;
+  }
+  wave_lds_sync();
+  if (keep_top || keep_bot) {
+    Rec* tp = sm.tp;
+    int ltop = keep_top ? lane + 1 : nsmp, lbot = keep_bot ? lane + 1 : nsmp;
+    for (int j = lane + 1; j < nsmp; ++j) {
+      const int dj = sDesc[j];
+      if ((dj >> 16) != run_id) break;
+      const Rec j0 = sTap[4 * j], j2 = sTap[4 * j + 2];
+      const int jt = j0.off, jb = (j2.off != j0.off) ? j2.off : -1;
+      const bool more_t = ltop == j && (jt == tp[0].off || jb == tp[0].off);
+      const bool more_b = lbot == j && (jt == tp[2].off || jb == tp[2].off);
+      if (more_t) {
+        const bool from_top = jt == tp[0].off;
+        tp[0].w += from_top ? j0.w : j2.w;
+        tp[1].w += from_top ? sTap[4 * j + 1].w : sTap[4 * j + 3].w;
+        ltop = j + 1;
+      }
+      if (more_b) {
+        const bool from_top = jt == tp[2].off;
+        tp[2].w += from_top ? j0.w : j2.w;
+        tp[3].w += from_top ? sTap[4 * j + 1].w : sTap[4 * j + 3].w;
+        lbot = j + 1;
+      }
+      if (!more_t && !more_b) break;
+    }
+  }
+  sm.keep_top = keep_top;
+  sm.keep_bot = keep_bot;
+  return sm;
+}
+
+// Tap slots of one round: four per sample.
+__host__ __device__ constexpr int tap_slots(int) { return 4 * kRound; }
+
+// LDS of one wave (16-byte multiple) and of the output tile.
+__host__ __device__ inline size_t wave_lds_bytes(int N, int S) {
+  const size_t npair = (size_t)kCpw * N;
+  const size_t b = sizeof(Rec) * tap_slots(S) + sizeof(int) * (kRound + 2 * kCpw + 2 * npair + 1);
+  return (b + 15) & ~(size_t)15;
+}
+
+// U whole gather steps: the lane's tap of step u is rec[u S] (a record per slot); all U loads are issued
+// before the first is used.
+template <int U, int S, class Ln>
+__device__ __forceinline__ void gather_steps(float* acc, const Rec* rec, __amdgpu_buffer_rsrc_t rs, int lane_off) {
+  typename Ln::Raw v[U];
+  float w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const Rec rr = rec[u * S];
+    w[u] = rr.w;
+    v[u] = Ln::load(rs, rr.off + lane_off);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) Ln::fma_into(acc, v[u], w[u]);
+}
+
+// A cell's accumulators, complete: sum the S slots and park the channels in column `ct` of the output tile;
+// the accumulators are cleared for the next cell.
+template <int L, int kVec>
+__device__ __forceinline__ void flush_cell(float (&acc)[kVec], float* sOut, int ct, int lane, int Cg) {
+  const int slot = lane / L, q = lane - slot * L;
+  if constexpr (L == 16 && kVec % 4 == 0) {
+    // reduce-scatter over the four slots: lane (row r, chunk q) ends with channel q kVec + 4 i + perm[r]
+    const int rrow = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < kVec; i += 4) {
+      const float e01 = swap32_add(acc[i], acc[i + 1]);
+      const float e23 = swap32_add(acc[i + 2], acc[i + 3]);
+      const float s = swap16_add(e01, e23);
+      const int ch = q * kVec + i + ((rrow & 1) ? 2 : 0) + (rrow >> 1);
+      sOut[ch * kOutLd + ct] = s;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      float s = row_sum_stride<L>(acc[i]);
+      s = swap16_add(s, s);
+      acc[i] = swap32_add(s, s);
+    }
+    if (slot == 0) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        const int ch = q * kVec + i;
+        if (ch < Cg) sOut[ch * kOutLd + ct] = acc[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
+}
+__host__ __device__ inline size_t out_tile_bytes(int Cg) {
+  return (sizeof(float) * (size_t)(Cg > 0 ? Cg : 1) * kOutLd + 15) & ~(size_t)15;
+}
+
+// Occupancy request and gather depth (loads in flight per lane), chosen so that no layout spills:
+// six waves per SIMD (80 VGPRs) up to 8 accumulated channels per lane, five (96) for 16.
+template <int D, int L, bool BF16>
+struct RunWaves {
+  static constexpr int kVec = BF16 ? 2 * D : D;
+  static constexpr int value = (kVec <= 4 || (BF16 && kVec <= 8 && L == 16)) ? 6 : (kVec <= 8 ? 5 : 4);
+  static constexpr int kLoads = (D >= 3 || (BF16 && D >= 2)) ? 4 : 8;
+};
+
+// Forward.  L lanes cover one tap's channel group with D dwords each (L * D * 4 == group bytes);
+// S = 64 / L taps per load instruction.
+template <int D, int L, bool BF16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
+void sampling_vt_runs_fwd(RunArgs a) {
+  using Ln = Lane<D, BF16>;
+  constexpr int kVec = Ln::kVec;
+  constexpr int S = kWave / L;
+  static_assert(S >= 4 && (S & 3) == 0, "lanes per tap divide the wave into at least four slots");
+  constexpr int kU = RunWaves<D, L, BF16>::kLoads;       // loads in flight per lane in the gather
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Problem& p = a.p;
+  const int N = p.N;
+  const int npair = kCpw * N;
+  CamRec* sCam = reinterpret_cast<CamRec*>(smem);
+  unsigned char* cur = smem + sizeof(CamRec) * N;
+  const int wid = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned char* wbase = cur + (wave_lds_bytes(N, S) + out_tile_bytes(a.Cg)) * wid;
+  float* sOut = reinterpret_cast<float*>(wbase + wave_lds_bytes(N, S));   // [Cg][kOutLd] this wave's cells
+  Rec* sTap = reinterpret_cast<Rec*>(wbase);                        // [tap_slots(S)] raw, then kept taps by step
+  int* sDesc = reinterpret_cast<int*>(sTap + tap_slots(S));         // [kRound] the round's samples
+  int* sCellLo = sDesc + kRound;                                    // [kCpw] first kept tap of the cell in the round
+  int* sCellHi = sCellLo + kCpw;                                    // [kCpw] end | complete << 30, or -1
+  int* sRun = sCellHi + kCpw;                                       // [npair] lo | hi << 16
+  int* sStart = sRun + npair;                                       // [npair + 1] first sample index of each run
+
+  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int yt = tile % a.tiles_y;
+  const int bx = tile / a.tiles_y;
+  const int x = bx % p.X;
+  const int b = bx / p.X;
+  const int y_tile = yt * kTileY;
+  const int y_wave = y_tile + wid * kCpw;
+
+  stage_cameras(sCam, p, b);
+
+  for (int e = lane; e < a.Cg * kOutLd; e += kWave) sOut[e] = 0.f;     // cells with no sample stay 0
+  const int ncell = min(kCpw, p.Y - y_wave);          // cells of this wave (may be <= 0)
+  const CellSet cs{x, y_wave, kCpw, kCpw};
+
+  // ---- phase A: runs of (cell, camera) pairs, cell-major, and their first sample indices
+  const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
+
+  // optional per-bin valid-camera counts (validation output)
+  if (a.write_counts) {
+    for (int e = lane; e < ncell * p.Z; e += kWave) {
+      const int cl = e / p.Z, k = e - cl * p.Z;
+      int cnt = 0;
+      for (int n = 0; n < N; ++n) {
+        const int r = sRun[cl * N + n];
+        cnt += ((r & 0xffff) <= k && k <= (r >> 16)) ? 1 : 0;
+      }
+      a.counts[(((size_t)b * p.X + x) * p.Y + y_wave + cl) * p.Z + k] = (uint8_t)cnt;
+    }
+  }
+
+  // gather lane roles
+  const int slot = lane / L;
+  const int q = lane - slot * L;
+  const int lane_off = a.c_lo * p.elem_bytes + q * 4 * D;
+  const size_t batch_bytes = (size_t)N * p.P * p.C * p.elem_bytes;
+  const unsigned char* fbase = reinterpret_cast<const unsigned char*>(p.feat) + (size_t)b * batch_bytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(fbase), 0, (int)batch_bytes, 0x00020000);
+  const int pix_bytes = p.C * p.elem_bytes;
+  float acc[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
+
+  for (int r0 = 0; r0 < total; r0 += kRound) {
+    const int nsmp = min(kRound, total - r0);
+    emit_round(sRun, sStart, npair, N, r0, sDesc, lane);
+    if (lane < kCpw) sCellHi[lane] = -1;
+    wave_lds_sync();
+    // ---- phase B: lane = sample; taps, count, row merging
+    const Sample sm = round_samples(sCam, p, cs, sRun, sDesc, sTap, nsmp, pix_bytes, lane);
+    const bool keep_top = sm.keep_top, keep_bot = sm.keep_bot;
+    const int cl = sm.cl;
+    const Rec* tp = sm.tp;
+    const uint64_t mt = __ballot(keep_top), mb = __ballot(keep_bot);
+    const int pos = 2 * (rank_below(mt) + rank_below(mb));
+    const int nkept = 2 * ((keep_top ? 1 : 0) + (keep_bot ? 1 : 0));
+    // per cell: its kept taps in this round, and whether its last sample is in this round
+    const int next_cl = lane_next(cl, -1), prev_cl = lane_prev(cl, -1);   // every lane takes part
+    const bool cell_first = lane < nsmp && (lane == 0 || prev_cl != cl);
+    const bool cell_last = lane < nsmp && (lane == nsmp - 1 || next_cl != cl);
+    wave_lds_sync();                                   // every lane has read the raw taps
+    if (keep_top) {
+      sTap[pos] = tp[0];
+      sTap[pos + 1] = tp[1];
+    }
+    if (keep_bot) {
+      sTap[pos + (keep_top ? 2 : 0)] = tp[2];
+      sTap[pos + (keep_top ? 3 : 1)] = tp[3];
+    }
+    if (cell_first) sCellLo[cl] = pos;
+    if (cell_last) {
+      const bool fin = sStart[(cl + 1) * N] <= r0 + kRound;
+      sCellHi[cl] = (pos + nkept) | (fin ? (1 << 30) : 0);
+    }
+    wave_lds_sync();
+    // ---- phase C: gather, cell by cell; a step takes S consecutive kept taps, kU steps in flight
+    const int cl_first = __builtin_amdgcn_readfirstlane(cl), cl_last = __builtin_amdgcn_readlane(cl, nsmp - 1);
+    for (int c = cl_first; c <= cl_last; ++c) {
+      const int hi_raw = uniform(sCellHi[c]);
+      if (hi_raw < 0) continue;
+      const int t1 = hi_raw & ((1 << 30) - 1);
+      int t = uniform(sCellLo[c]);
+      // whole steps in groups of kU, then of 2 and 1, with no masking; one masked step for the rest
+      for (; t + kU * S <= t1; t += kU * S) gather_steps<kU, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+      if (kU > 2 && t + 2 * S <= t1) {
+        gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+        t += 2 * S;
+      }
+      if (t + S <= t1) {
+        gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+        t += S;
+      }
+      if (t < t1) {
+        const bool in = t + slot < t1;
+        const Rec rr = sTap[t + slot];
+        Ln::fma_into(acc, Ln::load(rs, in ? rr.off + lane_off : kOutOfRange), in ? rr.w : 0.f);
+      }
+      if (hi_raw >> 30) flush_cell<L, kVec>(acc, sOut, c, lane, a.Cg);
+    }
+    wave_lds_sync();
+  }
+  wave_lds_sync();
+
+  // ---- write-out of this wave's cells: per channel, ncell consecutive y of one x-row (the four waves of
+  // the workgroup write the four quarters of each 128-byte line from one CU, so they meet in its L2)
+  if (ncell > 0) {
+    const size_t c_stride = (size_t)p.X * p.Y;
+    float* ob = a.out + (((size_t)b * p.out_ch + a.c_lo) * p.X + x) * p.Y + y_wave;
+    const bool vec = ncell == kCpw && (((uintptr_t)ob | (size_t)p.Y * 4) & 15) == 0;
+    for (int e = lane; e < a.Cg * 2; e += kWave) {
+      const int ch = e >> 1, h = (e & 1) * 4;
+      const float* src = sOut + ch * kOutLd + h;
+      float* dst = ob + ch * c_stride + h;
+      if (vec) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 v4 = {src[0], src[1], src[2], src[3]};
+        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(dst));
+      } else {
+        for (int k = 0; k < 4 && h + k < ncell; ++k) __builtin_nontemporal_store(src[k], dst + k);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Backward (gradient with respect to the features; the map is linear in them).  One workgroup = an
+// 8 x 8 block of cells and a group of up to 64 channels, eight waves, one x-row of 8 cells each.  The
+// waves list their samples exactly as the forward does (runs, taps, merged rows), and every kept tap
+// becomes an entry (pixel, cell, weight) of the workgroup.  A counting sort by pixel in LDS then makes
+// every pixel's entries contiguous: the keys are a window per camera (the bounding box of the pixels
+// that camera's taps reach), counts by integer LDS atomics, a block scan, and a scatter by atomic
+// cursors.  The pixels are shared among the waves by entry count; the four 16-lane groups of a wave
+// split one pixel's entries, grad(cell) * weight with the grad rows read from the block's
+// upstream-gradient tile in LDS (4 channels per lane), a reduce-scatter over the groups gives lane l
+// channel l, and each pixel leaves the workgroup as one fp32 global atomic over its consecutive
+// channels.  LDS float atomics are avoided: on this chip they are far slower than the integer ones.
+
+constexpr int kBWaves = 8;
+constexpr int kBThreads = kBWaves * kWave;
+constexpr int kBTileX = kBWaves;           // tile rows along x, one per wave
+constexpr int kBTileY = 8;                 // cells per row
+constexpr int kBCells = kBTileX * kBTileY;
+constexpr int kBCpw = kBTileY;             // cells per wave
+constexpr int kBCg = 64;                   // channels per workgroup: 16 lanes x 4 per pixel
+constexpr int kBgLd = kBCg + 4;            // upstream-gradient tile row (one cell's channels), 16-byte aligned
+constexpr int kBRedG = 4;                  // entries per lane group and reduction step
+
+struct BwdRunArgs {
+  Problem p;
+  const float* grad;     // [B, out_ch, X, Y]
+  float* dF;             // [B, N, P, C], zero-filled; atomically accumulated
+  int c_lo, Cg;          // channel group
+  int tiles_x, tiles_y;
+  int max_ent;           // entries held before a flush
+  int max_keys;          // window counters per counting pass
+};
+
+// Entry: pixel x (8 bits), row y (8 bits), camera n (6 bits), cell of the block (6 bits); and the weight.
+__device__ __forceinline__ int ent_pack(int x, int y, int n, int cell) { return x | (y << 8) | (n << 16) | (cell << 22); }
+
+// LDS carve-up of the backward (host and device agree on it).
+struct BwdLds {
+  size_t cam, g, box, win, misc, cnt, ent, sort, runs, total;
+};
+__host__ __device__ inline size_t bwd_round_bytes() {
+  return (sizeof(Rec) * 4 * kRound + sizeof(int) * kRound + 15) & ~(size_t)15;
+}
+__host__ __device__ inline BwdLds bwd_lds(int N, int max_ent, int max_keys) {
+  BwdLds l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += (bytes + 15) & ~(size_t)15; return at; };
+  l.cam = take(sizeof(CamRec) * N);
+  l.g = take(sizeof(float) * kBCells * kBgLd);
+  l.box = take(sizeof(int) * 4 * (N > 0 ? N : 1));
+  l.win = take(sizeof(int) * 4 * (N > 0 ? N : 1));
+  l.misc = take(sizeof(int) * 32);
+  l.cnt = take(sizeof(int) * (max_keys + 1));
+  l.ent = take(sizeof(int2) * max_ent);
+  // the sorted entries share their space with the waves' per-round buffers (never live at the same time)
+  const size_t sort_bytes = sizeof(int2) * max_ent, rounds = bwd_round_bytes() * kBWaves;
+  l.sort = take(sort_bytes > rounds ? sort_bytes : rounds);
+  l.runs = take(sizeof(int) * (2 * (size_t)kBCpw * N + 1) * kBWaves);
+  l.total = o;
+  return l;
+}
+
+// Minimum and maximum over the lanes of the wave (every lane gets them).
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, dpp_or<kQuadSwap1>(v, v));
+  v = min(v, dpp_or<kQuadSwap2>(v, v));
+  v = min(v, dpp_or<kHalfMirror>(v, v));
+  v = min(v, dpp_or<kRowMirror>(v, v));
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = min((int)r[0], (int)r[1]);
+  auto r2 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return min((int)r2[0], (int)r2[1]);
+}
+__device__ __forceinline__ int wave_max(int v) { return -wave_min(-v); }
+
+// Sort the block's entries by pixel and add each pixel's sums to dF (one counting pass per window of
+// max_keys keys).  Called by the whole workgroup; ends with the entries and camera boxes cleared.
+__device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds& lay, int b) {
+  const Problem& p = a.p;
+  const int N = p.N;
+  const float* sG = reinterpret_cast<const float*>(smem + lay.g);
+  int* sBox = reinterpret_cast<int*>(smem + lay.box);
+  int* sWin = reinterpret_cast<int*>(smem + lay.win);
+  int* sMisc = reinterpret_cast<int*>(smem + lay.misc);
+  int* sCnt = reinterpret_cast<int*>(smem + lay.cnt);
+  const int2* sEnt = reinterpret_cast<const int2*>(smem + lay.ent);
+  int2* sSort = reinterpret_cast<int2*>(smem + lay.sort);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  if (threadIdx.x == 0) {
+    int base = 0;
+    for (int n = 0; n < N; ++n) {
+      const int x_lo = sBox[4 * n], x_hi = sBox[4 * n + 1], y_lo = sBox[4 * n + 2], y_hi = sBox[4 * n + 3];
+      const bool used = x_lo <= x_hi;
+      sWin[4 * n] = base;
+      sWin[4 * n + 1] = x_lo;
+      sWin[4 * n + 2] = y_lo;
+      sWin[4 * n + 3] = used ? x_hi - x_lo + 1 : 0;
+      if (used) base += (x_hi - x_lo + 1) * (y_hi - y_lo + 1);
+    }
+    sMisc[1] = base;
+  }
+  __syncthreads();
+  const int nkeys = sMisc[1], nent = sMisc[0];
+  const size_t batch_elems = (size_t)N * p.P * p.C;
+  float* db = a.dF + (size_t)b * batch_elems + a.c_lo;
+  for (int k0 = 0; k0 < nkeys; k0 += a.max_keys) {
+    const int kn = min(a.max_keys, nkeys - k0);
+    for (int k = threadIdx.x; k <= kn; k += kBThreads) sCnt[k] = 0;
+    __syncthreads();
+    // counts per key of this pass
+    for (int e = threadIdx.x; e < nent; e += kBThreads) {
+      const int v = sEnt[e].x;
+      const int x = v & 0xff, y = (v >> 8) & 0xff, n = (v >> 16) & 63;
+      const int key = sWin[4 * n] + (y - sWin[4 * n + 2]) * sWin[4 * n + 3] + (x - sWin[4 * n + 1]) - k0;
+      if (key >= 0 && key < kn) atomicAdd(&sCnt[key], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the counts (a chunk of keys per thread, then the chunk sums across the block); the
+    // reduction's share of wave w is the keys from the first one that starts at or after w/8 of the pass's
+    // entries (sMisc[24 + w]; kn where there is none)
+    {
+      const int per = (kn + kBThreads - 1) / kBThreads;
+      const int c0 = min(kn, (int)threadIdx.x * per), c1 = min(kn, c0 + per);
+      int run = 0;
+      for (int k = c0; k < c1; ++k) run += sCnt[k];
+      const int prev_cnt = (c0 > 0 && c0 < c1) ? sCnt[c0 - 1] : 0;
+      const int incl = wave_scan_incl(run);
+      if (lane == kWave - 1) sMisc[16 + wid] = incl;
+      if (threadIdx.x < kBWaves) sMisc[24 + threadIdx.x] = threadIdx.x == 0 ? 0 : kn;
+      __syncthreads();
+      int base = incl - run, total = 0;
+#pragma unroll
+      for (int w = 0; w < kBWaves; ++w) {
+        const int t = sMisc[16 + w];
+        base += w < wid ? t : 0;
+        total += t;
+      }
+      int prev_start = c0 > 0 ? base - prev_cnt : -1;
+      for (int k = c0; k < c1; ++k) {
+        const int c = sCnt[k];
+        sCnt[k] = base;
+#pragma unroll
+        for (int w = 1; w < kBWaves; ++w) {
+          const int lo = (int)(((long long)total * w) / kBWaves);
+          if (prev_start < lo && base >= lo) sMisc[24 + w] = k;
+        }
+        prev_start = base;
+        base += c;
+      }
+    }
+    __syncthreads();
+    // scatter by atomic cursors: afterwards sCnt[k] is the end of key k (and the start of key k + 1)
+    for (int e = threadIdx.x; e < nent; e += kBThreads) {
+      const int2 en = sEnt[e];
+      const int x = en.x & 0xff, y = (en.x >> 8) & 0xff, n = (en.x >> 16) & 63;
+      const int key = sWin[4 * n] + (y - sWin[4 * n + 2]) * sWin[4 * n + 3] + (x - sWin[4 * n + 1]) - k0;
+      if (key >= 0 && key < kn) sSort[atomicAdd(&sCnt[key], 1)] = en;
+    }
+    __syncthreads();
+    // per-pixel sums.  Wave w takes keys [sMisc[24 + w], sMisc[25 + w]): about an eighth of the entries.
+    // The four 16-lane groups split a pixel's entries (entry i to group i mod 4), each lane holding 4
+    // channels, and a reduce-scatter over the groups leaves lane l with channel l of the pixel's sum (the
+    // tile's channel order in LDS is chosen for that), which goes to dF as one atomic over the pixel's
+    // consecutive channels.  Keys are taken 64 at a time, one per lane, so their ranges and pixels come
+    // from registers, and the next pixel's first entries are read while the current one is summed.
+    {
+      const int ka = sMisc[24 + wid], kb = wid + 1 < kBWaves ? sMisc[25 + wid] : kn;
+      const int grp = lane >> 4;
+      const float* gq = sG + 4 * (lane & 15);
+      for (int kc = ka; kc < kb; kc += kWave) {
+        const int k = kc + lane;
+        const int kend = k < kb ? sCnt[k] : 0;
+        const int kbeg = (k < kb && k > 0) ? sCnt[k - 1] : 0;
+        const bool some = kend > kbeg;
+        const int kpix = some ? sSort[kbeg].x : 0;
+        uint64_t todo = __ballot(some);
+        if (!todo) continue;
+        int i = (int)__builtin_ctzll(todo);
+        int nb = __builtin_amdgcn_readlane(kbeg, i), ne = __builtin_amdgcn_readlane(kend, i);
+        int2 en[kBRedG];
+#pragma unroll
+        for (int t = 0; t < kBRedG; ++t) en[t] = sSort[min(nb + 4 * t + grp, ne - 1)];
+        for (;;) {
+          const int beg = nb, end = ne, v = __builtin_amdgcn_readlane(kpix, i);
+          int2 e[kBRedG];
+#pragma unroll
+          for (int t = 0; t < kBRedG; ++t) e[t] = en[t];
+          todo &= todo - 1;
+          if (todo) {
+            i = (int)__builtin_ctzll(todo);
+            nb = __builtin_amdgcn_readlane(kbeg, i);
+            ne = __builtin_amdgcn_readlane(kend, i);
+#pragma unroll
+            for (int t = 0; t < kBRedG; ++t) en[t] = sSort[min(nb + 4 * t + grp, ne - 1)];
+          }
+          const int cnt = end - beg;
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int u0 = 0;;) {
+            float4 gv[kBRedG];
+#pragma unroll
+            for (int t = 0; t < kBRedG; ++t) gv[t] = *reinterpret_cast<const float4*>(gq + ((e[t].x >> 22) & 63) * kBgLd);
+#pragma unroll
+            for (int t = 0; t < kBRedG; ++t) {
+              const float w = (u0 + 4 * t + grp < cnt) ? __int_as_float(e[t].y) : 0.f;
+              acc.x = fmaf(w, gv[t].x, acc.x);
+              acc.y = fmaf(w, gv[t].y, acc.y);
+              acc.z = fmaf(w, gv[t].z, acc.z);
+              acc.w = fmaf(w, gv[t].w, acc.w);
+            }
+            u0 += 4 * kBRedG;
+            if (u0 >= cnt) break;
+#pragma unroll
+            for (int t = 0; t < kBRedG; ++t) e[t] = sSort[min(beg + u0 + 4 * t + grp, end - 1)];
+          }
+          const float sum = swap16_add(swap32_add(acc.x, acc.y), swap32_add(acc.z, acc.w));
+          const size_t pix = (size_t)((v >> 16) & 63) * p.P + (size_t)((v >> 8) & 0xff) * p.W + (v & 0xff);
+          if (lane < a.Cg) unsafeAtomicAdd(db + pix * p.C + lane, sum);
+          if (!todo) break;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // cleared for the next batch of entries
+  for (int e = threadIdx.x; e < N; e += kBThreads) {
+    sBox[4 * e] = 0x7fffffff;
+    sBox[4 * e + 1] = -1;
+    sBox[4 * e + 2] = 0x7fffffff;
+    sBox[4 * e + 3] = -1;
+  }
+  if (threadIdx.x == 0) sMisc[0] = 0;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Problem& p = a.p;
+  const int N = p.N;
+  const BwdLds lay = bwd_lds(N, a.max_ent, a.max_keys);
+  CamRec* sCam = reinterpret_cast<CamRec*>(smem + lay.cam);
+  float* sG = reinterpret_cast<float*>(smem + lay.g);
+  int* sBox = reinterpret_cast<int*>(smem + lay.box);
+  int* sMisc = reinterpret_cast<int*>(smem + lay.misc);
+  int2* sEnt = reinterpret_cast<int2*>(smem + lay.ent);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  Rec* sTap = reinterpret_cast<Rec*>(smem + lay.sort + bwd_round_bytes() * wid);
+  int* sDesc = reinterpret_cast<int*>(sTap + 4 * kRound);
+  const int npair = kBCpw * N;
+  int* sRun = reinterpret_cast<int*>(smem + lay.runs) + (2 * npair + 1) * wid;
+  int* sStart = sRun + npair;
+
+  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int yt = tile % a.tiles_y;
+  const int r1 = tile / a.tiles_y;
+  const int xt = r1 % a.tiles_x;
+  const int b = r1 / a.tiles_x;
+  const int x_tile = xt * kBTileX, y_tile = yt * kBTileY;
+
+  // upstream-gradient tile [cell][channel], loads issued before the camera table is staged
+  constexpr int kGPer = kBCells * kBCg / kBThreads;
+  float gpre[kGPer];
+  {
+    const size_t c_stride = (size_t)p.X * p.Y;
+    const float* gb = a.grad + (((size_t)b * p.out_ch + a.c_lo) * p.X) * p.Y;
+#pragma unroll
+    for (int i = 0; i < kGPer; ++i) {
+      const int e = threadIdx.x + i * kBThreads;
+      const int c = e / kBCells, cl = e - c * kBCells;
+      const int xx = x_tile + cl / kBTileY, yy = y_tile + cl % kBTileY;
+      gpre[i] = (c < a.Cg && xx < p.X && yy < p.Y) ? __builtin_nontemporal_load(gb + c * c_stride + (size_t)xx * p.Y + yy)
+                                                   : 0.f;
+    }
+  }
+  stage_cameras(sCam, p, b);
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int e = threadIdx.x + i * kBThreads;
+    const int c = e / kBCells, cl = e - c * kBCells;
+    // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3): where the per-pixel reduce-scatter
+    // leaves channel c in lane c
+    const int q = c & 15, r = c >> 4;
+    sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
+  }
+  for (int e = threadIdx.x; e < N; e += kBThreads) {
+    sBox[4 * e] = 0x7fffffff;
+    sBox[4 * e + 1] = -1;
+    sBox[4 * e + 2] = 0x7fffffff;
+    sBox[4 * e + 3] = -1;
+  }
+  if (threadIdx.x == 0) sMisc[0] = 0;
+  // this wave's cells: x-row wid of the block, 8 cells
+  const CellSet cs{x_tile + wid, y_tile, kBTileY, kBCpw};
+  const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
+  __syncthreads();
+
+  int r0 = 0;
+  for (;;) {
+    if (r0 < total) {
+      const int nsmp = min(kRound, total - r0);
+      emit_round(sRun, sStart, npair, N, r0, sDesc, lane);
+      wave_lds_sync();
+      const Sample sm = round_samples(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
+      const int x0 = sm.xy & 0xffff, y0 = sm.xy >> 16;
+      const int x1 = min(x0 + 1, p.W - 1), y1 = min(y0 + 1, p.H - 1);
+      // each camera's pixel box grows by its samples' taps: a wave reduction per camera present
+      uint64_t pend = __ballot(lane < nsmp);
+      while (pend) {
+        const int cam = __builtin_amdgcn_readlane(sm.n, (int)__builtin_ctzll(pend));
+        const bool mine = lane < nsmp && sm.n == cam;
+        pend &= ~__ballot(mine);
+        const int xa = wave_min(mine ? x0 : 0x7fffffff), xb = wave_max(mine ? x1 : -1);
+        const int ya = wave_min(mine ? y0 : 0x7fffffff), yb = wave_max(mine ? y1 : -1);
+        if (lane == 0) {
+          atomicMin(&sBox[4 * cam], xa);
+          atomicMax(&sBox[4 * cam + 1], xb);
+          atomicMin(&sBox[4 * cam + 2], ya);
+          atomicMax(&sBox[4 * cam + 3], yb);
+        }
+      }
+      const uint64_t mt = __ballot(sm.keep_top), mb = __ballot(sm.keep_bot);
+      const int nk = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sMisc[0], nk);
+      base = __builtin_amdgcn_readfirstlane(base);
+      const int pos = base + 2 * (rank_below(mt) + rank_below(mb));
+      const int cell = wid * kBCpw + sm.cl;
+      // the taps' pixels: top row (x0, y0), (x1, y0); bottom row one image row down
+      if (sm.keep_top) {
+        sEnt[pos] = make_int2(ent_pack(x0, y0, sm.n, cell), __float_as_int(sm.tp[0].w));
+        sEnt[pos + 1] = make_int2(ent_pack(x1, y0, sm.n, cell), __float_as_int(sm.tp[1].w));
+      }
+      if (sm.keep_bot) {
+        const int q = pos + (sm.keep_top ? 2 : 0);
+        sEnt[q] = make_int2(ent_pack(x0, y1, sm.n, cell), __float_as_int(sm.tp[2].w));
+        sEnt[q + 1] = make_int2(ent_pack(x1, y1, sm.n, cell), __float_as_int(sm.tp[3].w));
+      }
+      r0 += kRound;
+    }
+    // each wave's next round adds at most 4 entries per sample
+    if (lane == 0) sMisc[8 + wid] = 4 * max(min(kRound, total - r0), 0);
+    __syncthreads();
+    int next = 0;
+#pragma unroll
+    for (int w = 0; w < kBWaves; ++w) next += sMisc[8 + w];
+    const int nent = sMisc[0];
+    __syncthreads();                 // every wave has read the counts before any changes them
+    if (next == 0 || nent + next > a.max_ent) bwd_flush(a, smem, lay, b);
+    if (next == 0) break;
+  }
+}
+
+// Supported lane layouts (dwords per lane D, lanes per tap L): group bytes 4 L D.
+#define FBEV_RUN_LAYOUTS(X)                                                                             \
+  X(4, 16) X(8, 16) X(2, 16) X(1, 16) X(3, 16) X(4, 8) X(2, 8) X(1, 8) X(3, 8) X(4, 4) X(2, 4) X(1, 4)   \
+  X(3, 4) X(4, 2) X(2, 2) X(1, 2) X(3, 2) X(4, 1) X(2, 1) X(1, 1) X(3, 1)
+
+bool run_layout_supported(int D, int L) {
+#define FBEV_IS(d, l) if (D == d && L == l) return true;
+  FBEV_RUN_LAYOUTS(FBEV_IS)
+#undef FBEV_IS
+  return false;
+}
+
+template <bool BF16>
+bool dispatch_runs(int D, int L, const RunArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
+#define FBEV_CASE(d, l)                                                                                   \
+  if (D == d && L == l) {                                                                                 \
+    hipLaunchKernelGGL((sampling_vt_runs_fwd<d, l, BF16>), grid, dim3(kBlock), shmem, stream, a);         \
+    return true;                                                                                          \
+  }
+  FBEV_RUN_LAYOUTS(FBEV_CASE)
+#undef FBEV_CASE
+  return false;
+}
+
+// Lane layout for a channel group of `bytes` per pixel: the widest L (lanes per tap) that divides it into
+// a supported D (dwords per lane), trying 16-byte lanes first, then 8-byte, then 4-byte loads.  8- and
+// 16-byte loads need `vec16` (16-byte aligned features and pixel rows); without it only D = 1 or 3.
+void pick_run_layout(int bytes, bool vec16, int& D, int& L) {
+  static const int kL[] = {16, 8, 4, 2, 1};
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int l : kL) {
+      if (bytes % (4 * l) != 0) continue;
+      const int d = bytes / (4 * l);
+      const bool wide = d % 4 == 0 || d % 4 == 2;            // takes a 16- or 8-byte load
+      if (wide && !vec16) continue;
+      if ((pass == 0 && d % 4 != 0) || (pass == 1 && d % 2 != 0)) continue;
+      if (run_layout_supported(d, l)) {
+        D = d;
+        L = l;
+        return;
+      }
+    }
+  }
+  D = 0;
+  L = 0;
+}
+
+}  // namespace
+
+hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
+  RunArgs a;
+  a.p = p;
+  a.out = out;
+  a.counts = counts;
+  a.tiles_y = (p.Y + kTileY - 1) / kTileY;
+  const long long tiles = (long long)p.B * p.X * a.tiles_y;
+  if (tiles == 0) return hipSuccess;
+  if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
+  const int es = p.elem_bytes;
+  const bool vec16 = p.vec_bytes == 16;
+  // channel groups of at most 512 bytes per pixel (16 lanes x 8 dwords), each shrunk until its byte
+  // size maps onto a supported lane layout
+  const int max_group_ch = 512 / es;
+  int c = 0;
+  bool first = true;
+  do {
+    int Cg = p.C - c;
+    if (Cg > max_group_ch) Cg = max_group_ch;
+    int D = 0, L = 0;
+    while (Cg > 0) {
+      pick_run_layout(Cg * es, vec16, D, L);
+      if (L > 0) break;
+      --Cg;
+    }
+    if (Cg == 0) {
+      if (p.C > 0) return hipErrorInvalidValue;      // unreachable for 4-byte-multiple channel rows
+      D = 1;                                          // C == 0: counts only, no channel reads
+      L = 16;
+    }
+    a.c_lo = c;
+    a.Cg = Cg;
+    a.write_counts = (first && counts != nullptr) ? 1 : 0;
+    const size_t shmem = sizeof(CamRec) * p.N + (out_tile_bytes(Cg) + wave_lds_bytes(p.N, kWave / L)) * kWaves;
+    const dim3 grid((unsigned)tiles);
+    const bool ok = (es == 2) ? dispatch_runs<true>(D, L, a, grid, shmem, stream)
+                              : dispatch_runs<false>(D, L, a, grid, shmem, stream);
+    if (!ok) return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    c += Cg;
+    first = false;
+  } while (c < p.C);
+  return hipSuccess;
+}
+
+bool backward_runs_supported(const Problem& p) {
+  return p.L == 1 && p.W <= 256 && p.H <= 256 && p.N <= 64 && p.Z <= 65535;
+}
+
+hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* grad_feat, hipStream_t stream) {
+  BwdRunArgs a;
+  a.p = p;
+  a.grad = grad_out;
+  a.dF = grad_feat;
+  a.tiles_x = (p.X + kBTileX - 1) / kBTileX;
+  a.tiles_y = (p.Y + kBTileY - 1) / kBTileY;
+  a.max_ent = 3072;                     // at least one round of every wave
+  a.max_keys = 2048;
+  const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
+  if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
+  if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
+  const size_t shmem = bwd_lds(p.N, a.max_ent, a.max_keys).total;
+  for (int c = 0; c < p.C; c += kBCg) {
+    a.c_lo = c;
+    a.Cg = (p.C - c < kBCg) ? p.C - c : kBCg;
+    hipLaunchKernelGGL(sampling_vt_runs_bwd, dim3((unsigned)tiles), dim3(kBThreads), shmem, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace fbev

@@ -39,6 +39,37 @@ constexpr int kRowRor2 = 0x122;       // rotate the row by 2 lanes
 constexpr int kRowRor4 = 0x124;       // rotate the row by 4 lanes
 constexpr int kRowRor8 = 0x128;       // rotate the row by 8 lanes
 
+constexpr int kRowShr1 = 0x111;       // lane j of the row takes lane j - 1 (none below lane 0 of the row)
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;    // lane 15 of each row to every lane of the next row
+constexpr int kRowBcast31 = 0x143;    // lane 31 to every lane of rows 2 and 3
+constexpr int kWaveShl1 = 0x130;      // lane i takes lane i + 1 (none for lane 63)
+constexpr int kWaveShr1 = 0x138;      // lane i takes lane i - 1 (none for lane 0)
+
+// x of the lane that DPP control Ctrl names, or `none` where there is no such lane or its row is masked out.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ int dpp_or(int x, int none) {
+  return __builtin_amdgcn_update_dpp(none, x, Ctrl, RowMask, 0xF, false);
+}
+
+// Inclusive prefix sum over the wave in lane order: shifts within each row of 16, then the row
+// broadcasts carry each row's total into the rows above it (six DPP adds, no LDS).
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += dpp_or<kRowShr1>(v, 0);
+  v += dpp_or<kRowShr2>(v, 0);
+  v += dpp_or<kRowShr4>(v, 0);
+  v += dpp_or<kRowShr8>(v, 0);
+  v += dpp_or<kRowBcast15, 0xA>(v, 0);
+  v += dpp_or<kRowBcast31, 0xC>(v, 0);
+  return v;
+}
+
+// The value of the previous (next) lane of the wave, `none` for lane 0 (63).
+__device__ __forceinline__ int lane_prev(int x, int none) { return dpp_or<kWaveShr1>(x, none); }
+__device__ __forceinline__ int lane_next(int x, int none) { return dpp_or<kWaveShl1>(x, none); }
+
 // Sum over the four lanes of a quad.
 template <typename T>
 __device__ __forceinline__ T quad_sum(T x) {
