@@ -73,13 +73,13 @@ def kernel_source_hash(path: str = KERNEL_SRC) -> str:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic(kernel, workload: str):
-    """HBM bytes per launch from committed rocprofv3 PMC counters, or None when
-    they were taken on a different kernel source or workload (or never).  Each
-    workload's record names the source file(s) its counters were taken on.
-    ``kernel`` may be a list: the bytes of one pass of those kernels."""
+def measured_traffic(kernel, workload: str, field: str = "bytes_per_launch"):
+    """A per-launch figure from committed rocprofv3 PMC counters (``field``: HBM bytes, or
+    ``valu_insts`` for SQ_INSTS_VALU), or None when they were taken on a different kernel
+    source or workload (or never).  Each workload's record names the source file(s) its
+    counters were taken on.  ``kernel`` may be a list: the sum over one pass of those kernels."""
     if isinstance(kernel, (list, tuple)):
-        parts = [measured_traffic(k, workload) for k in kernel]
+        parts = [measured_traffic(k, workload, field) for k in kernel]
         return None if any(v is None for v in parts) else sum(parts)
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -97,7 +97,23 @@ def measured_traffic(kernel, workload: str):
     except OSError:
         return None
     k = w.get("kernels", {}).get(kernel)
-    return k.get("bytes_per_launch") if k else None
+    return k.get(field) if k else None
+
+
+# Vector-ALU issue peak without packed math: 256 CUs x 4 SIMDs x 16 lanes, one lane-operation per cycle
+# each at 2.4 GHz (a wave64 instruction occupies its SIMD for 4 cycles).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def counter_fracs(kernels, ms, workload):
+    """``valu_frac`` (SQ_INSTS_VALU x 64 lanes / time / VALU_PEAK_LANE_OPS) and ``hbm_frac_counters``
+    (FETCH_SIZE + WRITE_SIZE bytes / time / 8 TB/s) of a pass of ``kernels`` taking ``ms``, from the
+    committed counters (None when missing or stale)."""
+    s_ = ms * 1e-3
+    valu = measured_traffic(kernels, workload, "valu_insts")
+    traffic = measured_traffic(kernels, workload)
+    return {"valu_frac": None if valu is None else valu * 64 / s_ / VALU_PEAK_LANE_OPS,
+            "hbm_frac_counters": None if traffic is None else traffic / s_ / 1e9 / HBM_PEAK_GBPS}
 
 
 def pass_roofline(kernels, rate, nbytes, workload):
@@ -105,10 +121,33 @@ def pass_roofline(kernels, rate, nbytes, workload):
     ``kernels`` lists the pass's launches in order (their rocprofv3 durations add up to the pass);
     ``traffic`` sums their counter bytes (None when the counters are missing or stale)."""
     achieved = rate["hbm_gbps_algorithmic"]
-    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(kernels, workload),
-            "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
+    d = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": achieved / HBM_PEAK_GBPS,
+         "traffic": measured_traffic(kernels, workload),
+         "kernel": " + ".join(kernels), "launch_ms": rate["ms"], "algorithmic_bytes": nbytes}
+    d.update(counter_fracs(kernels, rate["ms"], workload))
+    return d
+
+
+def time_floor(args, dev, shape):
+    """The compulsory part of a forward pass: a torch ``fill_`` of an fp32 tensor of the output's shape
+    on the same stream (one launch and a write-only pass over the output), timed like the passes."""
+    import numpy as np
+    import torch
+    buf = torch.empty(shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        buf.fill_(1.0)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(ev):
+        a.record(stream)
+        buf.fill_(float(k))
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    log(f"[bench] floor: fill of {tuple(shape)} fp32 {ms * 1e3:.2f} us")
+    return ms
 
 
 def time_passes(args, dev, passes, label):
@@ -586,6 +625,9 @@ def main():
     g = to_dev(inp.grad_out)
     out = torch.empty((B, C, X, Y), dtype=torch.float32, device=dev)
     es = Fdev.element_size()
+    # the key of this run's counter record: the workload, plus the dtype when it is not the workload's first
+    first = wl.WORKLOADS[args.workload].dtypes[0] if args.workload in wl.WORKLOADS else "f32"
+    key = args.workload if inp.dtype == first else f"{args.workload}_{inp.dtype}"
 
     # valid (cell, z, camera) samples, for the samples/s figures (outside the timed region)
     _, cnt = fwd_call(with_counts=True)
@@ -606,9 +648,15 @@ def main():
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems, bilinear_samples_per_s=samples,
                      logical_samples_per_s=logical)
     # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch,
-    # all feature levels)
-    dom_k, dom, dom_bytes = (["sampling_vt_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        (["fill_zero_f32", "sampling_vt_bwd"], bwd, bwd_bytes)
+    # all feature levels); single-level problems run the bin-run kernels
+    fwd_k = ["sampling_vt_runs_fwd"] if nlev == 1 else ["sampling_vt_fwd"]
+    bwd_k = ["fill_zero_f32", "sampling_vt_runs_bwd" if nlev == 1 else "sampling_vt_bwd"]
+    fwd.update(counter_fracs(fwd_k, fwd_ms, key))
+    bwd.update(counter_fracs(bwd_k, bwd_ms, key))
+    floor_ms = time_floor(args, dev, (B, C, X, Y))
+    fwd["roofline"] = dict(pass_roofline(fwd_k, fwd, fwd_bytes, key), floor_ms=floor_ms,
+                           floor_frac=floor_ms / fwd_ms)
+    dom_k, dom, dom_bytes = (fwd_k, fwd, fwd_bytes) if fwd_ms >= bwd_ms else (bwd_k, bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step,
                       "f32" if inp.dtype == "f32" else "bf16 in, f32 accumulate",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features and upstream gradient",
@@ -617,7 +665,7 @@ def main():
                        "B": B, "N": N, "C": C, "H": H, "W": W, "levels": nlev, "X": X, "Y": Y, "Z": Z,
                        "valid_samples_per_pass": valid_tuples})
     line.update({"bilinear_samples_per_s": samples * 2 / (ms_step * 1e-3), "forward": fwd, "backward": bwd,
-                 "roofline": pass_roofline(dom_k, dom, dom_bytes, args.workload)})
+                 "roofline": dict(pass_roofline(dom_k, dom, dom_bytes, key), floor_ms=floor_ms)})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = baseline(inp, args.cpu_rows or X)

@@ -19,7 +19,7 @@
 // value is within rounding of zero, i.e. for a sample within ~1e-12 px of an
 // image edge.)
 //
-// Per wave: eight consecutive cells of one x-row.  Phase A: lane = (cell,
+// Per wave: eight consecutive cells of the flattened grid.  Phase A: lane = (cell,
 // camera), the run, and an exclusive prefix of the run lengths, so the wave's
 // samples have indices 0 .. T-1 in (cell, camera, bin) order.  Then rounds of
 // 64 samples: phase B, lane = sample: its count, the exact projection (fp64
@@ -31,8 +31,9 @@
 // chunk), a tap's channel group read as one coalesced channels-last row per
 // 16-lane (or L-lane) slot, fp32 accumulation, and at a cell's last tap the
 // slots are summed with lane swaps into the workgroup's output tile in LDS.
-// The tile (32 cells of one x-row) leaves as full 128-byte lines of the
-// [B, C, X, Y] output.
+// The tile (32 consecutive cells of the flattened [X, Y] grid) leaves as full,
+// aligned 128-byte lines of the [B, C, X, Y] output when X * Y is a multiple
+// of 32.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,7 +47,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kBlock = kWave * kWaves;
-constexpr int kTileY = 32;               // cells per tile along y: one 128-byte output line per (channel, x-row)
+constexpr int kTileY = 32;               // cells per tile (flattened grid): one 128-byte output line per channel
 constexpr int kCpw = kTileY / kWaves;    // cells per wave
 constexpr int kOutLd = kCpw + 1;         // padded LDS row of a wave's output tile (one channel, its cells)
 constexpr int kRound = kWave;            // samples per round, one per lane
@@ -189,19 +190,32 @@ struct RunArgs {
   uint8_t* counts;
   int c_lo;          // first channel of this launch's group
   int Cg;            // channels of the group
-  int tiles_y;       // ceil(Y / kTileY)
+  int tiles_pb;      // tiles per sample: ceil(X * Y / kTileY)
   int write_counts;
 };
 
 // Sample descriptor: bin k (16 bits), camera n (6 bits), cell of the wave (up to 6 bits).
 __device__ __forceinline__ int desc_pack(int k, int n, int cl) { return k | (n << 16) | (cl << 22); }
 
-// The cells a wave works on: cell cl (0 <= cl < n) is (x0 + cl / ny, y0 + cl % ny); cells outside the grid
-// have no samples.
+// The cells a wave works on: cell cl (0 <= cl < n) sits at position y0 + cl of rows of ny cells that start
+// at grid row x0, shifted by yoff along y: a flat run of the [X, Y] grid (ny = Y, yoff = 0), or one row of
+// a rectangular tile (y0 = 0, ny = tile width, yoff = the tile's first y).  Cells outside the grid have no
+// samples.
 struct CellSet {
-  int x0, y0, ny, n;
-  __device__ int x(int cl) const { return x0 + cl / ny; }
-  __device__ int y(int cl) const { return y0 + cl % ny; }
+  int x0, y0, ny, n, yoff;
+  __device__ int x(int cl) const {
+    int pos = y0 + cl, x = x0;
+    while (pos >= ny) {
+      pos -= ny;
+      ++x;
+    }
+    return x;
+  }
+  __device__ int y(int cl) const {
+    int pos = y0 + cl;
+    while (pos >= ny) pos -= ny;
+    return yoff + pos;
+  }
 };
 
 // Phase B for one sample: the four taps (byte offsets of their pixels, weights
@@ -455,19 +469,19 @@ void sampling_vt_runs_fwd(RunArgs a) {
   int* sRun = sCellHi + kCpw;                                       // [npair] lo | hi << 16
   int* sStart = sRun + npair;                                       // [npair + 1] first sample index of each run
 
+  // tile = kTileY consecutive cells of the flattened [X, Y] grid, so that every channel's part of the
+  // output tile is one aligned 128-byte line when X * Y is a multiple of 32
   const int tile = xcd_block(blockIdx.x, gridDim.x);
-  const int yt = tile % a.tiles_y;
-  const int bx = tile / a.tiles_y;
-  const int x = bx % p.X;
-  const int b = bx / p.X;
-  const int y_tile = yt * kTileY;
-  const int y_wave = y_tile + wid * kCpw;
+  const int b = tile / a.tiles_pb;
+  const long long XY = (long long)p.X * p.Y;
+  const long long f_wave = (long long)(tile - b * a.tiles_pb) * kTileY + wid * kCpw;
 
   stage_cameras(sCam, p, b);
 
   for (int e = lane; e < a.Cg * kOutLd; e += kWave) sOut[e] = 0.f;     // cells with no sample stay 0
-  const int ncell = min(kCpw, p.Y - y_wave);          // cells of this wave (may be <= 0)
-  const CellSet cs{x, y_wave, kCpw, kCpw};
+  const int ncell = (int)min((long long)kCpw, XY - f_wave);            // cells of this wave (may be <= 0)
+  const int x_first = (int)(min(f_wave, XY) / p.Y), y_first = (int)(min(f_wave, XY) % p.Y);
+  const CellSet cs{x_first, y_first, p.Y, kCpw, 0};
 
   // ---- phase A: runs of (cell, camera) pairs, cell-major, and their first sample indices
   const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
@@ -481,7 +495,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
         const int r = sRun[cl * N + n];
         cnt += ((r & 0xffff) <= k && k <= (r >> 16)) ? 1 : 0;
       }
-      a.counts[(((size_t)b * p.X + x) * p.Y + y_wave + cl) * p.Z + k] = (uint8_t)cnt;
+      a.counts[((size_t)b * XY + f_wave + cl) * p.Z + k] = (uint8_t)cnt;
     }
   }
 
@@ -558,11 +572,11 @@ void sampling_vt_runs_fwd(RunArgs a) {
   }
   wave_lds_sync();
 
-  // ---- write-out of this wave's cells: per channel, ncell consecutive y of one x-row (the four waves of
-  // the workgroup write the four quarters of each 128-byte line from one CU, so they meet in its L2)
+  // ---- write-out of this wave's cells: per channel, ncell consecutive cells of the flattened grid (the
+  // four waves of the workgroup write the four quarters of each 128-byte line from one CU)
   if (ncell > 0) {
-    const size_t c_stride = (size_t)p.X * p.Y;
-    float* ob = a.out + (((size_t)b * p.out_ch + a.c_lo) * p.X + x) * p.Y + y_wave;
+    const size_t c_stride = (size_t)XY;
+    float* ob = a.out + ((size_t)b * p.out_ch + a.c_lo) * c_stride + f_wave;
     const bool vec = ncell == kCpw && (((uintptr_t)ob | (size_t)p.Y * 4) & 15) == 0;
     for (int e = lane; e < a.Cg * 2; e += kWave) {
       const int ch = e >> 1, h = (e & 1) * 4;
@@ -854,16 +868,7 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
                                                    : 0.f;
     }
   }
-  stage_cameras(sCam, p, b);
-#pragma unroll
-  for (int i = 0; i < kGPer; ++i) {
-    const int e = threadIdx.x + i * kBThreads;
-    const int c = e / kBCells, cl = e - c * kBCells;
-    // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3): where the per-pixel reduce-scatter
-    // leaves channel c in lane c
-    const int q = c & 15, r = c >> 4;
-    sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
-  }
+  // boxes and the entry count start empty (visible after the camera staging's barrier)
   for (int e = threadIdx.x; e < N; e += kBThreads) {
     sBox[4 * e] = 0x7fffffff;
     sBox[4 * e + 1] = -1;
@@ -871,10 +876,12 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
     sBox[4 * e + 3] = -1;
   }
   if (threadIdx.x == 0) sMisc[0] = 0;
-  // this wave's cells: x-row wid of the block, 8 cells
-  const CellSet cs{x_tile + wid, y_tile, kBTileY, kBCpw};
+  stage_cameras(sCam, p, b);
+  // this wave's cells: x-row wid of the block, 8 cells; the waves go on without waiting for each other,
+  // and the gradient tile stays in registers (its loads in flight) until the first flush needs it
+  const CellSet cs{x_tile + wid, 0, kBTileY, kBCpw, y_tile};
   const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
-  __syncthreads();
+  bool g_staged = false;
 
   int r0 = 0;
   for (;;) {
@@ -927,7 +934,21 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
     for (int w = 0; w < kBWaves; ++w) next += sMisc[8 + w];
     const int nent = sMisc[0];
     __syncthreads();                 // every wave has read the counts before any changes them
-    if (next == 0 || nent + next > a.max_ent) bwd_flush(a, smem, lay, b);
+    if (next == 0 || nent + next > a.max_ent) {
+      if (!g_staged) {
+#pragma unroll
+        for (int i = 0; i < kGPer; ++i) {
+          const int e = threadIdx.x + i * kBThreads;
+          const int c = e / kBCells, cl = e - c * kBCells;
+          // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3): where the per-pixel
+          // reduce-scatter leaves channel c in lane c (the flush's barriers publish these stores)
+          const int q = c & 15, r = c >> 4;
+          sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
+        }
+        g_staged = true;
+      }
+      bwd_flush(a, smem, lay, b);
+    }
     if (next == 0) break;
   }
 }
@@ -986,10 +1007,11 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
   a.p = p;
   a.out = out;
   a.counts = counts;
-  a.tiles_y = (p.Y + kTileY - 1) / kTileY;
-  const long long tiles = (long long)p.B * p.X * a.tiles_y;
+  const long long tiles_pb = ((long long)p.X * p.Y + kTileY - 1) / kTileY;
+  const long long tiles = (long long)p.B * tiles_pb;
   if (tiles == 0) return hipSuccess;
   if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
+  a.tiles_pb = (int)tiles_pb;
   const int es = p.elem_bytes;
   const bool vec16 = p.vec_bytes == 16;
   // channel groups of at most 512 bytes per pixel (16 lanes x 8 dwords), each shrunk until its byte
