@@ -582,12 +582,11 @@ void sampling_vt_runs_fwd(RunArgs a) {
       const int ch = e >> 1, h = (e & 1) * 4;
       const float* src = sOut + ch * kOutLd + h;
       float* dst = ob + ch * c_stride + h;
+      // plain stores: the L2 merges the four waves' quarters of a line before it writes the line back
       if (vec) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 v4 = {src[0], src[1], src[2], src[3]};
-        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(dst));
+        *reinterpret_cast<float4*>(dst) = make_float4(src[0], src[1], src[2], src[3]);
       } else {
-        for (int k = 0; k < 4 && h + k < ncell; ++k) __builtin_nontemporal_store(src[k], dst + k);
+        for (int k = 0; k < 4 && h + k < ncell; ++k) dst[k] = src[k];
       }
     }
   }
