@@ -50,7 +50,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kBlock = kWave * kWaves;
-constexpr int kTileY = 16;               // cells per unit (one x-row)
+constexpr int kTileY = 32;               // cells per unit (one x-row): 128-byte rows of the upstream gradient
 constexpr int kCg = 64;                  // channels per unit
 constexpr int kGLd = kCg + 4;            // padded LDS row of one cell's upstream gradient
 constexpr int kRedLd = 13;               // padded LDS row of one lane's 12 partial sums
@@ -98,7 +98,7 @@ struct CamGradArgs {
 // V = 4: lane chunk j holds channels 4j..4j+3 of the group (one 16-byte load
 // per tap); V = 1: channels j, j+16, j+32, j+48 (four 4-byte loads).
 template <int V>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void camera_grad_main(CamGradArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(V == 4 ? 5 : 4))) void camera_grad_main(CamGradArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
   double* sP = reinterpret_cast<double*>(smem);                                   // [N][12]

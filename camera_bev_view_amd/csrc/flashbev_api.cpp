@@ -235,9 +235,9 @@ fbev_status check_cameras(const fbev_feat_desc& fd, int32_t X, int32_t Y, int32_
   if (batch_elems >= (int64_t)1 << 31)
     return fail(FBEV_ERR_UNSUPPORTED, "one sample's features span %lld elements (limit 2^31 - 1)",
                 (long long)batch_elems);
-  const int64_t units = (int64_t)X * ((Y + 15) / 16) * ((fd.C + 63) / 64);
+  const int64_t units = (int64_t)X * ((Y + 31) / 32) * ((fd.C + 63) / 64);
   if (units >= (int64_t)1 << 31)
-    return fail(FBEV_ERR_UNSUPPORTED, "%lld work units (x-rows x 16-cell tiles x 64-channel groups), limit 2^31 - 1",
+    return fail(FBEV_ERR_UNSUPPORTED, "%lld work units (x-rows x 32-cell tiles x 64-channel groups), limit 2^31 - 1",
                 (long long)units);
   p.elem_bytes = 4;
   p.vec_bytes = 4;

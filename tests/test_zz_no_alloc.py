@@ -60,11 +60,12 @@ def test_noalloc_allocates_nothing_and_rejects_oversize():
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == alloc0
     assert torch.cuda.mem_get_info()[0] == free0
-    # 30 cameras of one sample need 30 * 172032 bytes > 4 MiB: refused before any launch
-    big = wl.random_case(32, 1, 30, 4, 8, 22, 200, 200, 2, with_grad=True)
+    # 40 cameras of one sample need 40 * 12 * 8 * 1400 bytes (12 fp64 partial sums per camera and workgroup,
+    # one workgroup per 32-cell unit of the 200 x 200 grid) > 4 MiB: refused before any launch
+    big = wl.random_case(32, 1, 40, 4, 8, 22, 200, 200, 2, with_grad=True)
     F2, K2, R2, t2 = to_device(big)
     g2 = torch.from_numpy(big.grad_out).cuda()
-    o2 = (torch.empty((1, 30, 3, 3), device="cuda"), torch.empty((1, 30, 3, 3), device="cuda"),
-          torch.empty((1, 30, 3), device="cuda"))
+    o2 = (torch.empty((1, 40, 3, 3), device="cuda"), torch.empty((1, 40, 3, 3), device="cuda"),
+          torch.empty((1, 40, 3), device="cuda"))
     with pytest.raises(_lib.FlashBevError, match="allocation-free variant holds"):
         ops.camera_backward_noalloc(g2, F2, K2, R2, t2, big.rng6, 200, 200, 2, *o2)
