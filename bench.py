@@ -647,10 +647,10 @@ def main():
                      logical_samples_per_s=logical)
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems, bilinear_samples_per_s=samples,
                      logical_samples_per_s=logical)
-    # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch,
-    # all feature levels); single-level problems run the bin-run kernels
-    fwd_k = ["sampling_vt_runs_fwd"] if nlev == 1 else ["sampling_vt_fwd"]
-    bwd_k = ["fill_zero_f32", "sampling_vt_runs_bwd" if nlev == 1 else "sampling_vt_bwd"]
+    # the timed passes: the forward kernel alone; the backward's zero-fill and its kernel (one launch, all
+    # feature levels; the bin-run kernel for single-level maps of at most 256 x 256 pixels)
+    fwd_k = ["sampling_vt_runs_fwd"]
+    bwd_k = ["fill_zero_f32", "sampling_vt_runs_bwd" if nlev == 1 and max(H, W) <= 256 else "sampling_vt_bwd"]
     fwd.update(counter_fracs(fwd_k, fwd_ms, key))
     bwd.update(counter_fracs(bwd_k, bwd_ms, key))
     floor_ms = time_floor(args, dev, (B, C, X, Y))

@@ -1020,10 +1020,9 @@ __global__ void fill_zero_f32(float* __restrict__ dst, size_t n) {
 
 template <int D, int L, bool BF16>
 void launch_fwd_group(const FwdArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
-  if (a.p.L > 1)
-    hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16, true>), grid, dim3(kBlock), shmem, stream, a);
-  else
-    hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16, false>), grid, dim3(kBlock), shmem, stream, a);
+  // single level only: this forward serves the temporal fusion; fbev_forward and the pyramids run the
+  // bin-run forward (sampling_vt_runs.hip)
+  hipLaunchKernelGGL((sampling_vt_fwd<D, L, BF16, false>), grid, dim3(kBlock), shmem, stream, a);
 }
 
 // Supported lane layouts (dwords per lane D, lanes per tap L).
@@ -1149,8 +1148,7 @@ hipError_t forward_groups(const Problem& p, float* out, uint8_t* counts, const A
 }  // namespace
 
 hipError_t launch_forward(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
-  if (p.L == 1) return launch_forward_runs(p, out, counts, stream);
-  return forward_groups(p, out, counts, nullptr, nullptr, stream);
+  return launch_forward_runs(p, out, counts, stream);
 }
 
 hipError_t launch_forward_temporal(const Problem& p, float* out, uint8_t* counts, bool current, int Cp,

@@ -218,19 +218,38 @@ struct CellSet {
   }
 };
 
+// a / d for 0 <= a < 1024 and 1 <= d <= 64 by one multiply, given m = div_magic(d) (wave-uniform): the
+// error a (m / 65536 - 1 / d) stays below 1024 / 65536 <= 1 / d, so the floor is exact.
+__device__ __forceinline__ int div_magic(int d) { return uniform((65536 + d - 1) / d); }
+__device__ __forceinline__ int div_small(int a, int m) { return (a * m) >> 16; }
+
+template <class T>
+__device__ __forceinline__ T level_of(const T (&a)[kMaxLevels], int l) {
+  return l == 0 ? a[0] : l == 1 ? a[1] : l == 2 ? a[2] : a[3];
+}
+
 // Phase B for one sample: the four taps (byte offsets of their pixels, weights
 // / count).  u, v are clamped to the pixel-centre box before the floor so that
 // rounding at an edge never reaches outside the map; the clamped second tap at
-// the last column / row repeats the first with weight 0.
+// the last column / row repeats the first with weight 0.  With lvl_ir != 0 the
+// taps are those of a coarser pyramid level of ratio 1 / lvl_ir: the point's
+// level coordinate (u + 1/2) / r - 1/2, clamped to that level's box (the border
+// rule of the level mean).
 __device__ __forceinline__ void sample_taps(const CamRec& c, double px, double py, double pz, float rc, int H, int W,
                                             int pix_base, int pix_bytes, Rec (&t)[4], int& top, int& bot,
-                                            int& xy) {
+                                            int& xy, double lvl_ir = 0.0) {
   const double h0 = fma(c.P[0], px, fma(c.P[1], py, fma(c.P[2], pz, c.P[3])));
   const double h1 = fma(c.P[4], px, fma(c.P[5], py, fma(c.P[6], pz, c.P[7])));
   const double h2 = fma(c.P[8], px, fma(c.P[9], py, fma(c.P[10], pz, c.P[11])));
   const double r = recip(h2);
-  const double u = fmin(fmax(h0 * r, 0.0), (double)(W - 1));
-  const double v = fmin(fmax(h1 * r, 0.0), (double)(H - 1));
+  double uu = h0 * r, vv = h1 * r;
+  if (lvl_ir != 0.0) {
+    // a coarser pyramid level (H, W its size): the level-0 point in that level's pixels
+    uu = fma(uu + 0.5, lvl_ir, -0.5);
+    vv = fma(vv + 0.5, lvl_ir, -0.5);
+  }
+  const double u = fmin(fmax(uu, 0.0), (double)(W - 1));
+  const double v = fmin(fmax(vv, 0.0), (double)(H - 1));
   const double fu = floor(u), fv = floor(v);
   const int x0 = (int)fu, y0 = (int)fv;
   const float fa = (float)(u - fu), fb = (float)(v - fv);
@@ -248,17 +267,22 @@ __device__ __forceinline__ void sample_taps(const CamRec& c, double px, double p
   xy = x0 | (y0 << 16);
 }
 
-// Phase A for the wave's cells: the run [lo, hi] of every (cell, camera) pair (cell-major, lo | hi << 16)
-// and the index of its first sample (sStart[npair] = the total); returns the wave's sample total.
+// Phase A for the wave's cells: the run [lo, hi] of every (cell, virtual camera) pair, virtual camera
+// vn = n L + l for camera n and pyramid level l (validity is decided at level 0, so a camera's levels share
+// its run), cell-major, and the index of its first sample (sStart[npair] = the total); returns the wave's
+// sample total.
+template <bool ML>
 __device__ int wave_runs(const CamRec* sCam, const Problem& p, const CellSet& cs, int* sRun, int* sStart,
                          int lane) {
-  const int N = p.N, npair = cs.n * N;
+  const int L = ML ? p.L : 1, NL = p.N * L, npair = cs.n * NL;
+  const int mNL = ML ? div_magic(NL) : 0, mL = ML ? div_magic(L) : 0;
   const double z0 = p.oz + 0.5 * p.dz;
   const double Wm1 = (double)(p.W - 1), Hm1 = (double)(p.H - 1);
   int total = 0;
   for (int pb = 0; pb < npair; pb += kWave) {
     const int pi = pb + lane;
-    const int cl = pi / (N > 0 ? N : 1), n = pi - cl * N;
+    const int cl = ML ? div_small(pi, mNL) : pi / (NL > 0 ? NL : 1);
+    const int n = ML ? div_small(pi - cl * NL, mL) : pi - cl * NL;
     int lo = 1, hi = 0;
     if (pi < npair && cs.x(cl) < p.X && cs.y(cl) < p.Y) {
       const double px = p.ox + ((double)cs.x(cl) + 0.5) * p.dx;
@@ -299,14 +323,15 @@ __device__ void emit_round(const int* sRun, const int* sStart, int npair, int N,
 // On return tp holds the lane's (merged) taps, keep_top / keep_bot say which rows it keeps; sTap has been
 // read by every lane (the caller may overwrite it after a wave sync).
 struct Sample {
-  int cl, n, xy;              // cell of the wave, camera, top-left tap pixel (x | y << 16)
+  int cl, n, xy;              // cell of the wave, virtual camera (n L + level), top-left tap pixel (x | y << 16)
   bool keep_top, keep_bot;
   Rec tp[4];
 };
 
+template <bool ML>
 __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const CellSet& cs, const int* sRun,
                                 const int* sDesc, Rec* sTap, int nsmp, int pix_bytes, int lane) {
-  const int N = p.N;
+  const int N = p.N, L = ML ? p.L : 1, NL = p.N * L;
   Sample sm;
   sm.cl = -1;
   sm.n = 0;
@@ -314,21 +339,30 @@ __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const Cell
   int dsc = 0, top = -1, bot = -1;
   if (lane < nsmp) {
     dsc = sDesc[lane];
-    const int k = dsc & 0xffff, n = (dsc >> 16) & 63, cl = dsc >> 22;
+    const int k = dsc & 0xffff, vn = (dsc >> 16) & 63, cl = dsc >> 22;
+    const int n = ML ? div_small(vn, div_magic(L)) : vn, l = vn - n * L;
     int cnt = 0;
     for (int m = 0; m < N; ++m) {
-      const int r = sRun[cl * N + m];
+      const int r = sRun[cl * NL + m * L];
       cnt += ((r & 0xffff) <= k && k <= (r >> 16)) ? 1 : 0;
     }
     const double px = p.ox + ((double)cs.x(cl) + 0.5) * p.dx;
     const double py = p.oy + ((double)cs.y(cl) + 0.5) * p.dy;
     const double pz = p.oz + ((double)k + 0.5) * p.dz;
-    sample_taps(sCam[n], px, py, pz, __builtin_amdgcn_rcpf((float)cnt), p.H, p.W, n * p.P, pix_bytes, sm.tp, top,
-                bot, sm.xy);
+    // the level mean's 1/L rides with the valid-camera count
+    const float rc = __builtin_amdgcn_rcpf((float)(cnt * L));
+    if (ML) {
+      // level 0 is the map the run was decided on (lvl_H[0] = H, lvl_W[0] = W, lvl_off[0] = 0): no transform
+      sample_taps(sCam[n], px, py, pz, rc, level_of(p.lvl_H, l), level_of(p.lvl_W, l),
+                  n * p.P + level_of(p.lvl_off, l), pix_bytes, sm.tp, top, bot, sm.xy,
+                  l == 0 ? 0.0 : level_of(p.lvl_inv_r, l));
+    } else {
+      sample_taps(sCam[n], px, py, pz, rc, p.H, p.W, n * p.P, pix_bytes, sm.tp, top, bot, sm.xy);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) sTap[4 * lane + t] = sm.tp[t];
     sm.cl = cl;
-    sm.n = n;
+    sm.n = vn;
   }
   const int run_id = dsc >> 16;
   const int prev_run = lane_prev(run_id, -1), prev_top = lane_prev(top, -2), prev_bot = lane_prev(bot, -2);
@@ -444,7 +478,7 @@ struct RunWaves {
 
 // Forward.  L lanes cover one tap's channel group with D dwords each (L * D * 4 == group bytes);
 // S = 64 / L taps per load instruction.
-template <int D, int L, bool BF16>
+template <int D, int L, bool BF16, bool ML>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
 void sampling_vt_runs_fwd(RunArgs a) {
   using Ln = Lane<D, BF16>;
@@ -454,14 +488,14 @@ void sampling_vt_runs_fwd(RunArgs a) {
   constexpr int kU = RunWaves<D, L, BF16>::kLoads;       // loads in flight per lane in the gather
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
-  const int N = p.N;
-  const int npair = kCpw * N;
+  const int N = p.N, NL = ML ? p.N * p.L : p.N;    // cameras; virtual cameras (camera x pyramid level)
+  const int npair = kCpw * NL;
   CamRec* sCam = reinterpret_cast<CamRec*>(smem);
   unsigned char* cur = smem + sizeof(CamRec) * N;
   const int wid = uniform(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
-  unsigned char* wbase = cur + (wave_lds_bytes(N, S) + out_tile_bytes(a.Cg)) * wid;
-  float* sOut = reinterpret_cast<float*>(wbase + wave_lds_bytes(N, S));   // [Cg][kOutLd] this wave's cells
+  unsigned char* wbase = cur + (wave_lds_bytes(NL, S) + out_tile_bytes(a.Cg)) * wid;
+  float* sOut = reinterpret_cast<float*>(wbase + wave_lds_bytes(NL, S));  // [Cg][kOutLd] this wave's cells
   Rec* sTap = reinterpret_cast<Rec*>(wbase);                        // [tap_slots(S)] raw, then kept taps by step
   int* sDesc = reinterpret_cast<int*>(sTap + tap_slots(S));         // [kRound] the round's samples
   int* sCellLo = sDesc + kRound;                                    // [kCpw] first kept tap of the cell in the round
@@ -484,7 +518,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
   const CellSet cs{x_first, y_first, p.Y, kCpw, 0};
 
   // ---- phase A: runs of (cell, camera) pairs, cell-major, and their first sample indices
-  const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
+  const int total = wave_runs<ML>(sCam, p, cs, sRun, sStart, lane);
 
   // optional per-bin valid-camera counts (validation output)
   if (a.write_counts) {
@@ -492,7 +526,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
       const int cl = e / p.Z, k = e - cl * p.Z;
       int cnt = 0;
       for (int n = 0; n < N; ++n) {
-        const int r = sRun[cl * N + n];
+        const int r = sRun[cl * NL + n * (ML ? p.L : 1)];
         cnt += ((r & 0xffff) <= k && k <= (r >> 16)) ? 1 : 0;
       }
       a.counts[((size_t)b * XY + f_wave + cl) * p.Z + k] = (uint8_t)cnt;
@@ -514,11 +548,11 @@ void sampling_vt_runs_fwd(RunArgs a) {
 
   for (int r0 = 0; r0 < total; r0 += kRound) {
     const int nsmp = min(kRound, total - r0);
-    emit_round(sRun, sStart, npair, N, r0, sDesc, lane);
+    emit_round(sRun, sStart, npair, NL, r0, sDesc, lane);
     if (lane < kCpw) sCellHi[lane] = -1;
     wave_lds_sync();
     // ---- phase B: lane = sample; taps, count, row merging
-    const Sample sm = round_samples(sCam, p, cs, sRun, sDesc, sTap, nsmp, pix_bytes, lane);
+    const Sample sm = round_samples<ML>(sCam, p, cs, sRun, sDesc, sTap, nsmp, pix_bytes, lane);
     const bool keep_top = sm.keep_top, keep_bot = sm.keep_bot;
     const int cl = sm.cl;
     const Rec* tp = sm.tp;
@@ -540,7 +574,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
     }
     if (cell_first) sCellLo[cl] = pos;
     if (cell_last) {
-      const bool fin = sStart[(cl + 1) * N] <= r0 + kRound;
+      const bool fin = sStart[(cl + 1) * NL] <= r0 + kRound;
       sCellHi[cl] = (pos + nkept) | (fin ? (1 << 30) : 0);
     }
     wave_lds_sync();
@@ -635,21 +669,21 @@ struct BwdLds {
 __host__ __device__ inline size_t bwd_round_bytes() {
   return (sizeof(Rec) * 4 * kRound + sizeof(int) * kRound + 15) & ~(size_t)15;
 }
-__host__ __device__ inline BwdLds bwd_lds(int N, int max_ent, int max_keys) {
+__host__ __device__ inline BwdLds bwd_lds(int N, int NL, int max_ent, int max_keys) {
   BwdLds l;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += (bytes + 15) & ~(size_t)15; return at; };
   l.cam = take(sizeof(CamRec) * N);
   l.g = take(sizeof(float) * kBCells * kBgLd);
-  l.box = take(sizeof(int) * 4 * (N > 0 ? N : 1));
-  l.win = take(sizeof(int) * 4 * (N > 0 ? N : 1));
+  l.box = take(sizeof(int) * 4 * (NL > 0 ? NL : 1));
+  l.win = take(sizeof(int) * 4 * (NL > 0 ? NL : 1));
   l.misc = take(sizeof(int) * 32);
   l.cnt = take(sizeof(int) * (max_keys + 1));
   l.ent = take(sizeof(int2) * max_ent);
   // the sorted entries share their space with the waves' per-round buffers (never live at the same time)
   const size_t sort_bytes = sizeof(int2) * max_ent, rounds = bwd_round_bytes() * kBWaves;
   l.sort = take(sort_bytes > rounds ? sort_bytes : rounds);
-  l.runs = take(sizeof(int) * (2 * (size_t)kBCpw * N + 1) * kBWaves);
+  l.runs = take(sizeof(int) * (2 * (size_t)kBCpw * NL + 1) * kBWaves);
   l.total = o;
   return l;
 }
@@ -671,7 +705,7 @@ __device__ __forceinline__ int wave_max(int v) { return -wave_min(-v); }
 // max_keys keys).  Called by the whole workgroup; ends with the entries and camera boxes cleared.
 __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds& lay, int b) {
   const Problem& p = a.p;
-  const int N = p.N;
+  const int N = p.N, NL = p.N;
   const float* sG = reinterpret_cast<const float*>(smem + lay.g);
   int* sBox = reinterpret_cast<int*>(smem + lay.box);
   int* sWin = reinterpret_cast<int*>(smem + lay.win);
@@ -683,7 +717,7 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
   const int wid = uniform(threadIdx.x / kWave);
   if (threadIdx.x == 0) {
     int base = 0;
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < NL; ++n) {
       const int x_lo = sBox[4 * n], x_hi = sBox[4 * n + 1], y_lo = sBox[4 * n + 2], y_hi = sBox[4 * n + 3];
       const bool used = x_lo <= x_hi;
       sWin[4 * n] = base;
@@ -817,7 +851,7 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
     __syncthreads();
   }
   // cleared for the next batch of entries
-  for (int e = threadIdx.x; e < N; e += kBThreads) {
+  for (int e = threadIdx.x; e < NL; e += kBThreads) {
     sBox[4 * e] = 0x7fffffff;
     sBox[4 * e + 1] = -1;
     sBox[4 * e + 2] = 0x7fffffff;
@@ -830,8 +864,8 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
 __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
-  const int N = p.N;
-  const BwdLds lay = bwd_lds(N, a.max_ent, a.max_keys);
+  const int N = p.N, NL = p.N;                      // single level: the virtual cameras are the cameras
+  const BwdLds lay = bwd_lds(N, NL, a.max_ent, a.max_keys);
   CamRec* sCam = reinterpret_cast<CamRec*>(smem + lay.cam);
   float* sG = reinterpret_cast<float*>(smem + lay.g);
   int* sBox = reinterpret_cast<int*>(smem + lay.box);
@@ -841,7 +875,7 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
   const int wid = uniform(threadIdx.x / kWave);
   Rec* sTap = reinterpret_cast<Rec*>(smem + lay.sort + bwd_round_bytes() * wid);
   int* sDesc = reinterpret_cast<int*>(sTap + 4 * kRound);
-  const int npair = kBCpw * N;
+  const int npair = kBCpw * NL;
   int* sRun = reinterpret_cast<int*>(smem + lay.runs) + (2 * npair + 1) * wid;
   int* sStart = sRun + npair;
 
@@ -868,7 +902,7 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
     }
   }
   // boxes and the entry count start empty (visible after the camera staging's barrier)
-  for (int e = threadIdx.x; e < N; e += kBThreads) {
+  for (int e = threadIdx.x; e < NL; e += kBThreads) {
     sBox[4 * e] = 0x7fffffff;
     sBox[4 * e + 1] = -1;
     sBox[4 * e + 2] = 0x7fffffff;
@@ -879,16 +913,16 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
   // this wave's cells: x-row wid of the block, 8 cells; the waves go on without waiting for each other,
   // and the gradient tile stays in registers (its loads in flight) until the first flush needs it
   const CellSet cs{x_tile + wid, 0, kBTileY, kBCpw, y_tile};
-  const int total = wave_runs(sCam, p, cs, sRun, sStart, lane);
+  const int total = wave_runs<false>(sCam, p, cs, sRun, sStart, lane);
   bool g_staged = false;
 
   int r0 = 0;
   for (;;) {
     if (r0 < total) {
       const int nsmp = min(kRound, total - r0);
-      emit_round(sRun, sStart, npair, N, r0, sDesc, lane);
+      emit_round(sRun, sStart, npair, NL, r0, sDesc, lane);
       wave_lds_sync();
-      const Sample sm = round_samples(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
+      const Sample sm = round_samples<false>(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
       const int x0 = sm.xy & 0xffff, y0 = sm.xy >> 16;
       const int x1 = min(x0 + 1, p.W - 1), y1 = min(y0 + 1, p.H - 1);
       // each camera's pixel box grows by its samples' taps: a wave reduction per camera present
@@ -964,11 +998,11 @@ bool run_layout_supported(int D, int L) {
   return false;
 }
 
-template <bool BF16>
+template <bool BF16, bool ML>
 bool dispatch_runs(int D, int L, const RunArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
 #define FBEV_CASE(d, l)                                                                                   \
   if (D == d && L == l) {                                                                                 \
-    hipLaunchKernelGGL((sampling_vt_runs_fwd<d, l, BF16>), grid, dim3(kBlock), shmem, stream, a);         \
+    hipLaunchKernelGGL((sampling_vt_runs_fwd<d, l, BF16, ML>), grid, dim3(kBlock), shmem, stream, a);     \
     return true;                                                                                          \
   }
   FBEV_RUN_LAYOUTS(FBEV_CASE)
@@ -1035,10 +1069,14 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
     a.c_lo = c;
     a.Cg = Cg;
     a.write_counts = (first && counts != nullptr) ? 1 : 0;
-    const size_t shmem = sizeof(CamRec) * p.N + (out_tile_bytes(Cg) + wave_lds_bytes(p.N, kWave / L)) * kWaves;
+    const size_t shmem =
+        sizeof(CamRec) * p.N + (out_tile_bytes(Cg) + wave_lds_bytes(p.N * p.L, kWave / L)) * kWaves;
     const dim3 grid((unsigned)tiles);
-    const bool ok = (es == 2) ? dispatch_runs<true>(D, L, a, grid, shmem, stream)
-                              : dispatch_runs<false>(D, L, a, grid, shmem, stream);
+    const bool ml = p.L > 1;
+    const bool ok = (es == 2) ? (ml ? dispatch_runs<true, true>(D, L, a, grid, shmem, stream)
+                                    : dispatch_runs<true, false>(D, L, a, grid, shmem, stream))
+                              : (ml ? dispatch_runs<false, true>(D, L, a, grid, shmem, stream)
+                                    : dispatch_runs<false, false>(D, L, a, grid, shmem, stream));
     if (!ok) return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1049,6 +1087,8 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
 }
 
 bool backward_runs_supported(const Problem& p) {
+  // pyramids stay on the hash-table backward: their fine level puts many distinct pixels under a tile, and
+  // its 4 x 4 tiles measured faster there (142 against 416 us on the three-level workload)
   return p.L == 1 && p.W <= 256 && p.H <= 256 && p.N <= 64 && p.Z <= 65535;
 }
 
@@ -1064,7 +1104,7 @@ hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* 
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
   if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
-  const size_t shmem = bwd_lds(p.N, a.max_ent, a.max_keys).total;
+  const size_t shmem = bwd_lds(p.N, p.N, a.max_ent, a.max_keys).total;
   for (int c = 0; c < p.C; c += kBCg) {
     a.c_lo = c;
     a.Cg = (p.C - c < kBCg) ? p.C - c : kBCg;
