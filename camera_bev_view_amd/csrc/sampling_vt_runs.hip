@@ -633,11 +633,11 @@ void sampling_vt_runs_fwd(RunArgs a) {
 // becomes an entry (pixel, cell, weight) of the workgroup.  A counting sort by pixel in LDS then makes
 // every pixel's entries contiguous: the keys are a window per camera (the bounding box of the pixels
 // that camera's taps reach), counts by integer LDS atomics, a block scan, and a scatter by atomic
-// cursors.  The pixels are shared among the waves by entry count; the four 16-lane groups of a wave
-// split one pixel's entries, grad(cell) * weight with the grad rows read from the block's
-// upstream-gradient tile in LDS (4 channels per lane), a reduce-scatter over the groups gives lane l
-// channel l, and each pixel leaves the workgroup as one fp32 global atomic over its consecutive
-// channels.  LDS float atomics are avoided: on this chip they are far slower than the integer ones.
+// cursors.  The pixels are shared among the waves by entry count; each 16-lane group of a wave sums
+// one pixel's entries, grad(cell) * weight with the grad rows read from the block's upstream-gradient
+// tile in LDS (4 channels per lane), and each pixel leaves the workgroup as fp32 global atomics over
+// its consecutive channels.  LDS float atomics are avoided: on this chip they are far slower than the
+// integer ones.
 
 constexpr int kBWaves = 8;
 constexpr int kBThreads = kBWaves * kWave;
@@ -647,7 +647,6 @@ constexpr int kBCells = kBTileX * kBTileY;
 constexpr int kBCpw = kBTileY;             // cells per wave
 constexpr int kBCg = 64;                   // channels per workgroup: 16 lanes x 4 per pixel
 constexpr int kBgLd = kBCg + 4;            // upstream-gradient tile row (one cell's channels), 16-byte aligned
-constexpr int kBRedG = 4;                  // entries per lane group and reduction step
 
 struct BwdRunArgs {
   Problem p;
@@ -787,64 +786,63 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
     }
     __syncthreads();
     // per-pixel sums.  Wave w takes keys [sMisc[24 + w], sMisc[25 + w]): about an eighth of the entries.
-    // The four 16-lane groups split a pixel's entries (entry i to group i mod 4), each lane holding 4
-    // channels, and a reduce-scatter over the groups leaves lane l with channel l of the pixel's sum (the
-    // tile's channel order in LDS is chosen for that), which goes to dF as one atomic over the pixel's
-    // consecutive channels.  Keys are taken 64 at a time, one per lane, so their ranges and pixels come
-    // from registers, and the next pixel's first entries are read while the current one is summed.
+    // Keys are taken 64 at a time, one per lane; the non-empty ones are compacted to the low lanes by a
+    // forward lane permute, and each 16-lane group then sums one pixel: four pixels per step, each lane
+    // holding 4 channels, its pixel's entries taken 4 at a time (grad rows from the block's tile in LDS).
+    // With the tile's channel order, lane q of a group holds channels q, q + 32, q + 16 and q + 48, so the
+    // pixel leaves the workgroup as four fp32 atomics over 16 consecutive channels each.  A pixel costs its
+    // own entries plus a share of one step, whatever the spread of entries over pixels.
     {
       const int ka = sMisc[24 + wid], kb = wid + 1 < kBWaves ? sMisc[25 + wid] : kn;
-      const int grp = lane >> 4;
-      const float* gq = sG + 4 * (lane & 15);
+      const int grp = lane >> 4, q = lane & 15;
+      const float* gq = sG + 4 * q;
       for (int kc = ka; kc < kb; kc += kWave) {
         const int k = kc + lane;
         const int kend = k < kb ? sCnt[k] : 0;
         const int kbeg = (k < kb && k > 0) ? sCnt[k - 1] : 0;
         const bool some = kend > kbeg;
-        const int kpix = some ? sSort[kbeg].x : 0;
-        uint64_t todo = __ballot(some);
-        if (!todo) continue;
-        int i = (int)__builtin_ctzll(todo);
-        int nb = __builtin_amdgcn_readlane(kbeg, i), ne = __builtin_amdgcn_readlane(kend, i);
-        int2 en[kBRedG];
-#pragma unroll
-        for (int t = 0; t < kBRedG; ++t) en[t] = sSort[min(nb + 4 * t + grp, ne - 1)];
-        for (;;) {
-          const int beg = nb, end = ne, v = __builtin_amdgcn_readlane(kpix, i);
-          int2 e[kBRedG];
-#pragma unroll
-          for (int t = 0; t < kBRedG; ++t) e[t] = en[t];
-          todo &= todo - 1;
-          if (todo) {
-            i = (int)__builtin_ctzll(todo);
-            nb = __builtin_amdgcn_readlane(kbeg, i);
-            ne = __builtin_amdgcn_readlane(kend, i);
-#pragma unroll
-            for (int t = 0; t < kBRedG; ++t) en[t] = sSort[min(nb + 4 * t + grp, ne - 1)];
-          }
-          const int cnt = end - beg;
+        const uint64_t todo = __ballot(some);
+        const int nz = (int)__popcll(todo);
+        if (nz == 0) continue;
+        // lane j < nz holds the entry range of the j-th non-empty key (lanes with none write lane 63, which
+        // is only read when all 64 keys are non-empty, and then no lane writes there but its own key's)
+        const int dst = 4 * (some ? rank_below(todo) : kWave - 1);
+        const int cbeg = __builtin_amdgcn_ds_permute(dst, kbeg);
+        const int cend = __builtin_amdgcn_ds_permute(dst, kend);
+        for (int s = 0; s < nz; s += 4) {
+          // (the lane permutes run with every lane active: a lane permute reads 0 from an inactive lane)
+          const int j = s + grp;
+          const bool live = j < nz;
+          const int jb = __builtin_amdgcn_ds_bpermute(4 * j, cbeg), je = __builtin_amdgcn_ds_bpermute(4 * j, cend);
+          const int beg = live ? jb : 0;
+          const int cnt = live ? je - jb : 0;
           float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          for (int u0 = 0;;) {
-            float4 gv[kBRedG];
+          int v = 0;
+          for (int u0 = 0; __ballot(u0 < cnt) != 0; u0 += 4) {
+            int2 e[4];
 #pragma unroll
-            for (int t = 0; t < kBRedG; ++t) gv[t] = *reinterpret_cast<const float4*>(gq + ((e[t].x >> 22) & 63) * kBgLd);
+            for (int t = 0; t < 4; ++t) e[t] = sSort[beg + max(min(u0 + t, cnt - 1), 0)];
+            if (u0 == 0) v = e[0].x;
+            float4 gv[4];
 #pragma unroll
-            for (int t = 0; t < kBRedG; ++t) {
-              const float w = (u0 + 4 * t + grp < cnt) ? __int_as_float(e[t].y) : 0.f;
+            for (int t = 0; t < 4; ++t) gv[t] = *reinterpret_cast<const float4*>(gq + ((e[t].x >> 22) & 63) * kBgLd);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float w = (u0 + t < cnt) ? __int_as_float(e[t].y) : 0.f;
               acc.x = fmaf(w, gv[t].x, acc.x);
               acc.y = fmaf(w, gv[t].y, acc.y);
               acc.z = fmaf(w, gv[t].z, acc.z);
               acc.w = fmaf(w, gv[t].w, acc.w);
             }
-            u0 += 4 * kBRedG;
-            if (u0 >= cnt) break;
-#pragma unroll
-            for (int t = 0; t < kBRedG; ++t) e[t] = sSort[min(beg + u0 + 4 * t + grp, end - 1)];
           }
-          const float sum = swap16_add(swap32_add(acc.x, acc.y), swap32_add(acc.z, acc.w));
-          const size_t pix = (size_t)((v >> 16) & 63) * p.P + (size_t)((v >> 8) & 0xff) * p.W + (v & 0xff);
-          if (lane < a.Cg) unsafeAtomicAdd(db + pix * p.C + lane, sum);
-          if (!todo) break;
+          if (cnt > 0) {
+            const size_t pix = (size_t)((v >> 16) & 63) * p.P + (size_t)((v >> 8) & 0xff) * p.W + (v & 0xff);
+            float* d = db + pix * p.C + q;
+            if (q < a.Cg) unsafeAtomicAdd(d, acc.x);
+            if (q + 16 < a.Cg) unsafeAtomicAdd(d + 16, acc.z);
+            if (q + 32 < a.Cg) unsafeAtomicAdd(d + 32, acc.y);
+            if (q + 48 < a.Cg) unsafeAtomicAdd(d + 48, acc.w);
+          }
         }
       }
     }
