@@ -714,18 +714,26 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
   int2* sSort = reinterpret_cast<int2*>(smem + lay.sort);
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = uniform(threadIdx.x / kWave);
-  if (threadIdx.x == 0) {
-    int base = 0;
-    for (int n = 0; n < NL; ++n) {
-      const int x_lo = sBox[4 * n], x_hi = sBox[4 * n + 1], y_lo = sBox[4 * n + 2], y_hi = sBox[4 * n + 3];
-      const bool used = x_lo <= x_hi;
-      sWin[4 * n] = base;
-      sWin[4 * n + 1] = x_lo;
-      sWin[4 * n + 2] = y_lo;
-      sWin[4 * n + 3] = used ? x_hi - x_lo + 1 : 0;
-      if (used) base += (x_hi - x_lo + 1) * (y_hi - y_lo + 1);
+  // the windows: lane n of wave 0 takes camera n's box, a wave scan places the windows one after another
+  if (wid == 0) {
+    int sz = 0, x_lo = 0, y_lo = 0, wdt = 0;
+    if (lane < NL) {
+      x_lo = sBox[4 * lane];
+      y_lo = sBox[4 * lane + 2];
+      const int x_hi = sBox[4 * lane + 1], y_hi = sBox[4 * lane + 3];
+      if (x_lo <= x_hi) {
+        wdt = x_hi - x_lo + 1;
+        sz = wdt * (y_hi - y_lo + 1);
+      }
     }
-    sMisc[1] = base;
+    const int incl = wave_scan_incl(sz);
+    if (lane < NL) {
+      sWin[4 * lane] = incl - sz;
+      sWin[4 * lane + 1] = x_lo;
+      sWin[4 * lane + 2] = y_lo;
+      sWin[4 * lane + 3] = wdt;
+    }
+    if (lane == kWave - 1) sMisc[1] = incl;
   }
   __syncthreads();
   const int nkeys = sMisc[1], nent = sMisc[0];
@@ -816,24 +824,36 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
           const int jb = __builtin_amdgcn_ds_bpermute(4 * j, cbeg), je = __builtin_amdgcn_ds_bpermute(4 * j, cend);
           const int beg = live ? jb : 0;
           const int cnt = live ? je - jb : 0;
+          const int last = max(cnt - 1, 0);
+          // entries 4 at a time; the next four are read while the current ones' grad rows are summed
+          int2 e[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) e[t] = sSort[beg + min(t, last)];
+          const int v = e[0].x;
           float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          int v = 0;
-          for (int u0 = 0; __ballot(u0 < cnt) != 0; u0 += 4) {
-            int2 e[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) e[t] = sSort[beg + max(min(u0 + t, cnt - 1), 0)];
-            if (u0 == 0) v = e[0].x;
+          for (int u0 = 0;;) {
             float4 gv[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) gv[t] = *reinterpret_cast<const float4*>(gq + ((e[t].x >> 22) & 63) * kBgLd);
+            float w[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const float w = (u0 + t < cnt) ? __int_as_float(e[t].y) : 0.f;
-              acc.x = fmaf(w, gv[t].x, acc.x);
-              acc.y = fmaf(w, gv[t].y, acc.y);
-              acc.z = fmaf(w, gv[t].z, acc.z);
-              acc.w = fmaf(w, gv[t].w, acc.w);
+              gv[t] = *reinterpret_cast<const float4*>(gq + ((e[t].x >> 22) & 63) * kBgLd);
+              w[t] = (u0 + t < cnt) ? __int_as_float(e[t].y) : 0.f;
             }
+            // (read unconditionally, so that the waits for this step's grad rows need not cover them)
+            const int un = u0 + 4;
+            const bool more = __ballot(un < cnt) != 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) e[t] = sSort[beg + min(un + t, last)];
+            __builtin_amdgcn_sched_barrier(0);        // keep those reads ahead of the sums
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              acc.x = fmaf(w[t], gv[t].x, acc.x);
+              acc.y = fmaf(w[t], gv[t].y, acc.y);
+              acc.z = fmaf(w[t], gv[t].z, acc.z);
+              acc.w = fmaf(w[t], gv[t].w, acc.w);
+            }
+            if (!more) break;
+            u0 = un;
           }
           if (cnt > 0) {
             const size_t pix = (size_t)((v >> 16) & 63) * p.P + (size_t)((v >> 8) & 0xff) * p.W + (v & 0xff);
