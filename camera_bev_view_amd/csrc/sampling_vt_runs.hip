@@ -321,7 +321,8 @@ __device__ void emit_round(const int* sRun, const int* sStart, int npair, int N,
 // of the same run (same cell and camera, consecutive bins) merged: a row is kept by the first sample of the
 // run that has it, which adds the weights of the following samples for as long as each of them has the row.
 // On return tp holds the lane's (merged) taps, keep_top / keep_bot say which rows it keeps; sTap has been
-// read by every lane (the caller may overwrite it after a wave sync).
+// read by every lane (the caller may overwrite it after a wave sync).  The raw taps sit in sTap's space as
+// offsets [4][kRound] then weights [4][kRound], so that lanes write and read consecutive words.
 struct Sample {
   int cl, n, xy;              // cell of the wave, virtual camera (n L + level), top-left tap pixel (x | y << 16)
   bool keep_top, keep_bot;
@@ -332,6 +333,8 @@ template <bool ML>
 __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const CellSet& cs, const int* sRun,
                                 const int* sDesc, Rec* sTap, int nsmp, int pix_bytes, int lane) {
   const int N = p.N, L = ML ? p.L : 1, NL = p.N * L;
+  int* rOff = reinterpret_cast<int*>(sTap);
+  float* rW = reinterpret_cast<float*>(sTap) + 4 * kRound;
   Sample sm;
   sm.cl = -1;
   sm.n = 0;
@@ -360,7 +363,10 @@ __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const Cell
       sample_taps(sCam[n], px, py, pz, rc, p.H, p.W, n * p.P, pix_bytes, sm.tp, top, bot, sm.xy);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sTap[4 * lane + t] = sm.tp[t];
+    for (int t = 0; t < 4; ++t) {
+      rOff[t * kRound + lane] = sm.tp[t].off;
+      rW[t * kRound + lane] = sm.tp[t].w;
+    }
     sm.cl = cl;
     sm.n = vn;
   }
@@ -379,20 +385,20 @@ __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const Cell
     for (int j = lane + 1; j < nsmp; ++j) {
       const int dj = sDesc[j];
       if ((dj >> 16) != run_id) break;
-      const Rec j0 = sTap[4 * j], j2 = sTap[4 * j + 2];
+      const Rec j0{rOff[j], rW[j]}, j2{rOff[2 * kRound + j], rW[2 * kRound + j]};
       const int jt = j0.off, jb = (j2.off != j0.off) ? j2.off : -1;
       const bool more_t = ltop == j && (jt == tp[0].off || jb == tp[0].off);
       const bool more_b = lbot == j && (jt == tp[2].off || jb == tp[2].off);
       if (more_t) {
         const bool from_top = jt == tp[0].off;
         tp[0].w += from_top ? j0.w : j2.w;
-        tp[1].w += from_top ? sTap[4 * j + 1].w : sTap[4 * j + 3].w;
+        tp[1].w += from_top ? rW[kRound + j] : rW[3 * kRound + j];
         ltop = j + 1;
       }
       if (more_b) {
         const bool from_top = jt == tp[2].off;
         tp[2].w += from_top ? j0.w : j2.w;
-        tp[3].w += from_top ? sTap[4 * j + 1].w : sTap[4 * j + 3].w;
+        tp[3].w += from_top ? rW[kRound + j] : rW[3 * kRound + j];
         lbot = j + 1;
       }
       if (!more_t && !more_b) break;
