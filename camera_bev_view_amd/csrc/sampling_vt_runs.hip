@@ -320,7 +320,9 @@ __device__ void emit_round(const int* sRun, const int* sStart, int npair, int N,
 // (Rec offsets = pixel index * pix_bytes) with weights / count, then rows shared with the neighbouring samples
 // of the same run (same cell and camera, consecutive bins) merged: a row is kept by the first sample of the
 // run that has it, which adds the weights of the following samples for as long as each of them has the row.
-// On return tp holds the lane's (merged) taps, keep_top / keep_bot say which rows it keeps.
+// On return tp holds the lane's (merged) taps, keep_top / keep_bot say which rows it keeps; sTap has been
+// read by every lane (the caller may overwrite it after a wave sync).  The raw taps sit in sTap's space as
+// offsets [4][kRound] then weights [4][kRound], so that lanes write and read consecutive words.
 struct Sample {
   int cl, n, xy;              // cell of the wave, virtual camera (n L + level), top-left tap pixel (x | y << 16)
   bool keep_top, keep_bot;
@@ -329,14 +331,14 @@ struct Sample {
 
 template <bool ML>
 __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const CellSet& cs, const int* sRun,
-                                const int* sDesc, int nsmp, int pix_bytes, int lane) {
+                                const int* sDesc, Rec* sTap, int nsmp, int pix_bytes, int lane) {
   const int N = p.N, L = ML ? p.L : 1, NL = p.N * L;
+  int* rOff = reinterpret_cast<int*>(sTap);
+  float* rW = reinterpret_cast<float*>(sTap) + 4 * kRound;
   Sample sm;
   sm.cl = -1;
   sm.n = 0;
   sm.xy = 0;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) sm.tp[t] = Rec{-1, 0.f};
   int dsc = 0, top = -1, bot = -1;
   if (lane < nsmp) {
     dsc = sDesc[lane];
@@ -360,6 +362,11 @@ __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const Cell
     } else {
       sample_taps(sCam[n], px, py, pz, rc, p.H, p.W, n * p.P, pix_bytes, sm.tp, top, bot, sm.xy);
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      rOff[t * kRound + lane] = sm.tp[t].off;
+      rW[t * kRound + lane] = sm.tp[t].w;
+    }
     sm.cl = cl;
     sm.n = vn;
   }
@@ -371,35 +378,30 @@ __device__ Sample round_samples(const CamRec* sCam, const Problem& p, const Cell
     keep_top = keep_top && top != prev_top && top != prev_bot;
     keep_bot = keep_bot && bot != prev_top && bot != prev_bot;
   }
-  // Row merging with the raw taps of the following lanes, shifted one lane per step (lane + d's values
-  // at step d): a kept row takes the weights of sample lane + d as long as every sample up to it has
-  // that row.  Every lane takes part in the shifts.
-  {
+  wave_lds_sync();
+  if (keep_top || keep_bot) {
     Rec* tp = sm.tp;
-    const int own_t = tp[0].off, own_b = tp[2].off;
-    int s_run = run_id, s_o0 = tp[0].off, s_o2 = tp[2].off;
-    float s_w[4] = {tp[0].w, tp[1].w, tp[2].w, tp[3].w};
-    bool act_t = keep_top, act_b = keep_bot;
-    for (int d = 1; __ballot(act_t || act_b) != 0; ++d) {
-      s_run = lane_next(s_run, -1);
-      s_o0 = lane_next(s_o0, -1);
-      s_o2 = lane_next(s_o2, -1);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) s_w[t] = __int_as_float(lane_next(__float_as_int(s_w[t]), 0));
-      const bool valid = lane + d < nsmp && s_run == run_id;
-      const int jt = s_o0, jb = (s_o2 != s_o0) ? s_o2 : -1;
-      act_t = act_t && valid && (jt == own_t || jb == own_t);
-      act_b = act_b && valid && (jt == own_b || jb == own_b);
-      if (act_t) {
-        const bool from_top = jt == own_t;
-        tp[0].w += from_top ? s_w[0] : s_w[2];
-        tp[1].w += from_top ? s_w[1] : s_w[3];
+    int ltop = keep_top ? lane + 1 : nsmp, lbot = keep_bot ? lane + 1 : nsmp;
+    for (int j = lane + 1; j < nsmp; ++j) {
+      const int dj = sDesc[j];
+      if ((dj >> 16) != run_id) break;
+      const Rec j0{rOff[j], rW[j]}, j2{rOff[2 * kRound + j], rW[2 * kRound + j]};
+      const int jt = j0.off, jb = (j2.off != j0.off) ? j2.off : -1;
+      const bool more_t = ltop == j && (jt == tp[0].off || jb == tp[0].off);
+      const bool more_b = lbot == j && (jt == tp[2].off || jb == tp[2].off);
+      if (more_t) {
+        const bool from_top = jt == tp[0].off;
+        tp[0].w += from_top ? j0.w : j2.w;
+        tp[1].w += from_top ? rW[kRound + j] : rW[3 * kRound + j];
+        ltop = j + 1;
       }
-      if (act_b) {
-        const bool from_top = jt == own_b;
-        tp[2].w += from_top ? s_w[0] : s_w[2];
-        tp[3].w += from_top ? s_w[1] : s_w[3];
+      if (more_b) {
+        const bool from_top = jt == tp[2].off;
+        tp[2].w += from_top ? j0.w : j2.w;
+        tp[3].w += from_top ? rW[kRound + j] : rW[3 * kRound + j];
+        lbot = j + 1;
       }
+      if (!more_t && !more_b) break;
     }
   }
   sm.keep_top = keep_top;
@@ -500,7 +502,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   unsigned char* wbase = cur + (wave_lds_bytes(NL, S) + out_tile_bytes(a.Cg)) * wid;
   float* sOut = reinterpret_cast<float*>(wbase + wave_lds_bytes(NL, S));  // [Cg][kOutLd] this wave's cells
-  Rec* sTap = reinterpret_cast<Rec*>(wbase);                        // [tap_slots(S)] the round's kept taps by step
+  Rec* sTap = reinterpret_cast<Rec*>(wbase);                        // [tap_slots(S)] raw, then kept taps by step
   int* sDesc = reinterpret_cast<int*>(sTap + tap_slots(S));         // [kRound] the round's samples
   int* sCellLo = sDesc + kRound;                                    // [kCpw] first kept tap of the cell in the round
   int* sCellHi = sCellLo + kCpw;                                    // [kCpw] end | complete << 30, or -1
@@ -556,7 +558,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
     if (lane < kCpw) sCellHi[lane] = -1;
     wave_lds_sync();
     // ---- phase B: lane = sample; taps, count, row merging
-    const Sample sm = round_samples<ML>(sCam, p, cs, sRun, sDesc, nsmp, pix_bytes, lane);
+    const Sample sm = round_samples<ML>(sCam, p, cs, sRun, sDesc, sTap, nsmp, pix_bytes, lane);
     const bool keep_top = sm.keep_top, keep_bot = sm.keep_bot;
     const int cl = sm.cl;
     const Rec* tp = sm.tp;
@@ -567,6 +569,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
     const int next_cl = lane_next(cl, -1), prev_cl = lane_prev(cl, -1);   // every lane takes part
     const bool cell_first = lane < nsmp && (lane == 0 || prev_cl != cl);
     const bool cell_last = lane < nsmp && (lane == nsmp - 1 || next_cl != cl);
+    wave_lds_sync();                                   // every lane has read the raw taps
     if (keep_top) {
       sTap[pos] = tp[0];
       sTap[pos + 1] = tp[1];
@@ -668,7 +671,9 @@ __device__ __forceinline__ int ent_pack(int x, int y, int n, int cell) { return 
 struct BwdLds {
   size_t cam, g, box, win, misc, cnt, ent, sort, runs, total;
 };
-__host__ __device__ inline size_t bwd_round_bytes() { return sizeof(int) * kRound; }
+__host__ __device__ inline size_t bwd_round_bytes() {
+  return (sizeof(Rec) * 4 * kRound + sizeof(int) * kRound + 15) & ~(size_t)15;
+}
 __host__ __device__ inline BwdLds bwd_lds(int N, int NL, int max_ent, int max_keys) {
   BwdLds l;
   size_t o = 0;
@@ -892,7 +897,8 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
   int2* sEnt = reinterpret_cast<int2*>(smem + lay.ent);
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = uniform(threadIdx.x / kWave);
-  int* sDesc = reinterpret_cast<int*>(smem + lay.sort + bwd_round_bytes() * wid);   // [kRound] the round's samples
+  Rec* sTap = reinterpret_cast<Rec*>(smem + lay.sort + bwd_round_bytes() * wid);
+  int* sDesc = reinterpret_cast<int*>(sTap + 4 * kRound);
   const int npair = kBCpw * NL;
   int* sRun = reinterpret_cast<int*>(smem + lay.runs) + (2 * npair + 1) * wid;
   int* sStart = sRun + npair;
@@ -940,7 +946,7 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
       const int nsmp = min(kRound, total - r0);
       emit_round(sRun, sStart, npair, NL, r0, sDesc, lane);
       wave_lds_sync();
-      const Sample sm = round_samples<false>(sCam, p, cs, sRun, sDesc, nsmp, 1, lane);
+      const Sample sm = round_samples<false>(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
       const int x0 = sm.xy & 0xffff, y0 = sm.xy >> 16;
       const int x1 = min(x0 + 1, p.W - 1), y1 = min(y0 + 1, p.H - 1);
       // each camera's pixel box grows by its samples' taps: a wave reduction per camera present
