@@ -8,8 +8,8 @@ For one bench workload, given the databases (``run_results.db``) of a kernel-tra
     for the bench's calibration copy of a known size) and its median SQ_INSTS_VALU, together with the
     sha256 of the sources the counters were taken on (``bench.py`` ignores a record whose sources
     changed since);
-  * writes ``profiles/sampling_vt_<key>.md``: the kernel-trace table, the traffic table and the
-    instruction counts, with the commands that produced them.
+  * writes ``profiles/<prefix>_<key>.md`` (prefix ``sampling_vt`` by default): the kernel-trace table,
+    the traffic table and the instruction counts, with the commands that produced them.
 
 Usage (from the repository root, after the rocprofv3 runs):
 
@@ -31,7 +31,7 @@ from typing import Dict, List
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
-# the files whose contents decide the launched kernels of the Sampling-VT passes
+# the files whose contents decide the launched kernels of the Sampling-VT passes (the default --sources)
 SOURCES = ("camera_bev_view_amd/csrc/sampling_vt.hip", "camera_bev_view_amd/csrc/sampling_vt_runs.hip",
            "camera_bev_view_amd/csrc/wave_ops.h", "camera_bev_view_amd/csrc/bev_align.h",
            "camera_bev_view_amd/csrc/kernels.h", "camera_bev_view_amd/csrc/flashbev_api.cpp")
@@ -104,6 +104,10 @@ def main(argv=None) -> None:
     ap.add_argument("--calib-mib", type=int, default=256)
     ap.add_argument("--command", action="append", default=[], help="a command that produced the inputs")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--prefix", default="sampling_vt", help="summary file name prefix (kernel family)")
+    ap.add_argument("--sources", default=",".join(SOURCES),
+                    help="comma-separated files (from the repository root) that decide the recorded kernels")
+    ap.add_argument("--family", default="Sampling-VT", help="kernel family named in the summary's heading")
     ap.add_argument("--record", default=RECORD, help="the JSON record to merge into")
     a = ap.parse_args(argv)
 
@@ -131,7 +135,7 @@ def main(argv=None) -> None:
                        "for the bench's elementwise calibration copy (--calib-copy-mib) in the same run, and the "
                        "median SQ_INSTS_VALU; written by camera_bev_view_amd/profile_record.py")
     record.setdefault("workloads", {})[a.key] = {
-        "sources": {s: sha(s) for s in SOURCES},
+        "sources": {s: sha(s) for s in a.sources.split(",") if s},
         "commands": a.command,
         "calibration": {"copy_kernel": cal_k, "copy_bytes": a.calib_mib << 20, "fetch_kib_read": cal_f,
                         "write_kib_read": cal_w, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
@@ -143,7 +147,7 @@ def main(argv=None) -> None:
 
     tr = trace(a.trace)
     total = sum(sum(v) for v in tr.values())
-    lines = [f"# Sampling-VT kernels, {a.key}: rocprofv3 kernel trace and counters (MI355X)", "", a.title, "",
+    lines = [f"# {a.family} kernels, {a.key}: rocprofv3 kernel trace and counters (MI355X)", "", a.title, "",
              "Commands (from the repository root; `<out>` is a scratch directory):", ""]
     lines += [f"    {c}" for c in a.command]
     lines += ["", "## Kernel trace", "", "| kernel | calls | average (us) | min (us) | max (us) | share |",
@@ -160,7 +164,7 @@ def main(argv=None) -> None:
                      f"{r['write_bytes']:,} | {r['bytes_per_launch']:,} | {r.get('valu_insts', 0):,} | "
                      f"{r.get('waves', 0):,} |")
     lines.append("")
-    path = os.path.join(a.out, f"sampling_vt_{a.key}.md")
+    path = os.path.join(a.out, f"{a.prefix}_{a.key}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
     print(f"wrote {path} and {a.record}")
