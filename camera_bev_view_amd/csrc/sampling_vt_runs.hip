@@ -693,19 +693,6 @@ __host__ __device__ inline BwdLds bwd_lds(int N, int NL, int max_ent, int max_ke
   return l;
 }
 
-// Minimum and maximum over the lanes of the wave (every lane gets them).
-__device__ __forceinline__ int wave_min(int v) {
-  v = min(v, dpp_or<kQuadSwap1>(v, v));
-  v = min(v, dpp_or<kQuadSwap2>(v, v));
-  v = min(v, dpp_or<kHalfMirror>(v, v));
-  v = min(v, dpp_or<kRowMirror>(v, v));
-  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-  v = min((int)r[0], (int)r[1]);
-  auto r2 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-  return min((int)r2[0], (int)r2[1]);
-}
-__device__ __forceinline__ int wave_max(int v) { return -wave_min(-v); }
-
 // Sort the block's entries by pixel and add each pixel's sums to dF (one counting pass per window of
 // max_keys keys).  Called by the whole workgroup; ends with the entries and camera boxes cleared.
 __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds& lay, int b) {
@@ -949,20 +936,17 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
       const Sample sm = round_samples<false>(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
       const int x0 = sm.xy & 0xffff, y0 = sm.xy >> 16;
       const int x1 = min(x0 + 1, p.W - 1), y1 = min(y0 + 1, p.H - 1);
-      // each camera's pixel box grows by its samples' taps: a wave reduction per camera present
-      uint64_t pend = __ballot(lane < nsmp);
-      while (pend) {
-        const int cam = __builtin_amdgcn_readlane(sm.n, (int)__builtin_ctzll(pend));
-        const bool mine = lane < nsmp && sm.n == cam;
-        pend &= ~__ballot(mine);
-        const int xa = wave_min(mine ? x0 : 0x7fffffff), xb = wave_max(mine ? x1 : -1);
-        const int ya = wave_min(mine ? y0 : 0x7fffffff), yb = wave_max(mine ? y1 : -1);
-        if (lane == 0) {
-          atomicMin(&sBox[4 * cam], xa);
-          atomicMax(&sBox[4 * cam + 1], xb);
-          atomicMin(&sBox[4 * cam + 2], ya);
-          atomicMax(&sBox[4 * cam + 3], yb);
-        }
+      // each camera's pixel box grows by its samples' taps.  Along a run (one cell and camera, consecutive
+      // bins, all in front of the camera) the projected u and v are monotone in the bin, so the run's taps lie
+      // between those of its first and last samples: only the round's first and last sample of each run update
+      // the box, by integer LDS atomics
+      const int rid = sm.cl * 64 + sm.n;
+      const int prev_rid = lane_prev(rid, -1), next_rid = lane_next(rid, -1);   // every lane takes part
+      if (lane < nsmp && (lane == 0 || lane == nsmp - 1 || prev_rid != rid || next_rid != rid)) {
+        atomicMin(&sBox[4 * sm.n], x0);
+        atomicMax(&sBox[4 * sm.n + 1], x1);
+        atomicMin(&sBox[4 * sm.n + 2], y0);
+        atomicMax(&sBox[4 * sm.n + 3], y1);
       }
       const uint64_t mt = __ballot(sm.keep_top), mb = __ballot(sm.keep_bot);
       const int nk = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
