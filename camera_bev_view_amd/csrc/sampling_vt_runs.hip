@@ -868,7 +868,11 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
     sBox[4 * e + 2] = 0x7fffffff;
     sBox[4 * e + 3] = -1;
   }
-  if (threadIdx.x == 0) sMisc[0] = 0;
+  if (threadIdx.x == 0) {
+    sMisc[0] = 0;
+    sMisc[2] = 0x7fffffff;
+    sMisc[3] = 0;
+  }
   __syncthreads();
 }
 
@@ -919,7 +923,11 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
     sBox[4 * e + 2] = 0x7fffffff;
     sBox[4 * e + 3] = -1;
   }
-  if (threadIdx.x == 0) sMisc[0] = 0;
+  if (threadIdx.x == 0) {
+    sMisc[0] = 0;                    // entries reserved
+    sMisc[2] = 0x7fffffff;           // first reservation that did not fit
+    sMisc[3] = 0;                    // some wave stopped for want of room
+  }
   stage_cameras(sCam, p, b);
   // this wave's cells: x-row wid of the block, 8 cells; the waves go on without waiting for each other,
   // and the gradient tile stays in registers (its loads in flight) until the first flush needs it
@@ -927,13 +935,29 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
   const int total = wave_runs<false>(sCam, p, cs, sRun, sStart, lane);
   bool g_staged = false;
 
+  // The waves list their rounds without waiting for each other, each reserving room for a round's entries
+  // with one LDS atomic; a round that does not fit stops its wave (it is listed again after the flush), and
+  // every reservation after it fails too, so the entries written are those below the first failed one.  The
+  // workgroup flushes when every wave has stopped or finished.
   int r0 = 0;
   for (;;) {
-    if (r0 < total) {
+    while (r0 < total) {
       const int nsmp = min(kRound, total - r0);
       emit_round(sRun, sStart, npair, NL, r0, sDesc, lane);
       wave_lds_sync();
       const Sample sm = round_samples<false>(sCam, p, cs, sRun, sDesc, sTap, nsmp, 1, lane);
+      const uint64_t mt = __ballot(sm.keep_top), mb = __ballot(sm.keep_bot);
+      const int nk = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sMisc[0], nk);
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (base + nk > a.max_ent) {
+        if (lane == 0) {
+          atomicMin(&sMisc[2], base);
+          sMisc[3] = 1;
+        }
+        break;
+      }
       const int x0 = sm.xy & 0xffff, y0 = sm.xy >> 16;
       const int x1 = min(x0 + 1, p.W - 1), y1 = min(y0 + 1, p.H - 1);
       // each camera's pixel box grows by its samples' taps.  Along a run (one cell and camera, consecutive
@@ -948,11 +972,6 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
         atomicMin(&sBox[4 * sm.n + 2], y0);
         atomicMax(&sBox[4 * sm.n + 3], y1);
       }
-      const uint64_t mt = __ballot(sm.keep_top), mb = __ballot(sm.keep_bot);
-      const int nk = 2 * ((int)__popcll(mt) + (int)__popcll(mb));
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&sMisc[0], nk);
-      base = __builtin_amdgcn_readfirstlane(base);
       const int pos = base + 2 * (rank_below(mt) + rank_below(mb));
       const int cell = wid * kBCpw + sm.cl;
       // the taps' pixels: top row (x0, y0), (x1, y0); bottom row one image row down
@@ -967,30 +986,26 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
       }
       r0 += kRound;
     }
-    // each wave's next round adds at most 4 entries per sample
-    if (lane == 0) sMisc[8 + wid] = 4 * max(min(kRound, total - r0), 0);
     __syncthreads();
-    int next = 0;
+    const bool again = sMisc[3] != 0;
+    const int nent = min(sMisc[0], sMisc[2]);
+    if (nent == 0 && !again) break;
+    __syncthreads();                 // every wave has read the flags before the entry count changes
+    if (threadIdx.x == 0) sMisc[0] = nent;
+    if (!g_staged) {
 #pragma unroll
-    for (int w = 0; w < kBWaves; ++w) next += sMisc[8 + w];
-    const int nent = sMisc[0];
-    __syncthreads();                 // every wave has read the counts before any changes them
-    if (next == 0 || nent + next > a.max_ent) {
-      if (!g_staged) {
-#pragma unroll
-        for (int i = 0; i < kGPer; ++i) {
-          const int e = threadIdx.x + i * kBThreads;
-          const int c = e / kBCells, cl = e - c * kBCells;
-          // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3): where the per-pixel
-          // reduce-scatter leaves channel c in lane c (the flush's barriers publish these stores)
-          const int q = c & 15, r = c >> 4;
-          sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
-        }
-        g_staged = true;
+      for (int i = 0; i < kGPer; ++i) {
+        const int e = threadIdx.x + i * kBThreads;
+        const int c = e / kBCells, cl = e - c * kBCells;
+        // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3), so that a lane's 16-byte read
+        // holds channels q, q + 32, q + 16, q + 48 (the flush's barriers publish these stores)
+        const int q = c & 15, r = c >> 4;
+        sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
       }
-      bwd_flush(a, smem, lay, b);
+      g_staged = true;
     }
-    if (next == 0) break;
+    bwd_flush(a, smem, lay, b);
+    if (!again) break;
   }
 }
 
@@ -1107,7 +1122,7 @@ hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* 
   a.dF = grad_feat;
   a.tiles_x = (p.X + kBTileX - 1) / kBTileX;
   a.tiles_y = (p.Y + kBTileY - 1) / kBTileY;
-  a.max_ent = 3072;                     // at least one round of every wave
+  a.max_ent = 3072;                     // entries held before a flush (at least one round of a wave)
   a.max_keys = 2048;
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
