@@ -634,7 +634,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
 
 // ---------------------------------------------------------------------------------------------------
 // Backward (gradient with respect to the features; the map is linear in them).  One workgroup = an
-// 8 x 8 block of cells and a group of up to 64 channels, eight waves, one x-row of 8 cells each.  The
+// 8 x 8 block of cells and all channels (in groups of 64), eight waves, one x-row of 8 cells each.  The
 // waves list their samples exactly as the forward does (runs, taps, merged rows), and every kept tap
 // becomes an entry (pixel, cell, weight) of the workgroup.  A counting sort by pixel in LDS then makes
 // every pixel's entries contiguous: the keys are a window per camera (the bounding box of the pixels
@@ -658,7 +658,6 @@ struct BwdRunArgs {
   Problem p;
   const float* grad;     // [B, out_ch, X, Y]
   float* dF;             // [B, N, P, C], zero-filled; atomically accumulated
-  int c_lo, Cg;          // channel group
   int tiles_x, tiles_y;
   int max_ent;           // entries held before a flush
   int max_keys;          // window counters per counting pass
@@ -693,12 +692,48 @@ __host__ __device__ inline BwdLds bwd_lds(int N, int NL, int max_ent, int max_ke
   return l;
 }
 
+constexpr int kGPer = kBCells * kBCg / kBThreads;     // upstream-gradient tile values per thread
+
+// Thread t's share of the block's upstream-gradient tile for channels [c_lo, c_lo + Cg): value i is channel
+// c = e / kBCells of cell e mod kBCells, e = t + i kBThreads (zero past the group or the grid).
+__device__ __forceinline__ void load_g_tile(const BwdRunArgs& a, int b, int x_tile, int y_tile, int c_lo, int Cg,
+                                            float (&v)[kGPer]) {
+  const Problem& p = a.p;
+  const size_t c_stride = (size_t)p.X * p.Y;
+  const float* gb = a.grad + ((size_t)b * p.out_ch + c_lo) * c_stride;
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int e = threadIdx.x + i * kBThreads;
+    const int c = e / kBCells, cl = e - c * kBCells;
+    const int xx = x_tile + cl / kBTileY, yy = y_tile + cl % kBTileY;
+    v[i] = (c < Cg && xx < p.X && yy < p.Y) ? __builtin_nontemporal_load(gb + c * c_stride + (size_t)xx * p.Y + yy)
+                                            : 0.f;
+  }
+}
+
+// Park a thread's share of a gradient tile in LDS.  Channel c = q + 16 r sits at 4 q + perm(r),
+// perm = (0, 2, 1, 3), so that a lane's 16-byte read holds channels q, q + 32, q + 16, q + 48.
+__device__ __forceinline__ void stage_g_tile(float* sG, const float (&v)[kGPer]) {
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int e = threadIdx.x + i * kBThreads;
+    const int c = e / kBCells, cl = e - c * kBCells;
+    const int q = c & 15, r = c >> 4;
+    sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = v[i];
+  }
+}
+
 // Sort the block's entries by pixel and add each pixel's sums to dF (one counting pass per window of
-// max_keys keys).  Called by the whole workgroup; ends with the entries and camera boxes cleared.
-__device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds& lay, int b) {
+// max_keys keys), for every 64-channel group in turn: the sorted entries serve all groups.  With one group
+// the caller has parked its gradient tile in LDS; with several, each group's tile is parked before its sums
+// (the first group's from g0, the next group's loads issued while the current group is summed).  Called by
+// the whole workgroup; ends with the entries and camera boxes cleared.
+template <bool MG>
+__device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds& lay, int b, int x_tile,
+                          int y_tile, const float (&g0)[kGPer]) {
   const Problem& p = a.p;
   const int N = p.N, NL = p.N;
-  const float* sG = reinterpret_cast<const float*>(smem + lay.g);
+  float* sG = reinterpret_cast<float*>(smem + lay.g);
   int* sBox = reinterpret_cast<int*>(smem + lay.box);
   int* sWin = reinterpret_cast<int*>(smem + lay.win);
   int* sMisc = reinterpret_cast<int*>(smem + lay.misc);
@@ -731,7 +766,8 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
   __syncthreads();
   const int nkeys = sMisc[1], nent = sMisc[0];
   const size_t batch_elems = (size_t)N * p.P * p.C;
-  float* db = a.dF + (size_t)b * batch_elems + a.c_lo;
+  float* db = a.dF + (size_t)b * batch_elems;
+  const int ngroups = MG ? (p.C + kBCg - 1) / kBCg : 1;
   for (int k0 = 0; k0 < nkeys; k0 += a.max_keys) {
     const int kn = min(a.max_keys, nkeys - k0);
     for (int k = threadIdx.x; k <= kn; k += kBThreads) sCnt[k] = 0;
@@ -793,7 +829,19 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
     // With the tile's channel order, lane q of a group holds channels q, q + 32, q + 16 and q + 48, so the
     // pixel leaves the workgroup as four fp32 atomics over 16 consecutive channels each.  A pixel costs its
     // own entries plus a share of one step, whatever the spread of entries over pixels.
-    {
+    float gn[kGPer];
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int c_lo = gi * kBCg, Cg = min(kBCg, p.C - c_lo);
+      if (MG) {
+        if (gi > 0) __syncthreads();               // the previous group's sums have read the tile
+        if (gi == 0) {
+          stage_g_tile(sG, g0);
+        } else {
+          stage_g_tile(sG, gn);
+        }
+        __syncthreads();
+      }
+      if (MG && gi + 1 < ngroups) load_g_tile(a, b, x_tile, y_tile, c_lo + kBCg, min(kBCg, p.C - c_lo - kBCg), gn);
       const int ka = sMisc[24 + wid], kb = wid + 1 < kBWaves ? sMisc[25 + wid] : kn;
       const int grp = lane >> 4, q = lane & 15;
       const float* gq = sG + 4 * q;
@@ -850,11 +898,11 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
           }
           if (cnt > 0) {
             const size_t pix = (size_t)((v >> 16) & 63) * p.P + (size_t)((v >> 8) & 0xff) * p.W + (v & 0xff);
-            float* d = db + pix * p.C + q;
-            if (q < a.Cg) unsafeAtomicAdd(d, acc.x);
-            if (q + 16 < a.Cg) unsafeAtomicAdd(d + 16, acc.z);
-            if (q + 32 < a.Cg) unsafeAtomicAdd(d + 32, acc.y);
-            if (q + 48 < a.Cg) unsafeAtomicAdd(d + 48, acc.w);
+            float* d = db + pix * p.C + c_lo + q;
+            if (q < Cg) unsafeAtomicAdd(d, acc.x);
+            if (q + 16 < Cg) unsafeAtomicAdd(d + 16, acc.z);
+            if (q + 32 < Cg) unsafeAtomicAdd(d + 32, acc.y);
+            if (q + 48 < Cg) unsafeAtomicAdd(d + 48, acc.w);
           }
         }
       }
@@ -876,13 +924,14 @@ __device__ void bwd_flush(const BwdRunArgs& a, unsigned char* smem, const BwdLds
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) {
+// MG: more than one 64-channel group.
+template <bool MG>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void sampling_vt_runs_bwd(BwdRunArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
   const int N = p.N, NL = p.N;                      // single level: the virtual cameras are the cameras
   const BwdLds lay = bwd_lds(N, NL, a.max_ent, a.max_keys);
   CamRec* sCam = reinterpret_cast<CamRec*>(smem + lay.cam);
-  float* sG = reinterpret_cast<float*>(smem + lay.g);
   int* sBox = reinterpret_cast<int*>(smem + lay.box);
   int* sMisc = reinterpret_cast<int*>(smem + lay.misc);
   int2* sEnt = reinterpret_cast<int2*>(smem + lay.ent);
@@ -901,21 +950,9 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
   const int b = r1 / a.tiles_x;
   const int x_tile = xt * kBTileX, y_tile = yt * kBTileY;
 
-  // upstream-gradient tile [cell][channel], loads issued before the camera table is staged
-  constexpr int kGPer = kBCells * kBCg / kBThreads;
+  // the first channel group's upstream-gradient tile, loads issued before the camera table is staged
   float gpre[kGPer];
-  {
-    const size_t c_stride = (size_t)p.X * p.Y;
-    const float* gb = a.grad + (((size_t)b * p.out_ch + a.c_lo) * p.X) * p.Y;
-#pragma unroll
-    for (int i = 0; i < kGPer; ++i) {
-      const int e = threadIdx.x + i * kBThreads;
-      const int c = e / kBCells, cl = e - c * kBCells;
-      const int xx = x_tile + cl / kBTileY, yy = y_tile + cl % kBTileY;
-      gpre[i] = (c < a.Cg && xx < p.X && yy < p.Y) ? __builtin_nontemporal_load(gb + c * c_stride + (size_t)xx * p.Y + yy)
-                                                   : 0.f;
-    }
-  }
+  load_g_tile(a, b, x_tile, y_tile, 0, min(kBCg, p.C), gpre);
   // boxes and the entry count start empty (visible after the camera staging's barrier)
   for (int e = threadIdx.x; e < NL; e += kBThreads) {
     sBox[4 * e] = 0x7fffffff;
@@ -992,19 +1029,12 @@ __global__ __launch_bounds__(kBThreads) void sampling_vt_runs_bwd(BwdRunArgs a) 
     if (nent == 0 && !again) break;
     __syncthreads();                 // every wave has read the flags before the entry count changes
     if (threadIdx.x == 0) sMisc[0] = nent;
-    if (!g_staged) {
-#pragma unroll
-      for (int i = 0; i < kGPer; ++i) {
-        const int e = threadIdx.x + i * kBThreads;
-        const int c = e / kBCells, cl = e - c * kBCells;
-        // channel c = q + 16 r sits at 4 q + perm(r), perm = (0, 2, 1, 3), so that a lane's 16-byte read
-        // holds channels q, q + 32, q + 16, q + 48 (the flush's barriers publish these stores)
-        const int q = c & 15, r = c >> 4;
-        sG[cl * kBgLd + 4 * q + ((r & 1) ? 2 : 0) + (r >> 1)] = gpre[i];
-      }
+    if (!MG && !g_staged) {
+      // one channel group: its tile is parked once, before the first flush (whose barriers publish it)
+      stage_g_tile(reinterpret_cast<float*>(smem + lay.g), gpre);
       g_staged = true;
     }
-    bwd_flush(a, smem, lay, b);
+    bwd_flush<MG>(a, smem, lay, b, x_tile, y_tile, gpre);
     if (!again) break;
   }
 }
@@ -1128,14 +1158,12 @@ hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* 
   if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
   if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
   const size_t shmem = bwd_lds(p.N, p.N, a.max_ent, a.max_keys).total;
-  for (int c = 0; c < p.C; c += kBCg) {
-    a.c_lo = c;
-    a.Cg = (p.C - c < kBCg) ? p.C - c : kBCg;
-    hipLaunchKernelGGL(sampling_vt_runs_bwd, dim3((unsigned)tiles), dim3(kBThreads), shmem, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  // one launch for all channels: the listing and the sort serve every 64-channel group
+  if (p.C > kBCg)
+    hipLaunchKernelGGL(sampling_vt_runs_bwd<true>, dim3((unsigned)tiles), dim3(kBThreads), shmem, stream, a);
+  else
+    hipLaunchKernelGGL(sampling_vt_runs_bwd<false>, dim3((unsigned)tiles), dim3(kBThreads), shmem, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace fbev
