@@ -190,6 +190,8 @@ struct RunArgs {
   uint8_t* counts;
   int c_lo;          // first channel of this launch's group
   int Cg;            // channels of the group
+  int ngroups;       // groups of Cg channels from c_lo taken by this launch in turn (the last one partial)
+  int C_launch;      // channels of this launch (Cg when ngroups == 1)
   int tiles_pb;      // tiles per sample: ceil(X * Y / kTileY)
   int write_counts;
 };
@@ -437,7 +439,7 @@ __device__ __forceinline__ void gather_steps(float* acc, const Rec* rec, __amdgp
 
 // A cell's accumulators, complete: sum the S slots and park the channels in column `ct` of the output tile;
 // the accumulators are cleared for the next cell.
-template <int L, int kVec>
+template <int L, int kVec, bool kAdd = false>
 __device__ __forceinline__ void flush_cell(float (&acc)[kVec], float* sOut, int ct, int lane, int Cg) {
   const int slot = lane / L, q = lane - slot * L;
   if constexpr (L == 16 && kVec % 4 == 0) {
@@ -449,7 +451,11 @@ __device__ __forceinline__ void flush_cell(float (&acc)[kVec], float* sOut, int 
       const float e23 = swap32_add(acc[i + 2], acc[i + 3]);
       const float s = swap16_add(e01, e23);
       const int ch = q * kVec + i + ((rrow & 1) ? 2 : 0) + (rrow >> 1);
-      sOut[ch * kOutLd + ct] = s;
+      if (kAdd) {
+        if (ch < Cg) sOut[ch * kOutLd + ct] += s;
+      } else {
+        sOut[ch * kOutLd + ct] = s;
+      }
     }
   } else {
 #pragma unroll
@@ -462,7 +468,12 @@ __device__ __forceinline__ void flush_cell(float (&acc)[kVec], float* sOut, int 
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
         const int ch = q * kVec + i;
-        if (ch < Cg) sOut[ch * kOutLd + ct] = acc[i];
+        if (ch < Cg) {
+          if (kAdd)
+            sOut[ch * kOutLd + ct] += acc[i];
+          else
+            sOut[ch * kOutLd + ct] = acc[i];
+        }
       }
     }
   }
@@ -483,8 +494,10 @@ struct RunWaves {
 };
 
 // Forward.  L lanes cover one tap's channel group with D dwords each (L * D * 4 == group bytes);
-// S = 64 / L taps per load instruction.
-template <int D, int L, bool BF16, bool ML>
+// S = 64 / L taps per load instruction.  MG: the launch takes a.ngroups groups of a.Cg channels in turn over
+// the same listed taps (the lanes past the last group's channels read nothing), each cell's sums added into
+// the output tile at the end of its taps in a round.
+template <int D, int L, bool BF16, bool ML, bool MG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
 void sampling_vt_runs_fwd(RunArgs a) {
   using Ln = Lane<D, BF16>;
@@ -500,7 +513,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
   unsigned char* cur = smem + sizeof(CamRec) * N;
   const int wid = uniform(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
-  unsigned char* wbase = cur + (wave_lds_bytes(NL, S) + out_tile_bytes(a.Cg)) * wid;
+  unsigned char* wbase = cur + (wave_lds_bytes(NL, S) + out_tile_bytes(a.C_launch)) * wid;
   float* sOut = reinterpret_cast<float*>(wbase + wave_lds_bytes(NL, S));  // [Cg][kOutLd] this wave's cells
   Rec* sTap = reinterpret_cast<Rec*>(wbase);                        // [tap_slots(S)] raw, then kept taps by step
   int* sDesc = reinterpret_cast<int*>(sTap + tap_slots(S));         // [kRound] the round's samples
@@ -518,7 +531,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
 
   stage_cameras(sCam, p, b);
 
-  for (int e = lane; e < a.Cg * kOutLd; e += kWave) sOut[e] = 0.f;     // cells with no sample stay 0
+  for (int e = lane; e < a.C_launch * kOutLd; e += kWave) sOut[e] = 0.f;   // cells with no sample stay 0
   const int ncell = (int)min((long long)kCpw, XY - f_wave);            // cells of this wave (may be <= 0)
   const int x_first = (int)(min(f_wave, XY) / p.Y), y_first = (int)(min(f_wave, XY) % p.Y);
   const CellSet cs{x_first, y_first, p.Y, kCpw, 0};
@@ -586,6 +599,34 @@ void sampling_vt_runs_fwd(RunArgs a) {
     wave_lds_sync();
     // ---- phase C: gather, cell by cell; a step takes S consecutive kept taps, kU steps in flight
     const int cl_first = __builtin_amdgcn_readfirstlane(cl), cl_last = __builtin_amdgcn_readlane(cl, nsmp - 1);
+    if constexpr (MG) {
+      for (int c = cl_first; c <= cl_last; ++c) {
+        const int hi_raw = uniform(sCellHi[c]);
+        if (hi_raw < 0) continue;
+        const int t1 = hi_raw & ((1 << 30) - 1), t0 = uniform(sCellLo[c]);
+        for (int gi = 0; gi < a.ngroups; ++gi) {
+          const int g_lo = gi * a.Cg, g_n = min(a.Cg, a.C_launch - g_lo);
+          // lanes past the group's channels read outside the buffer (zeros)
+          const int off_g = (q * kVec < g_n) ? lane_off + g_lo * p.elem_bytes : 0x40000000;
+          int t = t0;
+          for (; t + kU * S <= t1; t += kU * S) gather_steps<kU, S, Ln>(acc, sTap + t + slot, rs, off_g);
+          if (kU > 2 && t + 2 * S <= t1) {
+            gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, off_g);
+            t += 2 * S;
+          }
+          if (t + S <= t1) {
+            gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, off_g);
+            t += S;
+          }
+          if (t < t1) {
+            const bool in = t + slot < t1;
+            const Rec rr = sTap[t + slot];
+            Ln::fma_into(acc, Ln::load(rs, in ? rr.off + off_g : kOutOfRange), in ? rr.w : 0.f);
+          }
+          flush_cell<L, kVec, true>(acc, sOut + g_lo * kOutLd, c, lane, g_n);
+        }
+      }
+    } else
     for (int c = cl_first; c <= cl_last; ++c) {
       const int hi_raw = uniform(sCellHi[c]);
       if (hi_raw < 0) continue;
@@ -618,7 +659,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
     const size_t c_stride = (size_t)XY;
     float* ob = a.out + ((size_t)b * p.out_ch + a.c_lo) * c_stride + f_wave;
     const bool vec = ncell == kCpw && (((uintptr_t)ob | (size_t)p.Y * 4) & 15) == 0;
-    for (int e = lane; e < a.Cg * 2; e += kWave) {
+    for (int e = lane; e < a.C_launch * 2; e += kWave) {
       const int ch = e >> 1, h = (e & 1) * 4;
       const float* src = sOut + ch * kOutLd + h;
       float* dst = ob + ch * c_stride + h;
@@ -1053,9 +1094,15 @@ bool run_layout_supported(int D, int L) {
 
 template <bool BF16, bool ML>
 bool dispatch_runs(int D, int L, const RunArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
+  if (a.ngroups > 1) {
+    // several channel groups in one launch: the 16-byte, 16-lane layout only
+    if (ML || D != 4 || L != 16) return false;
+    hipLaunchKernelGGL((sampling_vt_runs_fwd<4, 16, BF16, false, true>), grid, dim3(kBlock), shmem, stream, a);
+    return true;
+  }
 #define FBEV_CASE(d, l)                                                                                   \
   if (D == d && L == l) {                                                                                 \
-    hipLaunchKernelGGL((sampling_vt_runs_fwd<d, l, BF16, ML>), grid, dim3(kBlock), shmem, stream, a);     \
+    hipLaunchKernelGGL((sampling_vt_runs_fwd<d, l, BF16, ML, false>), grid, dim3(kBlock), shmem, stream, a); \
     return true;                                                                                          \
   }
   FBEV_RUN_LAYOUTS(FBEV_CASE)
@@ -1121,9 +1168,17 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
     }
     a.c_lo = c;
     a.Cg = Cg;
+    a.ngroups = 1;
+    a.C_launch = Cg;
+    // the rest of the channels (at most one more group, 16-byte lanes) ride with this launch: the listing is
+    // done once for both groups
+    if (first && p.L == 1 && D == 4 && L == 16 && vec16 && p.C > Cg && p.C <= 2 * Cg) {
+      a.ngroups = 2;
+      a.C_launch = p.C;
+    }
     a.write_counts = (first && counts != nullptr) ? 1 : 0;
     const size_t shmem =
-        sizeof(CamRec) * p.N + (out_tile_bytes(Cg) + wave_lds_bytes(p.N * p.L, kWave / L)) * kWaves;
+        sizeof(CamRec) * p.N + (out_tile_bytes(a.C_launch) + wave_lds_bytes(p.N * p.L, kWave / L)) * kWaves;
     const dim3 grid((unsigned)tiles);
     const bool ml = p.L > 1;
     const bool ok = (es == 2) ? (ml ? dispatch_runs<true, true>(D, L, a, grid, shmem, stream)
@@ -1133,7 +1188,7 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
     if (!ok) return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    c += Cg;
+    c += a.C_launch;
     first = false;
   } while (c < p.C);
   return hipSuccess;
