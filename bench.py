@@ -543,8 +543,11 @@ def main_temporal(args):
     bwd_bytes = out_elems * 4 + feat_bytes + B * Cp * X * Y * 4 + cams       # upstream gradient, dL/dF, dL/dprev
     fwd = pass_rates(fwd_ms, fwd_bytes, out_elems_per_s=out_elems)
     bwd = pass_rates(bwd_ms, bwd_bytes, out_elems_per_s=out_elems)
-    dom_k, dom, dom_bytes = (["temporal_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else \
-        (["fill_zero_f32", "temporal_bwd"], bwd, bwd_bytes)
+    # the backward: zero-fill, the bin-run Sampling-VT backward and the resampling adjoint (maps of at most
+    # 256 x 256 pixels), else zero-fill and the fused hash-table kernel
+    bwd_k = ["fill_zero_f32", "sampling_vt_runs_bwd", "bev_align_bwd"] if max(H, W) <= 256 else \
+        ["fill_zero_f32", "temporal_bwd"]
+    dom_k, dom, dom_bytes = (["temporal_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else (bwd_k, bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
                       "seeded planar ego motion",

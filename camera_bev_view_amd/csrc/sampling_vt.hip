@@ -1226,7 +1226,9 @@ hipError_t launch_backward_temporal(const Problem& p, const float* grad_out, flo
   const BwdArgs a = bwd_args(p, grad_out, grad_feat, tiles);
   const bool current = nF > 0 && tiles > 0 && p.Z > 0 && p.C > 0;
   const bool previous = p.B > 0 && Cp > 0 && p.X > 0 && p.Y > 0;
-  if (!current || !previous || p.L != 1) {       // one part alone: its own launches
+  // one part alone, or a map the bin-run backward takes (faster alone than the hash-table backward fused with the
+  // resampling): separate launches
+  if (!current || !previous || p.L != 1 || backward_runs_supported(p)) {
     hipError_t e = launch_backward(p, grad_out, grad_feat, stream);
     if (e == hipSuccess && previous) e = launch_align_backward(p, grad_out, Cp, ego, grad_prev, c0, stream);
     return e;
