@@ -547,7 +547,10 @@ def main_temporal(args):
     # 256 x 256 pixels), else zero-fill and the fused hash-table kernel
     bwd_k = ["fill_zero_f32", "sampling_vt_runs_bwd", "bev_align_bwd"] if max(H, W) <= 256 else \
         ["fill_zero_f32", "temporal_bwd"]
-    dom_k, dom, dom_bytes = (["temporal_fwd"], fwd, fwd_bytes) if fwd_ms >= bwd_ms else (bwd_k, bwd, bwd_bytes)
+    # the forward: one launch of the bin-run kernel's tiles and the resampling units where the channels take the
+    # 16-byte, 16-lane layout (256 bytes per pixel), else the hash-era forward fused with the resampling
+    fwd_k = ["temporal_runs_fwd"] if C * 4 == 256 else ["temporal_fwd"]
+    dom_k, dom, dom_bytes = (fwd_k, fwd, fwd_bytes) if fwd_ms >= bwd_ms else (bwd_k, bwd, bwd_bytes)
     line = bench_line(args, out_elems / (ms_step * 1e-3), ms_step, "f32",
                       "synthetic: seeded 6-camera ring rig, N(0,1) features, previous map and upstream gradient, "
                       "seeded planar ego motion",

@@ -173,4 +173,10 @@ inline dim3 align_grid(AlignArgs& a) {
   return dim3((unsigned)((long long)a.nblk * a.nchunk * a.B));
 }
 
+// The temporal forward's Sampling-VT part (the bin-run kernel) and the previous map's resampling `al` (its
+// source, destination and motion set) in one launch; false, with nothing launched, where the bin-run forward
+// would need several launches or another lane layout (err holds the launch's status otherwise).
+bool launch_forward_runs_temporal(const Problem& p, float* out, uint8_t* counts, const AlignArgs& al,
+                                  hipStream_t stream, hipError_t& err);
+
 }  // namespace fbev

@@ -1160,6 +1160,10 @@ hipError_t launch_forward_temporal(const Problem& p, float* out, uint8_t* counts
     al.src = prev;
     al.dst = out;
     align_grid(al);
+    if (previous && p.C > 0) {
+      hipError_t e = hipSuccess;
+      if (launch_forward_runs_temporal(p, out, counts, al, stream, e)) return e;
+    }
     const hipError_t e = forward_groups(p, p.C > 0 ? out : nullptr, counts, (previous && p.L == 1) ? &al : nullptr,
                                         &al_done, stream);
     if (e != hipSuccess) return e;

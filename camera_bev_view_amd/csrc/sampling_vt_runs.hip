@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bev_align.h"
 #include "kernels.h"
 #include "wave_ops.h"
 
@@ -498,8 +499,7 @@ struct RunWaves {
 // the same listed taps (the lanes past the last group's channels read nothing), each cell's sums added into
 // the output tile at the end of its taps in a round.
 template <int D, int L, bool BF16, bool ML, bool MG>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
-void sampling_vt_runs_fwd(RunArgs a) {
+__device__ __forceinline__ void runs_fwd_body(const RunArgs& a, int blk, int nblk) {
   using Ln = Lane<D, BF16>;
   constexpr int kVec = Ln::kVec;
   constexpr int S = kWave / L;
@@ -524,7 +524,7 @@ void sampling_vt_runs_fwd(RunArgs a) {
 
   // tile = kTileY consecutive cells of the flattened [X, Y] grid, so that every channel's part of the
   // output tile is one aligned 128-byte line when X * Y is a multiple of 32
-  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = xcd_block(blk, nblk);
   const int b = tile / a.tiles_pb;
   const long long XY = (long long)p.X * p.Y;
   const long long f_wave = (long long)(tile - b * a.tiles_pb) * kTileY + wid * kCpw;
@@ -670,6 +670,26 @@ void sampling_vt_runs_fwd(RunArgs a) {
         for (int k = 0; k < 4 && h + k < ncell; ++k) dst[k] = src[k];
       }
     }
+  }
+}
+
+template <int D, int L, bool BF16, bool ML, bool MG>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
+void sampling_vt_runs_fwd(RunArgs a) {
+  runs_fwd_body<D, L, BF16, ML, MG>(a, blockIdx.x, gridDim.x);
+}
+
+// The temporal forward in one launch: the Sampling-VT tiles (svt of them, padded to svt_pad, a multiple of 8,
+// so that both parts keep their XCD numbering), then the previous map's resampling units, which the
+// dispatcher hands out as the Sampling-VT workgroups end.
+template <int D, int L, bool BF16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(RunWaves<D, L, BF16>::value)))
+void temporal_runs_fwd(RunArgs a, AlignArgs al, int svt, int svt_pad) {
+  static_assert(kBlock == kAlignBlock, "one workgroup size for both parts");
+  if ((int)blockIdx.x < svt_pad) {
+    if ((int)blockIdx.x < svt) runs_fwd_body<D, L, BF16, false, false>(a, blockIdx.x, svt);
+  } else {
+    align_fwd_body(al, blockIdx.x - svt_pad, gridDim.x - svt_pad);
   }
 }
 
@@ -1134,6 +1154,40 @@ void pick_run_layout(int bytes, bool vec16, int& D, int& L) {
 }
 
 }  // namespace
+
+bool launch_forward_runs_temporal(const Problem& p, float* out, uint8_t* counts, const AlignArgs& al,
+                                  hipStream_t stream, hipError_t& err) {
+  // one launch of the 16-byte, 16-lane layout covering every channel, single level
+  const int es = p.elem_bytes;
+  if (p.L != 1 || p.vec_bytes != 16 || p.C <= 0 || p.C * es > 512) return false;
+  int D = 0, L = 0;
+  pick_run_layout(p.C * es, true, D, L);
+  if (D != 4 || L != 16) return false;
+  const long long tiles_pb = ((long long)p.X * p.Y + kTileY - 1) / kTileY;
+  const long long svt = (long long)p.B * tiles_pb, svt_pad = (svt + 7) / 8 * 8;
+  AlignArgs a2 = al;
+  const long long align_blocks = align_grid(a2).x;
+  if (svt == 0 || svt_pad + align_blocks >= (1ll << 31)) return false;
+  RunArgs a;
+  a.p = p;
+  a.out = out;
+  a.counts = counts;
+  a.tiles_pb = (int)tiles_pb;
+  a.c_lo = 0;
+  a.Cg = p.C;
+  a.ngroups = 1;
+  a.C_launch = p.C;
+  a.write_counts = counts != nullptr ? 1 : 0;
+  const size_t shmem =
+      sizeof(CamRec) * p.N + (out_tile_bytes(p.C) + wave_lds_bytes(p.N, kWave / L)) * kWaves;
+  const dim3 grid((unsigned)(svt_pad + align_blocks)), block(kBlock);
+  if (es == 2)
+    hipLaunchKernelGGL((temporal_runs_fwd<4, 16, true>), grid, block, shmem, stream, a, a2, (int)svt, (int)svt_pad);
+  else
+    hipLaunchKernelGGL((temporal_runs_fwd<4, 16, false>), grid, block, shmem, stream, a, a2, (int)svt, (int)svt_pad);
+  err = hipGetLastError();
+  return true;
+}
 
 hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hipStream_t stream) {
   RunArgs a;
