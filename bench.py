@@ -151,11 +151,15 @@ def time_floor(args, dev, shape):
 
 
 def time_passes(args, dev, passes, label):
-    """W untimed warm-up steps, then K timed steps of ``passes`` (callables, run in order on the
-    current stream) bracketed by synchronizations; HIP events around every pass.  Returns
-    (ms per step over the whole timed region, [mean ms of each pass]).  With --cold a 1 GiB buffer is
-    overwritten before every timed step (more than the L2s and the 256 MB Infinity Cache hold), so each
-    step starts with its inputs in HBM only; the step time is then the sum of each step's own passes."""
+    """W untimed warm-up steps, then K timed steps of ``passes`` (callables, run in order on the current
+    stream) bracketed by synchronizations, with nothing else in the stream between them; then, untimed for
+    the step rate, up to 100 more steps with HIP events around every pass (an event between two kernels adds
+    a few microseconds of its own, so the step rate is taken without them).  Returns (ms per step over the
+    timed region, [mean ms of each pass]).  The host stays at most ~64 steps ahead of the GPU (it waits on
+    an event recorded 64 steps earlier), so a long run never fills the stream's queue, past which every
+    launch would wait for a free slot.  With --cold a 1 GiB buffer is overwritten before every timed step
+    (more than the L2s and the 256 MB Infinity Cache hold), so each step starts with its inputs in HBM only;
+    the step time is then the sum of each step's own passes, HIP events around every pass of every step."""
     import numpy as np
     import torch
     log(f"[bench] warmup {args.warmup} steps on {label}")
@@ -166,25 +170,48 @@ def time_passes(args, dev, passes, label):
     calibration_copy(args, dev)
     stream = torch.cuda.current_stream(dev)
     n = len(passes)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
-    log(f"[bench] timing {args.steps} steps" + (" (cold: cache sweep before each)" if args.cold else ""))
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        if sweep is not None:
-            sweep.fill_(float(k))
-        for i, f in enumerate(passes):
-            ev[k][i].record(stream)
-            f()
-        ev[k][n].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ahead = 64
+    marks = {}
+
+    def run(steps, ev=None, sweep=None):
+        for k in range(steps):
+            if k >= ahead and (k - ahead) in marks:
+                marks.pop(k - ahead).synchronize()
+            if sweep is not None:
+                sweep.fill_(float(k))
+            for i, f in enumerate(passes):
+                if ev is not None:
+                    ev[k][i].record(stream)
+                f()
+            if ev is not None:
+                ev[k][n].record(stream)
+            if k % 16 == 0:
+                marks[k] = torch.cuda.Event()
+                marks[k].record(stream)
+        marks.clear()
+
     if args.cold:
+        sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+        log(f"[bench] timing {args.steps} steps (cold: cache sweep before each)")
+        torch.cuda.synchronize()
+        run(args.steps, ev, sweep)
+        torch.cuda.synchronize()
         ms_step = float(np.mean([e[0].elapsed_time(e[n]) for e in ev]))
+    else:
+        log(f"[bench] timing {args.steps} steps")
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        run(args.steps)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = t_start.elapsed_time(t_end) / args.steps
+        n_ev = min(args.steps, 100)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(n_ev)]
+        run(n_ev, ev)
+        torch.cuda.synchronize()
     pass_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(n)]
     log(f"[bench] done: {ms_step * 1e3:.2f} us/step (passes " + ", ".join(f"{m * 1e3:.2f}" for m in pass_ms) + " us)")
     return ms_step, pass_ms
