@@ -438,6 +438,27 @@ __device__ __forceinline__ void gather_steps(float* acc, const Rec* rec, __amdgp
   for (int u = 0; u < U; ++u) Ln::fma_into(acc, v[u], w[u]);
 }
 
+// The kept taps [t, t1) of one cell into the lane's accumulators: whole steps of S taps in groups of U,
+// then of 2 and 1, with no masking; one masked step for the rest (its missing taps read outside the buffer).
+template <int U, int S, class Ln>
+__device__ __forceinline__ void gather_cell(float* acc, const Rec* sTap, int t, int t1, int slot,
+                                            __amdgpu_buffer_rsrc_t rs, int lane_off) {
+  for (; t + U * S <= t1; t += U * S) gather_steps<U, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+  if (U > 2 && t + 2 * S <= t1) {
+    gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+    t += 2 * S;
+  }
+  if (t + S <= t1) {
+    gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+    t += S;
+  }
+  if (t < t1) {
+    const bool in = t + slot < t1;
+    const Rec rr = sTap[t + slot];
+    Ln::fma_into(acc, Ln::load(rs, in ? rr.off + lane_off : kOutOfRange), in ? rr.w : 0.f);
+  }
+}
+
 // A cell's accumulators, complete: sum the S slots and park the channels in column `ct` of the output tile;
 // the accumulators are cleared for the next cell.
 template <int L, int kVec, bool kAdd = false>
@@ -608,21 +629,7 @@ __device__ __forceinline__ void runs_fwd_body(const RunArgs& a, int blk, int nbl
           const int g_lo = gi * a.Cg, g_n = min(a.Cg, a.C_launch - g_lo);
           // lanes past the group's channels read outside the buffer (zeros)
           const int off_g = (q * kVec < g_n) ? lane_off + g_lo * p.elem_bytes : 0x40000000;
-          int t = t0;
-          for (; t + kU * S <= t1; t += kU * S) gather_steps<kU, S, Ln>(acc, sTap + t + slot, rs, off_g);
-          if (kU > 2 && t + 2 * S <= t1) {
-            gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, off_g);
-            t += 2 * S;
-          }
-          if (t + S <= t1) {
-            gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, off_g);
-            t += S;
-          }
-          if (t < t1) {
-            const bool in = t + slot < t1;
-            const Rec rr = sTap[t + slot];
-            Ln::fma_into(acc, Ln::load(rs, in ? rr.off + off_g : kOutOfRange), in ? rr.w : 0.f);
-          }
+          gather_cell<kU, S, Ln>(acc, sTap, t0, t1, slot, rs, off_g);
           flush_cell<L, kVec, true>(acc, sOut + g_lo * kOutLd, c, lane, g_n);
         }
       }
@@ -631,22 +638,7 @@ __device__ __forceinline__ void runs_fwd_body(const RunArgs& a, int blk, int nbl
       const int hi_raw = uniform(sCellHi[c]);
       if (hi_raw < 0) continue;
       const int t1 = hi_raw & ((1 << 30) - 1);
-      int t = uniform(sCellLo[c]);
-      // whole steps in groups of kU, then of 2 and 1, with no masking; one masked step for the rest
-      for (; t + kU * S <= t1; t += kU * S) gather_steps<kU, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-      if (kU > 2 && t + 2 * S <= t1) {
-        gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-        t += 2 * S;
-      }
-      if (t + S <= t1) {
-        gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-        t += S;
-      }
-      if (t < t1) {
-        const bool in = t + slot < t1;
-        const Rec rr = sTap[t + slot];
-        Ln::fma_into(acc, Ln::load(rs, in ? rr.off + lane_off : kOutOfRange), in ? rr.w : 0.f);
-      }
+      gather_cell<kU, S, Ln>(acc, sTap, uniform(sCellLo[c]), t1, slot, rs, lane_off);
       if (hi_raw >> 30) flush_cell<L, kVec>(acc, sOut, c, lane, a.Cg);
     }
     wave_lds_sync();
