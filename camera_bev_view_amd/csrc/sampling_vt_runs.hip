@@ -439,11 +439,17 @@ __device__ __forceinline__ void gather_steps(float* acc, const Rec* rec, __amdgp
 }
 
 // The kept taps [t, t1) of one cell into the lane's accumulators: whole steps of S taps in groups of U,
-// then of 2 and 1, with no masking; one masked step for the rest (its missing taps read outside the buffer).
+// then at most one group each of 4, 2 and 1 (below U, so fewer than U whole steps remain after the loop),
+// with no masking; one masked step for the rest (its missing taps read outside the buffer).
 template <int U, int S, class Ln>
 __device__ __forceinline__ void gather_cell(float* acc, const Rec* sTap, int t, int t1, int slot,
                                             __amdgpu_buffer_rsrc_t rs, int lane_off) {
+  static_assert(U == 1 || U == 2 || U == 4 || U == 8, "the tail takes the powers of two below U");
   for (; t + U * S <= t1; t += U * S) gather_steps<U, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+  if (U > 4 && t + 4 * S <= t1) {
+    gather_steps<4, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+    t += 4 * S;
+  }
   if (U > 2 && t + 2 * S <= t1) {
     gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, lane_off);
     t += 2 * S;

@@ -117,6 +117,9 @@ RAGGED = [
     ("f32", 3, 1, 64, 16, 44, 21, 19, 8),     # one camera
     ("f32", 1, 11, 32, 16, 44, 13, 64, 17),   # 5 bins per pass, 4 passes
     ("f32", 1, 6, 64, 16, 44, 1, 1, 8),       # a single cell
+    ("f32", 1, 6, 70, 16, 44, 13, 37, 6),     # 280-byte rows: groups of 48, 16 (one dword per lane, 8 loads in flight) and 6
+    ("bf16", 1, 6, 20, 16, 44, 13, 37, 6),    # 40-byte rows: groups of 16 and 4 channels, one dword per lane, 8 loads in flight
+    ("f32", 2, 6, 100, 8, 22, 9, 33, 5),      # 64 + 36 channels in one launch, two samples
 ]
 
 
@@ -129,7 +132,8 @@ def test_ragged_forward(case):
 
 BWD_CASES = [
     ("f32", 1, 6, 20, 16, 44, 37, 45, 5),
-    ("f32", 2, 6, 200, 8, 22, 7, 40, 4),      # two backward channel groups (128 + 72)
+    ("f32", 2, 6, 200, 8, 22, 7, 40, 4),      # four 64-channel groups (3 x 64 + 8) in one launch
+    ("f32", 1, 6, 70, 16, 44, 13, 37, 6),     # 64 + 6 channels
     ("f32", 1, 5, 7, 12, 30, 11, 33, 6),
     ("f32", 1, 64, 16, 8, 22, 6, 35, 3),
 ]

@@ -99,6 +99,9 @@ TEMPORAL_CASES = [
     ("two channel groups, last fused", 1, 6, 320, 8, 22, 19, 41, 4, 6, -9.0, (-1.0, 2.5)),
     # 256 + 4 channels: the last group's 4-lane layout has no fused form, so the resampling runs on its own
     ("two channel groups, separate resampling", 1, 6, 260, 8, 22, 17, 23, 4, 3, 5.0, (0.5, -1.5)),
+    # 64 fp32 / 128 bf16 channels (256 bytes a pixel): the bin-run forward's tiles and the resampling in one launch
+    ("bin-run forward fused, fp32", 2, 6, 64, 8, 22, 26, 35, 5, 9, -14.0, (1.0, -2.0)),
+    ("bin-run forward fused, bf16", 1, 6, 128, 8, 22, 18, 29, 4, 5, 7.0, (-0.5, 1.5), "bf16"),
 ]
 
 
