@@ -438,30 +438,45 @@ __device__ __forceinline__ void gather_steps(float* acc, const Rec* rec, __amdgp
   for (int u = 0; u < U; ++u) Ln::fma_into(acc, v[u], w[u]);
 }
 
-// The kept taps [t, t1) of one cell into the lane's accumulators: whole steps of S taps in groups of U,
-// then at most one group each of 4, 2 and 1 (below U, so fewer than U whole steps remain after the loop),
-// with no masking; one masked step for the rest (its missing taps read outside the buffer).
+// K steps whose loads are all issued before the first is used, the last step masked: its slots past the
+// cell's taps (rec + u S >= end) read outside the buffer with weight 0.
+template <int K, int S, class Ln>
+__device__ __forceinline__ void gather_last(float* acc, const Rec* rec, __amdgpu_buffer_rsrc_t rs, int lane_off,
+                                            bool in_last) {
+  typename Ln::Raw v[K];
+  float w[K];
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    const Rec rr = rec[u * S];
+    const bool in = u + 1 < K || in_last;
+    w[u] = in ? rr.w : 0.f;
+    v[u] = Ln::load(rs, in ? rr.off + lane_off : kOutOfRange);
+  }
+#pragma unroll
+  for (int u = 0; u < K; ++u) Ln::fma_into(acc, v[u], w[u]);
+}
+
+// The kept taps [t, t1) of one cell into the lane's accumulators: whole groups of U steps of S taps while
+// more than U steps remain, then the rest (1 to U steps, the last one masked) as one group, so that a cell
+// of at most U steps costs one round trip to memory.
 template <int U, int S, class Ln>
 __device__ __forceinline__ void gather_cell(float* acc, const Rec* sTap, int t, int t1, int slot,
                                             __amdgpu_buffer_rsrc_t rs, int lane_off) {
-  static_assert(U == 1 || U == 2 || U == 4 || U == 8, "the tail takes the powers of two below U");
-  for (; t + U * S <= t1; t += U * S) gather_steps<U, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-  if (U > 4 && t + 4 * S <= t1) {
-    gather_steps<4, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-    t += 4 * S;
-  }
-  if (U > 2 && t + 2 * S <= t1) {
-    gather_steps<2, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-    t += 2 * S;
-  }
-  if (t + S <= t1) {
-    gather_steps<1, S, Ln>(acc, sTap + t + slot, rs, lane_off);
-    t += S;
-  }
-  if (t < t1) {
-    const bool in = t + slot < t1;
-    const Rec rr = sTap[t + slot];
-    Ln::fma_into(acc, Ln::load(rs, in ? rr.off + lane_off : kOutOfRange), in ? rr.w : 0.f);
+  static_assert(U >= 1 && U <= 8, "one to eight steps in flight");
+  for (; t + U * S < t1; t += U * S) gather_steps<U, S, Ln>(acc, sTap + t + slot, rs, lane_off);
+  if (t >= t1) return;
+  const int n = (t1 - t + S - 1) / S;                   // 1 .. U steps, wave-uniform
+  const bool in_last = t + (n - 1) * S + slot < t1;
+  const Rec* rec = sTap + t + slot;
+  switch (n) {
+    case 1: gather_last<1, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 2: if constexpr (U >= 2) gather_last<2, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 3: if constexpr (U >= 3) gather_last<3, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 4: if constexpr (U >= 4) gather_last<4, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 5: if constexpr (U >= 5) gather_last<5, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 6: if constexpr (U >= 6) gather_last<6, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    case 7: if constexpr (U >= 7) gather_last<7, S, Ln>(acc, rec, rs, lane_off, in_last); break;
+    default: if constexpr (U >= 8) gather_last<8, S, Ln>(acc, rec, rs, lane_off, in_last); break;
   }
 }
 
@@ -517,8 +532,9 @@ __host__ __device__ inline size_t out_tile_bytes(int Cg) {
 template <int D, int L, bool BF16>
 struct RunWaves {
   static constexpr int kVec = BF16 ? 2 * D : D;
-  static constexpr int value = (kVec <= 4 || (BF16 && kVec <= 8 && L == 16)) ? 6 : (kVec <= 8 ? 5 : 4);
-  static constexpr int kLoads = (D >= 3 || (BF16 && D >= 2)) ? 4 : 8;
+  static constexpr bool kWide = !BF16 && D == 4 && L == 16;   // fp32, 16-byte lanes: 8 loads at 5 waves
+  static constexpr int value = kWide ? 5 : (kVec <= 4 || (BF16 && kVec <= 8 && L == 16)) ? 6 : (kVec <= 8 ? 5 : 4);
+  static constexpr int kLoads = kWide ? 8 : (D >= 3 || (BF16 && D >= 2)) ? 4 : 8;
 };
 
 // Forward.  L lanes cover one tap's channel group with D dwords each (L * D * 4 == group bytes);
@@ -1009,9 +1025,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   const int b = r1 / a.tiles_x;
   const int x_tile = xt * kBTileX, y_tile = yt * kBTileY;
 
-  // the first channel group's upstream-gradient tile, loads issued before the camera table is staged
-  float gpre[kGPer];
-  load_g_tile(a, b, x_tile, y_tile, 0, min(kBCg, p.C), gpre);
   // boxes and the entry count start empty (visible after the camera staging's barrier)
   for (int e = threadIdx.x; e < NL; e += kBThreads) {
     sBox[4 * e] = 0x7fffffff;
@@ -1025,8 +1038,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     sMisc[3] = 0;                    // some wave stopped for want of room
   }
   stage_cameras(sCam, p, b);
-  // this wave's cells: x-row wid of the block, 8 cells; the waves go on without waiting for each other,
-  // and the gradient tile stays in registers (its loads in flight) until the first flush needs it
+  // the first channel group's upstream-gradient tile: its loads are issued once the camera table is staged
+  // (vector loads complete in issue order, so loads issued earlier would hold up the staging's wait for the
+  // camera entries), and it stays in registers, in flight during the listing, until the first flush needs it
+  float gpre[kGPer];
+  load_g_tile(a, b, x_tile, y_tile, 0, min(kBCg, p.C), gpre);
+  // this wave's cells: x-row wid of the block, 8 cells; the waves go on without waiting for each other
   const CellSet cs{x_tile + wid, 0, kBTileY, kBCpw, y_tile};
   const int total = wave_runs<false>(sCam, p, cs, sRun, sStart, lane);
   bool g_staged = false;
