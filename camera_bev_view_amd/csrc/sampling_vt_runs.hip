@@ -532,7 +532,7 @@ __host__ __device__ inline size_t out_tile_bytes(int Cg) {
 template <int D, int L, bool BF16>
 struct RunWaves {
   static constexpr int kVec = BF16 ? 2 * D : D;
-  static constexpr bool kWide = !BF16 && D == 4 && L == 16;   // fp32, 16-byte lanes: 8 loads at 5 waves
+  static constexpr bool kWide = D == 4 && L == 16;             // 16-byte lanes: 8 loads at 5 waves
   static constexpr int value = kWide ? 5 : (kVec <= 4 || (BF16 && kVec <= 8 && L == 16)) ? 6 : (kVec <= 8 ? 5 : 4);
   static constexpr int kLoads = kWide ? 8 : (D >= 3 || (BF16 && D >= 2)) ? 4 : 8;
 };
