@@ -1130,9 +1130,12 @@ bool run_layout_supported(int D, int L) {
 template <bool BF16, bool ML>
 bool dispatch_runs(int D, int L, const RunArgs& a, dim3 grid, size_t shmem, hipStream_t stream) {
   if (a.ngroups > 1) {
-    // several channel groups in one launch: the 16-byte, 16-lane layout only
-    if (ML || D != 4 || L != 16) return false;
-    hipLaunchKernelGGL((sampling_vt_runs_fwd<4, 16, BF16, false, true>), grid, dim3(kBlock), shmem, stream, a);
+    // several channel groups in one launch: 16-byte lanes, 16 or 8 lanes per tap
+    if (ML || D != 4 || (L != 16 && L != 8)) return false;
+    if (L == 16)
+      hipLaunchKernelGGL((sampling_vt_runs_fwd<4, 16, BF16, false, true>), grid, dim3(kBlock), shmem, stream, a);
+    else
+      hipLaunchKernelGGL((sampling_vt_runs_fwd<4, 8, BF16, false, true>), grid, dim3(kBlock), shmem, stream, a);
     return true;
   }
 #define FBEV_CASE(d, l)                                                                                   \
@@ -1241,7 +1244,7 @@ hipError_t launch_forward_runs(const Problem& p, float* out, uint8_t* counts, hi
     a.C_launch = Cg;
     // the rest of the channels (at most one more group, 16-byte lanes) ride with this launch: the listing is
     // done once for both groups
-    if (first && p.L == 1 && D == 4 && L == 16 && vec16 && p.C > Cg && p.C <= 2 * Cg) {
+    if (first && p.L == 1 && D == 4 && (L == 16 || L == 8) && vec16 && p.C > Cg && p.C <= 2 * Cg) {
       a.ngroups = 2;
       a.C_launch = p.C;
     }
