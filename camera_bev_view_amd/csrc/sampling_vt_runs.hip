@@ -741,6 +741,7 @@ struct BwdRunArgs {
   int tiles_x, tiles_y;
   int max_ent;           // entries held before a flush
   int max_keys;          // window counters per counting pass
+  int xcd_chunks;        // 1: each XCD takes a contiguous range of the tiles; 0: consecutive tiles on consecutive XCDs
 };
 
 // Entry: pixel x (8 bits), row y (8 bits), camera n (6 bits), cell of the block (6 bits); and the weight.
@@ -1023,7 +1024,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   int* sRun = reinterpret_cast<int*>(smem + lay.runs) + (2 * npair + 1) * wid;
   int* sStart = sRun + npair;
 
-  const int tile = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = a.xcd_chunks ? xcd_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int yt = tile % a.tiles_y;
   const int r1 = tile / a.tiles_y;
   const int xt = r1 % a.tiles_x;
@@ -1297,6 +1298,13 @@ hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* 
   a.tiles_y = (p.Y + kBTileY - 1) / kBTileY;
   a.max_ent = 3072;                     // entries held before a flush (at least one round of a wave)
   a.max_keys = 2048;
+  // contiguous tile ranges per XCD keep neighbouring tiles' atomics on the same pixels in one L2 (measured
+  // faster on nuScenes-shaped and batched maps); a single sample whose features exceed an L2 spreads its
+  // tiles over the XCDs instead (400 x 400 bf16 map: 830 -> 814 us)
+  {
+    const double feat_bytes = (double)p.B * p.N * p.P * p.C * p.elem_bytes;
+    a.xcd_chunks = (p.B == 1 && feat_bytes > 4.0 * (1 << 20)) ? 0 : 1;
+  }
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
   if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
