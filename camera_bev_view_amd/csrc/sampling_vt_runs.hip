@@ -1177,13 +1177,14 @@ void pick_run_layout(int bytes, bool vec16, int& D, int& L) {
   L = 0;
 }
 
-// Contiguous tile ranges per XCD (1) when the batch's features exceed one XCD's 4 MB L2 and there is more than
-// one sample to keep apart, and for pyramids (measured: three-level pyramid forward 51.9 against 52.9 us);
-// else consecutive tiles on consecutive XCDs (0; nuScenes-shaped forward 21.9 -> 21.7 us, the 400 x 400 bf16
-// map 193 -> 188 us).
+// Contiguous tile ranges per XCD (1), so that each XCD's L2 holds the features its part of the grid sees, unless
+// a single sample's features exceed an L2 anyway (single level): then consecutive tiles go to consecutive
+// XCDs (0), which spreads the dense tiles near the rig over all of them (400 x 400 bf16 map: 193 -> 188 us).
+// On maps whose features fit an L2 the spread measured ~1% faster but fetched every feature line into all
+// eight L2s (2.7x the fetched bytes on the nuScenes-shaped map), so they keep the ranges.
 int xcd_chunks(const Problem& p) {
   const double feat_bytes = (double)p.B * p.N * p.P * p.C * p.elem_bytes;
-  return (p.L > 1 || (p.B > 1 && feat_bytes > 4.0 * (1 << 20))) ? 1 : 0;
+  return (p.L == 1 && p.B == 1 && feat_bytes > 4.0 * (1 << 20)) ? 0 : 1;
 }
 
 }  // namespace
@@ -1299,12 +1300,9 @@ hipError_t launch_backward_runs(const Problem& p, const float* grad_out, float* 
   a.max_ent = 3072;                     // entries held before a flush (at least one round of a wave)
   a.max_keys = 2048;
   // contiguous tile ranges per XCD keep neighbouring tiles' atomics on the same pixels in one L2 (measured
-  // faster on nuScenes-shaped and batched maps); a single sample whose features exceed an L2 spreads its
-  // tiles over the XCDs instead (400 x 400 bf16 map: 830 -> 814 us)
-  {
-    const double feat_bytes = (double)p.B * p.N * p.P * p.C * p.elem_bytes;
-    a.xcd_chunks = (p.B == 1 && feat_bytes > 4.0 * (1 << 20)) ? 0 : 1;
-  }
+  // faster on nuScenes-shaped and batched maps: 39.1 against 40.6 us, 238 against 251 us); a single sample
+  // whose features exceed an L2 spreads its tiles over the XCDs instead (400 x 400 bf16 map: 830 -> 814 us)
+  a.xcd_chunks = xcd_chunks(p);      // (single level here)
   const long long tiles = (long long)p.B * a.tiles_x * a.tiles_y;
   if (tiles == 0 || p.C == 0 || p.Z == 0 || p.N == 0) return hipSuccess;
   if (tiles >= (1ll << 31)) return hipErrorInvalidValue;

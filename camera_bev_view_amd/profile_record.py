@@ -80,10 +80,11 @@ def trace(db: str) -> Dict[str, List[float]]:
 
 
 def calibration(fetch_db: str, write_db: str, calib_bytes: int):
-    """The calibration copy of ``calib_bytes`` (read and written once) is the dispatch with the most
-    FETCH_SIZE of its run; in the other run, the dispatch of the same kernel with the most WRITE_SIZE.
+    """The calibration copy of ``calib_bytes`` (read and written once) is the dispatch of a kernel outside this
+    library with the most FETCH_SIZE of its run (a library kernel can fetch more than the copy on a large
+    workload); in the other run, the dispatch of the same kernel with the most WRITE_SIZE.
     Returns (name, fetch KiB, write KiB, fetch factor, write factor)."""
-    fk, f = max(dispatches(fetch_db, "FETCH_SIZE"), key=lambda kv: kv[1])
+    fk, f = max(((k, v) for k, v in dispatches(fetch_db, "FETCH_SIZE") if "fbev::" not in k), key=lambda kv: kv[1])
     w = max(v for k, v in dispatches(write_db, "WRITE_SIZE") if k == fk)
     return short_name(fk), f, w, calib_bytes / (f * 1024.0), calib_bytes / (w * 1024.0)
 
