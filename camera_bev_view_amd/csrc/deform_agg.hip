@@ -143,6 +143,40 @@ __device__ __forceinline__ Taps taps_of(const Proj& pr, int n, int H, int W, int
   return t;
 }
 
+constexpr int kVecSteps = 8;             // 16-byte gather: steps (four taps each) in flight per lane
+constexpr int kOutOfRange = 0x7ffffff0;  // buffer offset the range check turns into a zero load
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+
+// K steps of the 16-byte gather, all loads issued before the first is used: lane (slot s, chunk j) takes tap
+// t0 + 4 u + s of step u, channels 4 j .. 4 j + 3 of the lane's block; taps at or past ntaps, and lanes past
+// the block's channels (lane_ok false), read nothing.
+template <int K>
+__device__ __forceinline__ void gather_vec(float (&acc)[4], const TapRec* rec, int t0, int ntaps, int slot,
+                                           __amdgpu_buffer_rsrc_t rs, int lane_off, bool lane_ok) {
+  u32x4 v[K];
+  float w[K];
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    const int tap = t0 + 4 * u + slot;
+    const bool in = tap < ntaps;
+    const TapRec rr = rec[in ? tap : 0];
+    w[u] = in ? rr.w : 0.f;
+    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (in && lane_ok) ? 4 * rr.off + lane_off : kOutOfRange, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[u], __uint_as_float(v[u][i]), acc[i]);
+  }
+}
+
+// Forward.  VEC: channels-last rows with C a multiple of 4 and 16-byte aligned, gathered with lanes =
+// (tap slot, 4-channel chunk): a load instruction takes four taps' 64-channel blocks, whole groups of
+// kVecSteps steps are issued before any is used (a query with up to 8 in-view pairs, 32 taps, costs one
+// round trip), and the four slots are summed with lane swaps at the end.  Otherwise lanes = channels,
+// one tap row per load, kUnroll in flight.
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);                                   // [N][12]
@@ -169,6 +203,14 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
   const int c = c0 + lane;
   const bool ch = c < a.C;
   float acc = 0.f;
+  // VEC lane roles: tap slot, and a 4-channel chunk of the block (lanes past the block's channels read nothing)
+  const int slot = lane >> 4, jc = lane & 15;
+  const bool ch4 = c0 + 4 * jc < a.C;
+  const int lane_off = 4 * (c0 + 4 * jc);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(fb), 0, VEC ? (int)(sizeof(float) * a.N * HWC) : 0,
+                                        0x00020000);
+  float acc4[4] = {0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < NK; base += kWave) {
     // ---- phase A: pair idx = n * Kp + k on this lane
     const int idx = base + lane;
@@ -196,24 +238,51 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
       rec[4 * s + 3] = TapRec{tp.p00 + tp.dy + tp.dx, wa1 * tp.b};
     }
     wave_lds_sync();
-    // ---- phase C: gather the listed taps, lanes = channels
+    // ---- phase C: gather the listed taps
     const int ntaps = 4 * cnt;
-    for (int j = 0; j < ntaps; j += kUnroll) {
-      float v[kUnroll], w[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int jj = j + u;
-        const bool in = jj < ntaps;
-        const TapRec rr = rec[in ? jj : 0];
-        w[u] = in ? rr.w : 0.f;
-        v[u] = (in && ch) ? fb[(size_t)rr.off + c] : 0.f;
+    if constexpr (VEC) {
+      for (int t0 = 0; t0 < ntaps; t0 += 4 * kVecSteps) {
+        const int n = min(kVecSteps, (ntaps - t0 + 3) / 4);      // steps of this group, wave-uniform
+        switch (n) {
+          case 1: gather_vec<1>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 2: gather_vec<2>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 3: gather_vec<3>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 4: gather_vec<4>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 5: gather_vec<5>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 6: gather_vec<6>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          case 7: gather_vec<7>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+          default: gather_vec<8>(acc4, rec, t0, ntaps, slot, rs, lane_off, ch4); break;
+        }
       }
+    } else {
+      for (int j = 0; j < ntaps; j += kUnroll) {
+        float v[kUnroll], w[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) acc = fmaf(w[u], v[u], acc);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int jj = j + u;
+          const bool in = jj < ntaps;
+          const TapRec rr = rec[in ? jj : 0];
+          w[u] = in ? rr.w : 0.f;
+          v[u] = (in && ch) ? fb[(size_t)rr.off + c] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc = fmaf(w[u], v[u], acc);
+      }
     }
     wave_lds_sync();   // the records are read before the next pass overwrites them
   }
-  if (ch) a.out[bq * a.C + c] = acc;
+  if constexpr (VEC) {
+    // sum over the four slots: afterwards every lane holds its chunk's totals
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc4[i] = swap32_add(acc4[i], acc4[i]);
+      acc4[i] = swap16_add(acc4[i], acc4[i]);
+    }
+    if (slot == 0 && ch4)
+      *reinterpret_cast<float4*>(a.out + bq * a.C + c0 + 4 * jc) = make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
+  } else {
+    if (ch) a.out[bq * a.C + c] = acc;
+  }
 }
 
 constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together (one per lane row)
@@ -648,7 +717,14 @@ hipError_t launch_deform_forward(const DeformArgs& a, hipStream_t stream) {
   const long long units = (long long)a.Q * ((a.C + kWave - 1) / kWave);
   const dim3 grid((unsigned)((units + kWaves - 1) / kWaves), (unsigned)a.B);
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(TapRec) * 4 * kWave * kWaves;
-  hipLaunchKernelGGL(deform_fwd, grid, dim3(kBlock), shmem, stream, a);
+  // the 16-byte gather needs 16-byte channel rows (C a multiple of 4, an aligned base) and buffer offsets
+  // that fit 31 bits
+  const bool vec = a.C % 4 == 0 && (reinterpret_cast<uintptr_t>(a.feat) & 15) == 0 &&
+                   sizeof(float) * (double)a.N * a.H * a.W * a.C < (double)kOutOfRange;
+  if (vec)
+    hipLaunchKernelGGL(deform_fwd<true>, grid, dim3(kBlock), shmem, stream, a);
+  else
+    hipLaunchKernelGGL(deform_fwd<false>, grid, dim3(kBlock), shmem, stream, a);
   return hipGetLastError();
 }
 
