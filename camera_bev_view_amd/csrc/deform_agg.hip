@@ -307,6 +307,25 @@ struct SampleRec {
 // dL/doffsets and dL/danchors are deterministic.
 // Five waves per SIMD (at most 96 VGPRs): with the table sized to the pass bound, a dense workload's
 // 27 KB of LDS then fits five workgroups per CU.
+// Four row sums at once: d[q] holds lane j's part of value q (j = lane % 16); afterwards every lane of quad q
+// of the row (j / 4 == q) holds the row's sum of value q (mirror across the row, then across each half, then
+// two quad swaps: 5 DPP adds for four sums).
+__device__ __forceinline__ float row_sums_x4(const float (&d)[4], int j) {
+  const bool lower = j < 8;
+  const float a0 = (lower ? d[0] : d[2]) + dpp<kRowMirror>(lower ? d[2] : d[0]);
+  const float a1 = (lower ? d[1] : d[3]) + dpp<kRowMirror>(lower ? d[3] : d[1]);
+  const bool lo4 = (j & 7) < 4;
+  float b = (lo4 ? a0 : a1) + dpp<kHalfMirror>(lo4 ? a1 : a0);
+  b += dpp<kQuadSwap1>(b);
+  b += dpp<kQuadSwap2>(b);
+  return b;
+}
+
+// VEC: the per-sample sums by 16-byte loads, lanes = (tap, 4-channel chunk): a lane forms the dot product of
+// its tap's channels with g, the 16 lanes of a row sum it (four samples at a time), and the sample's three
+// sums follow from its four tap dots: <sample, g> = sum of the bilinear weights times the dots, and the u and
+// v derivatives are the dots' differences along x and y.  Otherwise lanes = channels, four tap loads each.
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void deform_bwd(DeformArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
@@ -401,53 +420,101 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     wave_lds_sync();
     // ---- per in-view sample: this wave's channels of the three sums, four samples at a time with
     // all their tap loads in flight (past the list's end the last sample is read again, unused)
-    for (int s0 = 0; s0 < cnt; s0 += kSampUnroll) {
-      int p00[kSampUnroll], dx[kSampUnroll], dy[kSampUnroll];
-      float fa[kSampUnroll], fbt[kSampUnroll];
-#pragma unroll
-      for (int i = 0; i < kSampUnroll; ++i) {
-        const SampleRec sr = smp[min(s0 + i, cnt - 1)];
-        p00[i] = uniform(sr.pix) * a.C;
-        dx[i] = uniform(sr.dxp) * a.C;
-        dy[i] = uniform(sr.dyp) * a.C;
-        fa[i] = sr.a;
-        fbt[i] = sr.b;
-      }
-      float ds[kSampUnroll], du[kSampUnroll], dv[kSampUnroll];
-#pragma unroll
-      for (int i = 0; i < kSampUnroll; ++i) ds[i] = du[i] = dv[i] = 0.f;
-      for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) {
-        const float g = gq[c];
-        float F[kSampUnroll][4];
+    if constexpr (VEC) {
+      const int trow = lane >> 4, jc = lane & 15;            // tap (x1 by bit 0, y1 by bit 1), channel chunk
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(fb), 0, (int)(sizeof(float) * a.N * HWC), 0x00020000);
+      for (int s0 = 0; s0 < cnt; s0 += kSampUnroll) {
+        int off[kSampUnroll];
 #pragma unroll
         for (int i = 0; i < kSampUnroll; ++i) {
-          F[i][0] = fb[(size_t)p00[i] + c];
-          F[i][1] = fb[(size_t)p00[i] + dx[i] + c];
-          F[i][2] = fb[(size_t)p00[i] + dy[i] + c];
-          F[i][3] = fb[(size_t)p00[i] + dy[i] + dx[i] + c];
+          const SampleRec sr = smp[min(s0 + i, cnt - 1)];
+          off[i] = (sr.pix + ((trow & 1) ? sr.dxp : 0) + ((trow & 2) ? sr.dyp : 0)) * a.C;
         }
+        float d[kSampUnroll];
 #pragma unroll
+        for (int i = 0; i < kSampUnroll; ++i) d[i] = 0.f;
+        for (int cb = wq * kWave; cb < a.C; cb += wq_n * kWave) {
+          const int cc = cb + 4 * jc;
+          const bool ok = cc < a.C;
+          const float4 g4 = ok ? *reinterpret_cast<const float4*>(gq + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
+          u32x4 v[kSampUnroll];
+#pragma unroll
+          for (int i = 0; i < kSampUnroll; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? 4 * (off[i] + cc) : kOutOfRange, 0, 0);
+#pragma unroll
+          for (int i = 0; i < kSampUnroll; ++i) {
+            d[i] = fmaf(g4.x, __uint_as_float(v[i][0]), d[i]);
+            d[i] = fmaf(g4.y, __uint_as_float(v[i][1]), d[i]);
+            d[i] = fmaf(g4.z, __uint_as_float(v[i][2]), d[i]);
+            d[i] = fmaf(g4.w, __uint_as_float(v[i][3]), d[i]);
+          }
+        }
+        static_assert(kSampUnroll == 4, "four samples per row sum");
+        const float dot = row_sums_x4(d, jc);             // tap trow of sample s0 + jc / 4
+        const int qd = jc >> 2;
+        if ((jc & 3) == 0 && s0 + qd < cnt) sPart[(wid * kWave + s0 + qd) * 4 + trow] = dot;
+      }
+      wave_lds_sync();
+      // the sample's lane turns its four tap dots into the three sums (in place)
+      if (lane < cnt) {
+        const SampleRec sr = smp[lane];
+        const float4 dt = *reinterpret_cast<const float4*>(sPart + (wid * kWave + lane) * 4);
+        const float a0 = 1.f - sr.a, b0 = 1.f - sr.b;
+        const float smpv = a0 * b0 * dt.x + sr.a * b0 * dt.y + a0 * sr.b * dt.z + sr.a * sr.b * dt.w;
+        const float su = b0 * (dt.y - dt.x) + sr.b * (dt.w - dt.z);
+        const float sv = a0 * (dt.z - dt.x) + sr.a * (dt.w - dt.y);
+        *reinterpret_cast<float4*>(sPart + (wid * kWave + lane) * 4) = make_float4(smpv, su, sv, 0.f);
+      }
+    } else {
+      for (int s0 = 0; s0 < cnt; s0 += kSampUnroll) {
+        int p00[kSampUnroll], dx[kSampUnroll], dy[kSampUnroll];
+        float fa[kSampUnroll], fbt[kSampUnroll];
+  #pragma unroll
         for (int i = 0; i < kSampUnroll; ++i) {
-          const float a0 = 1.f - fa[i], b0 = 1.f - fbt[i];
-          const float smpv = a0 * b0 * F[i][0] + fa[i] * b0 * F[i][1] + a0 * fbt[i] * F[i][2] + fa[i] * fbt[i] * F[i][3];
-          const float su = b0 * (F[i][1] - F[i][0]) + fbt[i] * (F[i][3] - F[i][2]);
-          const float sv = a0 * (F[i][2] - F[i][0]) + fa[i] * (F[i][3] - F[i][1]);
-          ds[i] = fmaf(g, smpv, ds[i]);
-          du[i] = fmaf(g, su, du[i]);
-          dv[i] = fmaf(g, sv, dv[i]);
+          const SampleRec sr = smp[min(s0 + i, cnt - 1)];
+          p00[i] = uniform(sr.pix) * a.C;
+          dx[i] = uniform(sr.dxp) * a.C;
+          dy[i] = uniform(sr.dyp) * a.C;
+          fa[i] = sr.a;
+          fbt[i] = sr.b;
         }
+        float ds[kSampUnroll], du[kSampUnroll], dv[kSampUnroll];
+  #pragma unroll
+        for (int i = 0; i < kSampUnroll; ++i) ds[i] = du[i] = dv[i] = 0.f;
+        for (int c = wq * kWave + lane; c < a.C; c += wq_n * kWave) {
+          const float g = gq[c];
+          float F[kSampUnroll][4];
+  #pragma unroll
+          for (int i = 0; i < kSampUnroll; ++i) {
+            F[i][0] = fb[(size_t)p00[i] + c];
+            F[i][1] = fb[(size_t)p00[i] + dx[i] + c];
+            F[i][2] = fb[(size_t)p00[i] + dy[i] + c];
+            F[i][3] = fb[(size_t)p00[i] + dy[i] + dx[i] + c];
+          }
+  #pragma unroll
+          for (int i = 0; i < kSampUnroll; ++i) {
+            const float a0 = 1.f - fa[i], b0 = 1.f - fbt[i];
+            const float smpv = a0 * b0 * F[i][0] + fa[i] * b0 * F[i][1] + a0 * fbt[i] * F[i][2] + fa[i] * fbt[i] * F[i][3];
+            const float su = b0 * (F[i][1] - F[i][0]) + fbt[i] * (F[i][3] - F[i][2]);
+            const float sv = a0 * (F[i][2] - F[i][0]) + fa[i] * (F[i][3] - F[i][1]);
+            ds[i] = fmaf(g, smpv, ds[i]);
+            du[i] = fmaf(g, su, du[i]);
+            dv[i] = fmaf(g, sv, dv[i]);
+          }
+        }
+        float v[3 * kSampUnroll], z[3];
+  #pragma unroll
+        for (int i = 0; i < kSampUnroll; ++i) {
+          v[3 * i] = ds[i];
+          v[3 * i + 1] = du[i];
+          v[3 * i + 2] = dv[i];
+        }
+        wave_sum_4x3(v, z);
+        const int row = lane >> 4;
+        if ((lane & 15) == 0 && s0 + row < cnt)
+          *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + row) * 4) = make_float4(z[0], z[1], z[2], 0.f);
       }
-      float v[3 * kSampUnroll], z[3];
-#pragma unroll
-      for (int i = 0; i < kSampUnroll; ++i) {
-        v[3 * i] = ds[i];
-        v[3 * i + 1] = du[i];
-        v[3 * i + 2] = dv[i];
-      }
-      wave_sum_4x3(v, z);
-      const int row = lane >> 4;
-      if ((lane & 15) == 0 && s0 + row < cnt)
-        *reinterpret_cast<float4*>(sPart + (wid * kWave + s0 + row) * 4) = make_float4(z[0], z[1], z[2], 0.f);
     }
     // ---- the feature gradient: one entry (pixel, rank, merged weight) per merged pixel, the rank
     // taken from the pixel's counter; the gather kernels add w * g over each pixel's entries
@@ -820,7 +887,14 @@ hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t str
   const size_t shmem = sizeof(double) * 12 * a.N + sizeof(SampleRec) * kWave * kWaves +
                        sizeof(float) * 4 * kWave * kWaves + sizeof(int2) * a.tab_max * kWaves +
                        sizeof(float) * 3 * a.Kp * kWaves;
-  hipLaunchKernelGGL(deform_bwd, grid, dim3(kBlock), shmem, stream, a);
+  // the 16-byte tap loads need 16-byte channel rows of the features and of the upstream gradient (C a
+  // multiple of 4, aligned bases) and buffer offsets that fit 31 bits
+  const bool vec = a.C % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.feat) | reinterpret_cast<uintptr_t>(a.grad)) & 15) == 0 &&
+                   sizeof(float) * (double)a.N * a.H * a.W * a.C < (double)kOutOfRange;
+  if (vec)
+    hipLaunchKernelGGL(deform_bwd<true>, grid, dim3(kBlock), shmem, stream, a);
+  else
+    hipLaunchKernelGGL(deform_bwd<false>, grid, dim3(kBlock), shmem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !gather) return e;
   const int np = (int)npix;
