@@ -720,29 +720,37 @@ __global__ __launch_bounds__(kBlock) void deform_gather(DeformArgs a, int npix) 
   if (ch) a.gfeat[(size_t)p * a.C + c] = acc;
 }
 
-// The same for C % 4 == 0 with 16-byte aligned rows: lanes = (entry slot e, channel quad q), a wave
-// covers up to 256 channels of its pixel as Qw quads (Qw = 16, 32 or 64, the power of two at or
-// above the block's quads) and takes E = 64 / Qw entries per float4 load; eight loads in flight and
-// the next step's entries read ahead.  The E slots are summed by lane swaps at the end.
-template <int Qw>
+// The same for C % 4 == 0 with 16-byte aligned rows: lanes = (entry slot e, channel quad q), a wave covers up
+// to 256 channels of its pixel as Qw quads (Qw = 16, 32 or 64, the power of two at or above the block's quads)
+// and takes E = 64 / Qw entries per float4 load, eight loads in flight and the next step's entries read ahead;
+// its E slots are summed by lane swaps at the end.  WP waves share a (pixel, 256-channel block): with WP = 4
+// (pixels with a few hundred entries, as in the dense BEV form) the workgroup's waves take every fourth step of
+// the pixel's entries and the first wave adds the others' sums in wave order; with WP = 1 a workgroup takes
+// four pixels.
+template <int Qw, int WP>
 __global__ __launch_bounds__(kBlock) void deform_gather4(DeformArgs a, int npix) {
+  static_assert(WP == 1 || WP == kWaves, "one wave or the whole workgroup per pixel");
   constexpr int E = kWave / Qw;
   constexpr int kStep = kGatherUnroll * E;
+  __shared__ float4 sAcc[WP > 1 ? WP - 1 : 1][Qw];
   const int lane = threadIdx.x & (kWave - 1);
+  const int wid = uniform(threadIdx.x / kWave);
+  const int wp = wid % WP;                          // this wave's share of the pixel's entries
   const int e = lane / Qw, q = lane - e * Qw;
   const int groups = (a.C + 4 * kWave - 1) / (4 * kWave);
-  const long long unit = (long long)xcd_block(blockIdx.x, gridDim.x) * kWaves + threadIdx.x / kWave;
-  if (unit >= (long long)npix * groups) return;
+  const long long unit = (long long)xcd_block(blockIdx.x, gridDim.x) * (kWaves / WP) + wid / WP;
+  if (unit >= (long long)npix * groups) return;      // (with WP > 1 the whole workgroup: no barrier follows)
   const int p = (int)(unit / groups);
   const int c = (int)(unit - (long long)p * groups) * 4 * kWave + 4 * q;
   const bool ch = c < a.C;
   const int n = uniform(a.pix_count[p]);
   const int2* bk = a.bucket + uniform(a.pix_first[p]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int j0 = wp * kStep;
   int2 en[kGatherUnroll];
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) en[u] = (n > 0) ? bk[min(u * E + e, n - 1)] : make_int2(0, 0);
-  for (int j = 0; j < n; j += kStep) {
+  for (int u = 0; u < kGatherUnroll; ++u) en[u] = (j0 < n) ? bk[min(j0 + u * E + e, n - 1)] : make_int2(0, 0);
+  for (int j = j0; j < n; j += WP * kStep) {
     float4 v[kGatherUnroll];
     float w[kGatherUnroll];
 #pragma unroll
@@ -750,9 +758,10 @@ __global__ __launch_bounds__(kBlock) void deform_gather4(DeformArgs a, int npix)
       w[u] = (j + u * E + e < n) ? __int_as_float(en[u].y) : 0.f;
       v[u] = ch ? *reinterpret_cast<const float4*>(a.grad + (size_t)en[u].x * a.C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (j + kStep < n) {
+    const int jn = j + WP * kStep;
+    if (jn < n) {
 #pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) en[u] = bk[min(j + kStep + u * E + e, n - 1)];
+      for (int u = 0; u < kGatherUnroll; ++u) en[u] = bk[min(jn + u * E + e, n - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
@@ -774,7 +783,21 @@ __global__ __launch_bounds__(kBlock) void deform_gather4(DeformArgs a, int npix)
     acc.z = swap32_add(acc.z, acc.z);
     acc.w = swap32_add(acc.w, acc.w);
   }
-  if (e == 0 && ch) *reinterpret_cast<float4*>(a.gfeat + (size_t)p * a.C + c) = acc;
+  if constexpr (WP > 1) {
+    if (wp > 0 && e == 0) sAcc[wp - 1][q] = acc;
+    __syncthreads();
+    if (wp == 0 && e == 0) {
+#pragma unroll
+      for (int w = 0; w < WP - 1; ++w) {
+        const float4 o = sAcc[w][q];
+        acc.x += o.x;
+        acc.y += o.y;
+        acc.z += o.z;
+        acc.w += o.w;
+      }
+    }
+  }
+  if (wp == 0 && e == 0 && ch) *reinterpret_cast<float4*>(a.gfeat + (size_t)p * a.C + c) = acc;
 }
 
 }  // namespace
@@ -912,13 +935,23 @@ hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t str
   const bool vec4 = a.C % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.grad) | reinterpret_cast<uintptr_t>(a.gfeat)) & 15) == 0;
   if (vec4) {
     const size_t units = npix * ((a.C + 4 * kWave - 1) / (4 * kWave));
-    const dim3 g4((unsigned)((units + kWaves - 1) / kWaves));
-    if (a.C <= 64)
-      hipLaunchKernelGGL(deform_gather4<16>, g4, dim3(kBlock), 0, stream, a, np);
-    else if (a.C <= 128)
-      hipLaunchKernelGGL(deform_gather4<32>, g4, dim3(kBlock), 0, stream, a, np);
-    else
-      hipLaunchKernelGGL(deform_gather4<64>, g4, dim3(kBlock), 0, stream, a, np);
+    // a workgroup per (pixel, block) when the pixels can hold a few hundred entries on average (the dense BEV
+    // form: 123 against 127 us), else four per workgroup (the sparse queries: 38 against 39 us)
+    const bool split = (double)a.B * a.Q * a.cap >= 512.0 * (double)npix;
+    const dim3 g4((unsigned)(split ? units : (units + kWaves - 1) / kWaves));
+#define FBEV_GATHER4(qw)                                                                   \
+    if (split)                                                                             \
+      hipLaunchKernelGGL((deform_gather4<qw, kWaves>), g4, dim3(kBlock), 0, stream, a, np); \
+    else                                                                                   \
+      hipLaunchKernelGGL((deform_gather4<qw, 1>), g4, dim3(kBlock), 0, stream, a, np);
+    if (a.C <= 64) {
+      FBEV_GATHER4(16)
+    } else if (a.C <= 128) {
+      FBEV_GATHER4(32)
+    } else {
+      FBEV_GATHER4(64)
+    }
+#undef FBEV_GATHER4
   } else {
     const size_t units = npix * blocks;
     hipLaunchKernelGGL(deform_gather, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream, a,
