@@ -286,6 +286,7 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
 }
 
 constexpr int kSampUnroll = 4;           // backward samples whose tap loads are in flight together (one per lane row)
+constexpr int kVecSamples = 8;           // the same for the 16-byte tap loads (a multiple of four)
 constexpr int kTabMinBits = 6;           // a pass uses 2^bits slots, at least 4/3 of its 4 cnt taps (at most 3/4 full)
 
 // Per-wave LDS of the backward: the in-view samples of one pass.
@@ -424,36 +425,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
       const int trow = lane >> 4, jc = lane & 15;            // tap (x1 by bit 0, y1 by bit 1), channel chunk
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(fb), 0, (int)(sizeof(float) * a.N * HWC), 0x00020000);
-      for (int s0 = 0; s0 < cnt; s0 += kSampUnroll) {
-        int off[kSampUnroll];
+      for (int s0 = 0; s0 < cnt; s0 += kVecSamples) {
+        int off[kVecSamples];
 #pragma unroll
-        for (int i = 0; i < kSampUnroll; ++i) {
+        for (int i = 0; i < kVecSamples; ++i) {
           const SampleRec sr = smp[min(s0 + i, cnt - 1)];
           off[i] = (sr.pix + ((trow & 1) ? sr.dxp : 0) + ((trow & 2) ? sr.dyp : 0)) * a.C;
         }
-        float d[kSampUnroll];
+        float d[kVecSamples];
 #pragma unroll
-        for (int i = 0; i < kSampUnroll; ++i) d[i] = 0.f;
+        for (int i = 0; i < kVecSamples; ++i) d[i] = 0.f;
         for (int cb = wq * kWave; cb < a.C; cb += wq_n * kWave) {
           const int cc = cb + 4 * jc;
           const bool ok = cc < a.C;
           const float4 g4 = ok ? *reinterpret_cast<const float4*>(gq + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
-          u32x4 v[kSampUnroll];
+          u32x4 v[kVecSamples];
 #pragma unroll
-          for (int i = 0; i < kSampUnroll; ++i)
+          for (int i = 0; i < kVecSamples; ++i)
             v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? 4 * (off[i] + cc) : kOutOfRange, 0, 0);
 #pragma unroll
-          for (int i = 0; i < kSampUnroll; ++i) {
+          for (int i = 0; i < kVecSamples; ++i) {
             d[i] = fmaf(g4.x, __uint_as_float(v[i][0]), d[i]);
             d[i] = fmaf(g4.y, __uint_as_float(v[i][1]), d[i]);
             d[i] = fmaf(g4.z, __uint_as_float(v[i][2]), d[i]);
             d[i] = fmaf(g4.w, __uint_as_float(v[i][3]), d[i]);
           }
         }
-        static_assert(kSampUnroll == 4, "four samples per row sum");
-        const float dot = row_sums_x4(d, jc);             // tap trow of sample s0 + jc / 4
         const int qd = jc >> 2;
-        if ((jc & 3) == 0 && s0 + qd < cnt) sPart[(wid * kWave + s0 + qd) * 4 + trow] = dot;
+#pragma unroll
+        for (int h = 0; h < kVecSamples; h += 4) {
+          const float d4[4] = {d[h], d[h + 1], d[h + 2], d[h + 3]};
+          const float dot = row_sums_x4(d4, jc);          // tap trow of sample s0 + h + jc / 4
+          if ((jc & 3) == 0 && s0 + h + qd < cnt) sPart[(wid * kWave + s0 + h + qd) * 4 + trow] = dot;
+        }
       }
       wave_lds_sync();
       // the sample's lane turns its four tap dots into the three sums (in place)
