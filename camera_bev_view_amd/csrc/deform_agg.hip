@@ -220,12 +220,10 @@ __global__ __launch_bounds__(kBlock) void deform_fwd(DeformArgs a) {
     if (idx < NK) {
       const int n = idx / a.Kp, k = idx - n * a.Kp;
       const float* o = a.offsets + (bq * a.Kp + k) * 3;
+      wq = a.weights[bq * NK + idx];                 // loaded with the offsets: one round trip for both
       const Proj pr = project_pair(sP + n * 12, ax + (double)o[0], ay + (double)o[1], az + (double)o[2], a.H, a.W);
       valid = pr.valid;
-      if (valid) {
-        tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
-        wq = a.weights[bq * NK + idx];
-      }
+      if (valid) tp = taps_of(pr, n, a.H, a.W, a.C, HWC);
     }
     const uint64_t m = __ballot(valid);
     const int cnt = (int)__builtin_popcountll(m);
