@@ -120,6 +120,8 @@ RAGGED = [
     ("f32", 1, 6, 70, 16, 44, 13, 37, 6),     # 280-byte rows: groups of 48, 16 (one dword per lane, 8 loads in flight) and 6
     ("bf16", 1, 6, 20, 16, 44, 13, 37, 6),    # 40-byte rows: groups of 16 and 4 channels, one dword per lane, 8 loads in flight
     ("f32", 2, 6, 100, 8, 22, 9, 33, 5),      # 64 + 36 channels in one launch, two samples
+    ("f32", 1, 6, 40, 16, 44, 13, 37, 6),     # 160-byte rows: 32 + 8 channels in one launch, 8 lanes per tap
+    ("bf16", 1, 6, 72, 16, 44, 11, 41, 5),    # 144-byte rows: 64 + 8 channels in one launch, 8 lanes per tap
 ]
 
 
