@@ -324,7 +324,9 @@ __device__ __forceinline__ float row_sums_x4(const float (&d)[4], int j) {
 // its tap's channels with g, the 16 lanes of a row sum it (four samples at a time), and the sample's three
 // sums follow from its four tap dots: <sample, g> = sum of the bilinear weights times the dots, and the u and
 // v derivatives are the dots' differences along x and y.  Otherwise lanes = channels, four tap loads each.
-template <bool VEC>
+// W1: one wave per query (C <= 64), so the query's steps need only wave-level order: no workgroup barrier after
+// the camera staging, and each wave goes at its own pace.
+template <bool VEC, bool W1>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void deform_bwd(DeformArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* sP = reinterpret_cast<double*>(smem);                                             // [N][12]
@@ -532,7 +534,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
       }
       ecount += nu;
     }
-    __syncthreads();
+    if constexpr (W1) {
+      wave_lds_sync();
+    } else {
+      __syncthreads();
+    }
     // ---- the query's first wave: sums over its waves (wave order), dL/dw, keypoint contributions
     if (wq == 0 && lane < cnt) {
       float4 t = *reinterpret_cast<const float4*>(sPart + (lead * kWave + lane) * 4);
@@ -573,7 +579,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         gk[kk * 3 + 2] = gz;
       }
     }
-    __syncthreads();   // the sample lists and parts are rewritten by the next pass
+    // the sample lists and parts are rewritten by the next pass
+    if constexpr (W1) {
+      wave_lds_sync();
+    } else {
+      __syncthreads();
+    }
   }
   // ---- the query's keypoint and anchor gradients (first wave)
   if (!active || wq != 0) return;                      // no barrier follows
@@ -916,10 +927,17 @@ hipError_t launch_deform_backward(DeformArgs a, void* workspace, hipStream_t str
   // multiple of 4, aligned bases) and buffer offsets that fit 31 bits
   const bool vec = a.C % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.feat) | reinterpret_cast<uintptr_t>(a.grad)) & 15) == 0 &&
                    sizeof(float) * (double)a.N * a.H * a.W * a.C < (double)kOutOfRange;
-  if (vec)
-    hipLaunchKernelGGL(deform_bwd<true>, grid, dim3(kBlock), shmem, stream, a);
-  else
-    hipLaunchKernelGGL(deform_bwd<false>, grid, dim3(kBlock), shmem, stream, a);
+  if (a.wq_n == 1) {
+    if (vec)
+      hipLaunchKernelGGL((deform_bwd<true, true>), grid, dim3(kBlock), shmem, stream, a);
+    else
+      hipLaunchKernelGGL((deform_bwd<false, true>), grid, dim3(kBlock), shmem, stream, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((deform_bwd<true, false>), grid, dim3(kBlock), shmem, stream, a);
+    else
+      hipLaunchKernelGGL((deform_bwd<false, false>), grid, dim3(kBlock), shmem, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !gather) return e;
   const int np = (int)npix;
