@@ -672,9 +672,20 @@ __device__ __forceinline__ void runs_fwd_body(const RunArgs& a, int blk, int nbl
   }
   wave_lds_sync();
 
-  // ---- write-out of this wave's cells: per channel, ncell consecutive cells of the flattened grid (the
-  // four waves of the workgroup write the four quarters of each 128-byte line from one CU)
-  if (ncell > 0) {
+  // ---- write-out.  When the tile is 32 whole cells of one aligned 128-byte line per channel, the workgroup
+  // writes it together after a barrier: each half-wave writes one channel's whole line (a lane per cell, read
+  // from the four waves' LDS tiles) with non-temporal stores.  Otherwise each wave writes its own cells.
+  const long long f_tile = f_wave - (long long)wid * kCpw;
+  float* otile = a.out + ((size_t)b * p.out_ch + a.c_lo) * (size_t)XY + f_tile;
+  const bool whole = f_tile + kTileY <= XY && (((uintptr_t)otile | ((size_t)XY * 4)) & 127) == 0;
+  if (whole) {
+    __syncthreads();
+    const size_t wstride = wave_lds_bytes(NL, S) + out_tile_bytes(a.C_launch);
+    const int cell = lane & 31, owner = cell / kCpw;
+    const float* src = reinterpret_cast<const float*>(cur + wstride * owner + wave_lds_bytes(NL, S)) + (cell - owner * kCpw);
+    for (int ch = 2 * wid + (lane >> 5); ch < a.C_launch; ch += 2 * kWaves)
+      __builtin_nontemporal_store(src[ch * kOutLd], otile + (size_t)ch * XY + cell);
+  } else if (ncell > 0) {
     const size_t c_stride = (size_t)XY;
     float* ob = a.out + ((size_t)b * p.out_ch + a.c_lo) * c_stride + f_wave;
     const bool vec = ncell == kCpw && (((uintptr_t)ob | (size_t)p.Y * 4) & 15) == 0;
