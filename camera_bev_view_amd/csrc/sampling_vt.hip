@@ -874,7 +874,8 @@ __device__ __forceinline__ void sampling_vt_bwd_tile(const BwdArgs& a, unsigned 
       for (int i = 0; i < kGPer; ++i) {
         const int e = threadIdx.x + i * kBlock;
         const int c = e / n_cells, k = e - c * n_cells;
-        if (e < Cg * n_cells) sG[k * kBwdGLd + c] = gpre[i];
+        // channel c = q + 16 r of the group sits at 4 q + r, so a lane's 16-byte read holds q, q + 16, q + 32, q + 48
+        if (e < Cg * n_cells) sG[k * kBwdGLd + 4 * (c & 15) + (c >> 4)] = gpre[i];
       }
       grad_staged = true;
     }
@@ -959,18 +960,16 @@ __device__ __forceinline__ void sampling_vt_bwd_tile(const BwdArgs& a, unsigned 
             acc.w = fmaf(w[u], gv[u].w, acc.w);
           }
         }
-        // transpose through lane permutes so that each slot leaves as one atomic over
-        // 64 consecutive channels (one request per cache line instead of four)
-        const int r = lane & 3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (kb + i >= n_occ) break;
-          const int src = 16 * i + (lane >> 2);
-          const float v0 = __shfl(acc.x, src), v1 = __shfl(acc.y, src);
-          const float v2 = __shfl(acc.z, src), v3 = __shfl(acc.w, src);
-          const float v = r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3;
-          const int pix = __builtin_amdgcn_readlane(m.x, 16 * i);
-          if (ch_lane) unsafeAtomicAdd(db + (size_t)pix * p.C + lane, v);
+        // each group's slot leaves as four atomics over 16 consecutive channels each (lane q holds channels q,
+        // q + 16, q + 32, q + 48): per instruction the wave covers 64-byte pieces of four pixels, which the
+        // atomic units take faster than one pixel's 256 bytes
+        if (k < n_occ && count > 0) {
+          const int q = lane & 15;
+          float* d = db + (size_t)m.x * p.C + q;
+          if (q < Cg) unsafeAtomicAdd(d, acc.x);
+          if (q + 16 < Cg) unsafeAtomicAdd(d + 16, acc.y);
+          if (q + 32 < Cg) unsafeAtomicAdd(d + 32, acc.z);
+          if (q + 48 < Cg) unsafeAtomicAdd(d + 48, acc.w);
         }
       }
     }

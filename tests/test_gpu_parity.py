@@ -138,6 +138,7 @@ BWD_CASES = [
     ("f32", 1, 6, 70, 16, 44, 13, 37, 6),     # 64 + 6 channels
     ("f32", 1, 5, 7, 12, 30, 11, 33, 6),
     ("f32", 1, 64, 16, 8, 22, 6, 35, 3),
+    ("f32", 1, 2, 24, 4, 300, 9, 13, 3),      # a map wider than 256 pixels: the hash-table backward
 ]
 
 
