@@ -481,6 +481,46 @@ __device__ __forceinline__ void gather_cell(float* acc, const Rec* sTap, int t, 
   }
 }
 
+// Two channel groups of the same taps at once: K steps, each tap's record read once and both groups' loads
+// (lane offsets off0, off1) issued before the first is used; the last step masked as in gather_last.
+template <int K, int S, class Ln>
+__device__ __forceinline__ void gather2_last(float* acc0, float* acc1, const Rec* rec, __amdgpu_buffer_rsrc_t rs,
+                                             int off0, int off1, bool in_last) {
+  typename Ln::Raw v0[K], v1[K];
+  float w[K];
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    const Rec rr = rec[u * S];
+    const bool in = u + 1 < K || in_last;
+    w[u] = in ? rr.w : 0.f;
+    v0[u] = Ln::load(rs, in ? rr.off + off0 : kOutOfRange);
+    v1[u] = Ln::load(rs, in ? rr.off + off1 : kOutOfRange);
+  }
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    Ln::fma_into(acc0, v0[u], w[u]);
+    Ln::fma_into(acc1, v1[u], w[u]);
+  }
+}
+
+// A cell's kept taps for two channel groups: groups of U steps, the last 1 to U steps (only the last masked) as one.
+template <int U, int S, class Ln>
+__device__ __forceinline__ void gather2_cell(float* acc0, float* acc1, const Rec* sTap, int t, int t1, int slot,
+                                             __amdgpu_buffer_rsrc_t rs, int off0, int off1) {
+  static_assert(U >= 1 && U <= 4, "one to four steps of two groups in flight");
+  for (; t + U * S < t1; t += U * S) gather2_last<U, S, Ln>(acc0, acc1, sTap + t + slot, rs, off0, off1, true);
+  if (t >= t1) return;
+  const int n = (t1 - t + S - 1) / S;
+  const bool in_last = t + (n - 1) * S + slot < t1;
+  const Rec* rec = sTap + t + slot;
+  switch (n) {
+    case 1: gather2_last<1, S, Ln>(acc0, acc1, rec, rs, off0, off1, in_last); break;
+    case 2: if constexpr (U >= 2) gather2_last<2, S, Ln>(acc0, acc1, rec, rs, off0, off1, in_last); break;
+    case 3: if constexpr (U >= 3) gather2_last<3, S, Ln>(acc0, acc1, rec, rs, off0, off1, in_last); break;
+    default: if constexpr (U >= 4) gather2_last<4, S, Ln>(acc0, acc1, rec, rs, off0, off1, in_last); break;
+  }
+}
+
 // A cell's accumulators, complete: sum the S slots and park the channels in column `ct` of the output tile;
 // the accumulators are cleared for the next cell.
 template <int L, int kVec, bool kAdd = false>
@@ -648,17 +688,21 @@ __device__ __forceinline__ void runs_fwd_body(const RunArgs& a, int blk, int nbl
     // ---- phase C: gather, cell by cell; a step takes S consecutive kept taps, kU steps in flight
     const int cl_first = __builtin_amdgcn_readfirstlane(cl), cl_last = __builtin_amdgcn_readlane(cl, nsmp - 1);
     if constexpr (MG) {
+      // two channel groups (the launch's a.ngroups is 2): both groups' loads of a step issued together, so a cell
+      // costs the round trips of one group; lanes past the second group's channels read outside the buffer (zeros)
+      constexpr int kU2 = (kVec > 4 || L < 16) ? 2 : (kU > 4 ? 4 : kU);   // steps of both groups in flight, no spills
+      const int g1_n = a.C_launch - a.Cg;
+      const int off1 = (q * kVec < g1_n) ? lane_off + a.Cg * p.elem_bytes : 0x40000000;
+      float acc1[kVec];
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) acc1[i] = 0.f;
       for (int c = cl_first; c <= cl_last; ++c) {
         const int hi_raw = uniform(sCellHi[c]);
         if (hi_raw < 0) continue;
         const int t1 = hi_raw & ((1 << 30) - 1), t0 = uniform(sCellLo[c]);
-        for (int gi = 0; gi < a.ngroups; ++gi) {
-          const int g_lo = gi * a.Cg, g_n = min(a.Cg, a.C_launch - g_lo);
-          // lanes past the group's channels read outside the buffer (zeros)
-          const int off_g = (q * kVec < g_n) ? lane_off + g_lo * p.elem_bytes : 0x40000000;
-          gather_cell<kU, S, Ln>(acc, sTap, t0, t1, slot, rs, off_g);
-          flush_cell<L, kVec, true>(acc, sOut + g_lo * kOutLd, c, lane, g_n);
-        }
+        gather2_cell<kU2, S, Ln>(acc, acc1, sTap, t0, t1, slot, rs, lane_off, off1);
+        flush_cell<L, kVec, true>(acc, sOut, c, lane, a.Cg);
+        flush_cell<L, kVec, true>(acc1, sOut + a.Cg * kOutLd, c, lane, g1_n);
       }
     } else
     for (int c = cl_first; c <= cl_last; ++c) {
